@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the segmented multi-LoRA linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: segment-metadata
+build, shrink (H = X_a A_a^T), and the base GEMM with the LoRA expand fused
+into its epilogue (``--path separate``: base GEMM, then expand +
+scatter-add).  Inputs are resident in HBM before timing starts.  Each step
+uses the next of several copies of the layer's tensors (like consecutive
+layers of a model), so that the 256 MB last-level cache cannot serve weights
+read in the previous step.
+
+Prints one JSON line (rank 0; one GPU):
+  value      = token rows per second of the whole step (headline workload)
+  roofline   = dominant kernel: algorithmic bytes (or flops) per launch over
+               its mean HIP-event duration, against the MI355X peak
+  kernels    = the same figures for every kernel of the step
+  prefill    = the prefill workload's step (tokens/s, TFLOP/s, MFMA fraction)
+  cpu_baseline = the float64 CPU oracle on a bounded sample of the headline
+               workload, on this host's cores
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--path fused]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+F32_TFLOPS = 157.3
+
+WORKLOAD_NAMES = {
+    1: "tiny fp32: d_in=d_out=512, 32 rows in 4 segments [0,8,12,28,32] (r 8/base/16/8)",
+    2: "decode bf16: d_in=d_out=4096, 256 rows (1 token/request), 128 slots r=16, 10% base-only",
+    3: "prefill bf16: d_in=4096 -> d_out=14336, 8 requests 512..4096 tokens, ranks 8..64, 1 base-only",
+    4: "skewed decode bf16: d=4096, 1024 rows, 1000 slots r in {8,16,32,64}, Zipf(1.0) ids",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--path", choices=["fused", "separate"], default="fused")
+    p.add_argument("--policy", choices=["exact", "two_buckets", "padded"], default="exact")
+    p.add_argument("--rotate-mb", type=float, default=600.0,
+                   help="total size of the rotated copies of the layer tensors")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every call from Python instead of replaying a captured HIP graph")
+    p.add_argument("--kernel-loops", type=int, default=None,
+                   help="launches per kernel in the per-kernel timing (default: steps)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (true ranks; base-only rows carry no LoRA work)
+# ---------------------------------------------------------------------------
+def work_figures(w):
+    e = 2 if w.dtype == "bf16" else 4
+    keys = [int(a) for a in w.row_slot]
+    lora_rows = [(i, a) for i, a in enumerate(keys)
+                 if 0 <= a < w.n_slots and 0 < int(w.slot_rank[a]) <= w.r_max]
+    distinct = sorted({a for _, a in lora_rows})
+    sum_r_distinct = sum(int(w.slot_rank[a]) for a in distinct)
+    sum_r_rows = sum(int(w.slot_rank[a]) for _, a in lora_rows)
+    n_lora = len(lora_rows)
+    n, di, do = w.n, w.d_in, w.d_out
+    f = {
+        "n_lora_rows": n_lora,
+        "distinct_adapters": len(distinct),
+        "bytes": {
+            "build": n * 4 + 2 * n * 4 + 2 * w.n_slots * 4,
+            "shrink": sum_r_distinct * di * e + n_lora * di * e + sum_r_rows * 4,
+            "expand": sum_r_distinct * do * e + sum_r_rows * 4 + 2 * n_lora * do * e,
+            "base": do * di * e + n * di * e + n * do * e,
+            "fused": do * di * e + n * di * e + n * do * e + sum_r_distinct * do * e + sum_r_rows * 4,
+        },
+        "flops": {
+            "shrink": 2 * sum_r_rows * di,
+            "expand": 2 * sum_r_rows * do,
+            "base": 2 * n * di * do,
+            "fused": 2 * n * di * do + 2 * sum_r_rows * do,
+        },
+    }
+    return f
+
+
+# ---------------------------------------------------------------------------
+# device state
+# ---------------------------------------------------------------------------
+class Layer:
+    def __init__(self, w, policy, device):
+        import torch
+        import segmented_rank_gemm_segment_amd as srg
+        import workloads as wl
+        d = wl.device_tensors(w, device)
+        self.X, self.W, self.row_slot = d["X"], d["W"], d["row_slot"]
+        self.alpha = w.slot_alpha
+        self.pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha, policy)
+        self.seg = srg.Segments(w.n, w.n_slots, device)
+        dt = self.X.dtype
+        self.H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=device)
+        self.Y = torch.empty((w.n, w.d_out), dtype=dt, device=device)
+        self.nbytes = sum(t.numel() * t.element_size()
+                          for t in (self.X, self.W, d["A"], d["Bt"], self.Y, self.H))
+
+    def clone(self, device):
+        import copy
+        import torch
+        import segmented_rank_gemm_segment_amd as srg
+        c = copy.copy(self)
+        c.X, c.W = self.X.clone(), self.W.clone()
+        p = self.pool
+        c.row_slot = self.row_slot.clone()
+        c.pool = srg.Pool(p.A.clone(), p.Bt.clone(), p.slot_rank.clone(), self.alpha,
+                          p.rank_policy)
+        c.seg = srg.Segments(self.seg.n_rows, p.n_slots, device)
+        c.H, c.Y = torch.zeros_like(self.H), torch.empty_like(self.Y)
+        return c
+
+
+def k_build(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_build_segments(L.row_slot, L.pool, L.seg)
+
+
+def k_shrink(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_shrink(L.X, L.seg, L.pool, L.H)
+
+
+def k_fused(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_linear_fused(L.X, L.W, L.H, L.seg, L.pool, L.Y)
+
+
+def k_base(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_base_gemm(L.X, L.W, L.Y)
+
+
+def k_expand(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_expand(L.H, L.seg, L.pool, L.Y)
+
+
+STEP = {"fused": (k_build, k_shrink, k_fused), "separate": (k_build, k_shrink, k_base, k_expand)}
+KNAME = {k_build: "build", k_shrink: "shrink", k_fused: "fused", k_base: "base", k_expand: "expand"}
+
+
+def _graph(fn_seq, layers, count, start=0):
+    """Capture `count` calls cycling through `layers` into one HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            for fn in fn_seq:
+                fn(layers[(start + i) % len(layers)])
+    return g
+
+
+def time_calls(fn_seq, layers, iters, warmup, use_graph):
+    """Mean device time of one pass of fn_seq over `iters` passes cycling
+    through `layers`, bracketed by HIP events on the launch stream.  With
+    use_graph the passes are captured in one HIP graph (replayed once)."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        gw = _graph(fn_seq, layers, max(1, warmup))
+        gt = _graph(fn_seq, layers, iters, start=max(1, warmup))
+        gw.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ev0.record()
+        gt.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+    else:
+        for i in range(warmup):
+            for fn in fn_seq:
+                fn(layers[i % len(layers)])
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ev0.record()
+        for i in range(iters):
+            for fn in fn_seq:
+                fn(layers[i % len(layers)])
+        ev1.record()
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    return ev0.elapsed_time(ev1) * 1e-3 / iters, wall
+
+
+def measure(w, path, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
+            device="cuda:0"):
+    import torch
+    L0 = Layer(w, policy, device)
+    copies = max(1, int(np.ceil(rotate_mb * 1e6 / L0.nbytes)))
+    layers = [L0] + [L0.clone(device) for _ in range(copies - 1)]
+    for L in layers:                      # metadata/H valid for per-kernel loops
+        k_build(L)
+        k_shrink(L)
+    torch.cuda.synchronize()
+    step_s, wall = time_calls(STEP[path], layers, steps, warmup, use_graph)
+    kl = kernel_loops or steps
+    per_kernel = {}
+    for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
+        per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
+    return {"step_s": step_s, "wall_s": wall, "per_kernel_s": per_kernel, "copies": copies,
+            "layer_bytes": L0.nbytes}
+
+
+def kernel_table(fig, per_kernel, dtype):
+    out = {}
+    for k, sec in per_kernel.items():
+        b = fig["bytes"].get(k)
+        fl = fig["flops"].get(k, 0)
+        d = {"us": round(sec * 1e6, 3)}
+        if b is not None:
+            d["GB_s"] = round(b / sec / 1e9, 1)
+            d["hbm_frac"] = round(b / sec / 1e9 / HBM_PEAK_GBS, 4)
+            d["alg_bytes"] = int(b)
+        if fl:
+            d["TFLOP_s"] = round(fl / sec / 1e12, 2)
+            peak = MFMA_BF16_TFLOPS if dtype == "bf16" else F32_TFLOPS
+            d["mfma_frac"] = round(fl / sec / 1e12 / peak, 4)
+        out[k] = d
+    return out
+
+
+def roofline_for(kernel, fig, sec, dtype):
+    b = fig["bytes"][kernel]
+    fl = fig["flops"].get(kernel, 0)
+    peak_f = MFMA_BF16_TFLOPS if dtype == "bf16" else F32_TFLOPS
+    ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if fl and fl / b > ridge:
+        a = fl / sec / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(a / peak_f, 4), "traffic": None, "kernel": kernel}
+    a = b / sec / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle as it stands, on the whole headline batch, repeated for
+    about `budget_s` seconds of host time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    runs, rows, t0 = 0, 0, time.perf_counter()
+    while True:
+        oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)
+        oracle.lora_forward(w.X, w.W, w.A, w.B, w.row_slot, w.slot_rank, w.slot_alpha, w.r_max,
+                            w.dtype)
+        runs += 1
+        rows += w.n
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(rows / el, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{runs} full passes of the {w.n}-row batch (metadata + float64 row loop) in {el:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this layer's kernels run on a single MI355X; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import segmented_rank_gemm_segment_amd as srg
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    srg.lib()
+
+    w = wl.make_config(args.config)
+    fig = work_figures(w)
+    m = measure(w, args.path, args.policy, args.steps, args.warmup, args.rotate_mb,
+                args.kernel_loops, not args.eager)
+    kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
+    main_k = "fused" if args.path == "fused" else max(("base", "expand", "shrink"),
+                                                      key=lambda k: m["per_kernel_s"][k])
+    if args.path == "fused":
+        main_k = max(("fused", "shrink", "build"), key=lambda k: m["per_kernel_s"][k])
+    roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)
+    step_s = m["step_s"]
+    sh, ex = m["per_kernel_s"]["shrink"], m["per_kernel_s"]["expand"]
+    se_bytes = fig["bytes"]["shrink"] + fig["bytes"]["expand"]
+    out = {
+        "metric": "multi-LoRA layer tokens/s; shrink+expand HBM GB/s & % roofline (decode, prefill)",
+        "value": round(w.n / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normals; mapping per the workload recipe)",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "path": args.path,
+                   "rank_policy": args.policy, "rows": w.n, "lora_rows": fig["n_lora_rows"],
+                   "distinct_adapters": fig["distinct_adapters"],
+                   "rotated_copies": m["copies"], "launch": "eager" if args.eager else "hip_graph",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "shrink_expand": {"GB_s": round(se_bytes / (sh + ex) / 1e9, 1),
+                          "hbm_frac": round(se_bytes / (sh + ex) / 1e9 / HBM_PEAK_GBS, 4),
+                          "us": round((sh + ex) * 1e6, 3)},
+        "kernels": kt,
+        "host_wall_s": round(m["wall_s"], 4),
+    }
+    if not args.no_prefill and args.config != 3:
+        w3 = wl.make_config(3)
+        f3 = work_figures(w3)
+        st3 = max(5, args.steps // 10)
+        m3 = measure(w3, "fused", args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
+                     not args.eager)
+        k3 = kernel_table(f3, m3["per_kernel_s"], "bf16")
+        out["prefill"] = {
+            "workload": WORKLOAD_NAMES[3], "rows": w3.n, "tokens_s": round(w3.n / m3["step_s"], 1),
+            "ms_per_step": round(m3["step_s"] * 1e3, 4),
+            "fused_gemm": roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
+            "shrink_expand": {"GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
+                                            (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1)},
+            "kernels": k3,
+        }
+        del w3
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

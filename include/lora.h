@@ -1,0 +1,190 @@
+/*
+ * lora.h - C ABI of the segmented multi-LoRA linear layer for MI355X (gfx950).
+ *
+ * The layer (Multi-LoRA Serving: adapter batching, charlestar.github.io,
+ * sections "LoRA 在一层 Linear 上增加了什么" and "一个混合 Batch 的数学形式"):
+ *
+ *     Y = X W^T + s_a (X_a A_a^T) B_a^T,     s_a = alpha_a / r_a,
+ *
+ * where every token row i carries its own adapter slot a(i) (or none), the
+ * base product X W^T is shared by all rows, and row i only ever uses its
+ * own A_a, B_a, s_a.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *   structs themselves live in host memory.  The caller owns every buffer;
+ *   the library allocates nothing and keeps no state between calls.
+ * - Calls are asynchronous on the given HIP stream (`hipStream_t` passed as
+ *   `void*`, NULL = the default stream).  Argument errors are detected on
+ *   the host and returned before anything is launched; no output is touched
+ *   then.  LORA_ERR_HIP reports a failed launch.
+ * - Row-major storage.  Leading dimensions (`ld*`) are in elements, at least
+ *   the row width, and multiples of 8; every tensor base pointer is 16-byte
+ *   aligned; d_in and d_out are positive multiples of 8.  Otherwise
+ *   LORA_ERR_ALIGN / LORA_ERR_SHAPE.
+ * - X, W, Y, A and Bt share the pool's dtype (bf16 or fp32).  H is fp32.
+ *   Accumulation is fp32.
+ * - Data errors found on the device (a row's slot outside [-1, n_slots) or
+ *   a slot rank outside [0, r_max]) never alias memory: the row is treated
+ *   as base-only and counted in `*status` by lora_build_segments.
+ * - Calls that share output buffers and overlap on one device race.
+ */
+#ifndef LORA_H_
+#define LORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+/* Largest pool: the segment builder keeps per-slot tables in LDS. */
+#define LORA_MAX_SLOTS 4095
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_ERR_NULL = -1,      /* a required pointer is NULL */
+  LORA_ERR_SHAPE = -2,     /* a size is out of range or inconsistent */
+  LORA_ERR_RANK = -3,      /* r_max not one of 8, 16, 32, 64 */
+  LORA_ERR_ALIGN = -4,     /* pointer not 16-byte aligned or ld not a multiple of 8 */
+  LORA_ERR_DTYPE = -5,     /* unknown dtype */
+  LORA_ERR_CAPACITY = -6,  /* segment arrays too small for the worst case */
+  LORA_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
+  LORA_ERR_POLICY = -8     /* unknown rank policy */
+} lora_status;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/*
+ * How a segment of true rank r is processed (adapter-batching page, section
+ * "不同 LoRA Rank 会怎样影响 Kernel": padding every slot to r_max versus
+ * kernels chosen per rank bucket).  Work and bytes read per segment scale
+ * with the processed width; the result never depends on the policy, because
+ * rank rows at or past r are masked to zero, never multiplied in.
+ */
+typedef enum {
+  LORA_RANK_EXACT = 0,       /* r rounded up to the next of 8, 16, 32, 64 */
+  LORA_RANK_TWO_BUCKETS = 1, /* r <= 16 -> 16, else 64 (the page's {8,16} / {32,64}) */
+  LORA_RANK_PADDED = 2       /* every segment at r_max */
+} lora_rank_policy;
+
+/*
+ * Fixed-slot adapter pool (LoRA/QLoRA 多租户 GPU 推理服务化实战, section 1.1
+ * "Adapter的统一尺寸对齐": one preallocated buffer, uniform slot size, O(1)
+ * lookup by slot offset).  Slot a holds, rank-major,
+ *   A [n_slots][r_max][d_in]   row k = row k of A_a      (A_a in R^{r x d_in})
+ *   Bt[n_slots][r_max][d_out]  row k = column k of B_a   (B_a in R^{d_out x r})
+ * Rows k >= slot_rank[a] are padding and are never multiplied in.
+ * slot_scale[a] is s_a = alpha_a / r_a (0 for a rank-0 slot).
+ */
+typedef struct {
+  int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
+  int32_t r_max;             /* 8, 16, 32 or 64 */
+  int32_t d_in;
+  int32_t d_out;
+  int32_t dtype;             /* lora_dtype */
+  int32_t rank_policy;       /* lora_rank_policy */
+  const void *A;             /* device */
+  const void *Bt;            /* device */
+  const int32_t *slot_rank;  /* device, [n_slots] */
+  const float *slot_scale;   /* device, [n_slots] */
+} lora_pool;
+
+/*
+ * Segment metadata (adapter-batching page, section "Segmented Kernel 需要哪些
+ * Metadata": segment_offsets, adapter_slots, token_indices, ranks, scales).
+ * Written by lora_build_segments, read by the other calls.  Host fields:
+ * n_rows (token rows of the batch) and max_segments (capacity of the
+ * per-segment arrays; must be >= min(n_rows, n_slots + 1)).  Device arrays:
+ *   token_indices  [n_rows]          sorted position -> original row
+ *   row_segment    [n_rows]          original row -> segment id
+ *   segment_offsets[max_segments+1]  segment s = sorted positions [off[s], off[s+1])
+ *   segment_slots  [max_segments]    slot, -1 for the base-only segment
+ *   segment_ranks  [max_segments]    0 for base-only
+ *   segment_scales [max_segments]    0 for base-only and rank-0 slots
+ *   num_segments   [1]
+ *   status         [1]               rows demoted to base-only (bad slot/rank)
+ * Segments appear in first-appearance order of their slot; rows inside a
+ * segment are ascending.  Entries past num_segments are left untouched.
+ */
+typedef struct {
+  int32_t n_rows;
+  int32_t max_segments;
+  int32_t *token_indices;
+  int32_t *row_segment;
+  int32_t *segment_offsets;
+  int32_t *segment_slots;
+  int32_t *segment_ranks;
+  float *segment_scales;
+  int32_t *num_segments;
+  int32_t *status;
+} lora_segments;
+
+/* ABI version of the loaded library (LORA_ABI_VERSION). */
+int32_t lora_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *lora_status_str(int32_t status);
+
+/*
+ * Group the batch's token rows by slot (adapter-batching page, "Segmented
+ * Kernel 需要哪些 Metadata"; one segment per distinct slot, as S-LoRA 深度解析
+ * section 3.1 asks, requests of one adapter merged into one product).
+ * row_slot: device int32 [seg->n_rows], -1 = base-only.  One launch, no
+ * host synchronisation.  n_rows == 0 writes num_segments = 0,
+ * segment_offsets[0] = 0 and status = 0.
+ */
+lora_status lora_build_segments(const int32_t *row_slot, const lora_pool *pool,
+                                const lora_segments *seg, void *stream);
+
+/*
+ * Shrink, H_a = X_a A_a^T per segment (adapter-batching page, "Segmented
+ * Kernel 需要哪些 Metadata").  X [n_rows][d_in] (ld ldx), pool dtype.
+ * H: fp32 [n_rows][r_max] indexed by ORIGINAL row; for a row of a segment of
+ * rank r > 0, H[i][0:r] is written; every other entry of H is untouched.
+ */
+lora_status lora_shrink(const void *X, int64_t ldx, const lora_segments *seg,
+                        const lora_pool *pool, float *H, void *stream);
+
+/*
+ * Expand and scatter-add, Y[i] += s_a H[i][0:r] B_a^T for every row i of a
+ * segment of rank r > 0 (same section: Delta Y_a = s_a H_a B_a^T, added back
+ * to the original rows).  Y [n_rows][d_out] (ld ldy), pool dtype; each Y
+ * element is read, added in fp32 and rounded once.  Rows of base-only and
+ * rank-0 segments are not touched.  Each row belongs to exactly one segment,
+ * so no atomics are used and the result is deterministic.
+ */
+lora_status lora_expand(const float *H, const lora_segments *seg, const lora_pool *pool,
+                        void *Y, int64_t ldy, void *stream);
+
+/*
+ * Base product only, Y = X W^T (adapter-batching page, "一个混合 Batch 的数学
+ * 形式": one GEMM shared by all rows).  X [n_rows][d_in], W [d_out][d_in]
+ * (nn.Linear layout), Y [n_rows][d_out], all of `dtype`.  bf16 runs on
+ * MFMA with fp32 accumulation and one rounding.
+ */
+lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                           void *Y, int64_t ldy, int32_t n_rows, int32_t d_in,
+                           int32_t d_out, int32_t dtype, void *stream);
+
+/*
+ * Base product with the LoRA expand fused into its epilogue:
+ *   Y[i] = X[i] W^T + s_a H[i][0:r] B_a^T
+ * (the second low-rank product added straight into the base output, as the
+ * epilogue-fusion passage of the ybb.press multi-LoRA serving article,
+ * section 5.3, describes).  H comes from lora_shrink on the same metadata.
+ * The fp32 accumulator is rounded to the output dtype once.  Rows of
+ * base-only and rank-0 segments equal lora_base_gemm's output bit for bit.
+ */
+lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                              const float *H, const lora_segments *seg,
+                              const lora_pool *pool, void *Y, int64_t ldy, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H_ */

@@ -1,0 +1,278 @@
+"""Segmented multi-LoRA linear layer for MI355X (gfx950): Python binding.
+
+Thin ctypes layer over ``liblora.so`` (C ABI in ``include/lora.h``).  It only
+marshals arguments: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.
+
+Entry points carry the C names:
+
+* ``lora_build_segments(row_slot, pool, seg)``
+* ``lora_shrink(X, seg, pool, H)``
+* ``lora_expand(H, seg, pool, Y)``            (Y += ...)
+* ``lora_base_gemm(X, W, Y)``                 (Y = X W^T)
+* ``lora_linear_fused(X, W, H, seg, pool, Y)``  (Y = X W^T + LoRA)
+
+If the library is missing the import still succeeds, but every entry point
+raises ``RuntimeError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
+RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
+MAX_SLOTS = 4095
+ABI_VERSION = 1
+
+_c_int32_p = ctypes.POINTER(ctypes.c_int32)
+
+
+class LoraPoolC(ctypes.Structure):
+    _fields_ = [
+        ("n_slots", ctypes.c_int32),
+        ("r_max", ctypes.c_int32),
+        ("d_in", ctypes.c_int32),
+        ("d_out", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rank_policy", ctypes.c_int32),
+        ("A", ctypes.c_void_p),
+        ("Bt", ctypes.c_void_p),
+        ("slot_rank", ctypes.c_void_p),
+        ("slot_scale", ctypes.c_void_p),
+    ]
+
+
+class LoraSegmentsC(ctypes.Structure):
+    _fields_ = [
+        ("n_rows", ctypes.c_int32),
+        ("max_segments", ctypes.c_int32),
+        ("token_indices", ctypes.c_void_p),
+        ("row_segment", ctypes.c_void_p),
+        ("segment_offsets", ctypes.c_void_p),
+        ("segment_slots", ctypes.c_void_p),
+        ("segment_ranks", ctypes.c_void_p),
+        ("segment_scales", ctypes.c_void_p),
+        ("num_segments", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+class LoraError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"liblora status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+EXPORTS = (
+    "lora_abi_version",
+    "lora_status_str",
+    "lora_build_segments",
+    "lora_shrink",
+    "lora_expand",
+    "lora_base_gemm",
+    "lora_linear_fused",
+)
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblora.so (built by ``python -m segmented_rank_gemm_segment_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m segmented_rank_gemm_segment_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    PP, SP = ctypes.POINTER(LoraPoolC), ctypes.POINTER(LoraSegmentsC)
+    L.lora_abi_version.restype = i32
+    L.lora_abi_version.argtypes = []
+    L.lora_status_str.restype = ctypes.c_char_p
+    L.lora_status_str.argtypes = [i32]
+    L.lora_build_segments.restype = i32
+    L.lora_build_segments.argtypes = [vp, PP, SP, vp]
+    L.lora_shrink.restype = i32
+    L.lora_shrink.argtypes = [vp, i64, SP, PP, vp, vp]
+    L.lora_expand.restype = i32
+    L.lora_expand.argtypes = [vp, SP, PP, vp, i64, vp]
+    L.lora_base_gemm.restype = i32
+    L.lora_base_gemm.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
+    L.lora_linear_fused.restype = i32
+    L.lora_linear_fused.argtypes = [vp, i64, vp, i64, vp, SP, PP, vp, i64, vp]
+    if L.lora_abi_version() != ABI_VERSION:
+        raise RuntimeError("liblora ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise LoraError(code, lib().lora_status_str(code).decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return LORA_BF16
+    if t == torch.float32:
+        return LORA_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() == 2 and t.numel() == 0:
+        return max(int(t.shape[1]), 8)
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a row-major 2-D tensor")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+# pool and metadata holders
+# ---------------------------------------------------------------------------
+class Pool:
+    """Fixed-slot adapter pool resident on the device.
+
+    ``A``  [n_slots, r_max, d_in]  and  ``Bt`` [n_slots, r_max, d_out]
+    (rank-major; row k of Bt[a] is column k of B_a), ``slot_rank`` int32
+    [n_slots] and per-slot alpha.  The per-slot scale alpha/r is stored as
+    float32 (0 for rank 0) when the pool is created, as adapter loading does.
+    """
+
+    def __init__(self, A: torch.Tensor, Bt: torch.Tensor, slot_rank: torch.Tensor,
+                 slot_alpha, rank_policy: str = "exact"):
+        if A.dim() != 3 or Bt.dim() != 3 or A.shape[:2] != Bt.shape[:2]:
+            raise ValueError("A [n_slots, r_max, d_in] and Bt [n_slots, r_max, d_out] expected")
+        if A.dtype != Bt.dtype or not A.is_contiguous() or not Bt.is_contiguous():
+            raise ValueError("A and Bt: same dtype, contiguous")
+        self.A, self.Bt = A, Bt
+        self.n_slots, self.r_max, self.d_in = A.shape
+        self.d_out = Bt.shape[2]
+        self.dtype = A.dtype
+        self.slot_rank = slot_rank.to(device=A.device, dtype=torch.int32).contiguous()
+        rank_host = self.slot_rank.cpu().to(torch.float64)
+        alpha = torch.as_tensor(slot_alpha, dtype=torch.float64).reshape(-1)
+        scale = torch.where(rank_host > 0, alpha / rank_host.clamp(min=1), torch.zeros_like(alpha))
+        self.slot_scale = scale.to(torch.float32).to(A.device).contiguous()
+        self.set_policy(rank_policy)
+
+    def set_policy(self, rank_policy: str):
+        self.rank_policy = rank_policy
+        self._c = LoraPoolC(self.n_slots, self.r_max, self.d_in, self.d_out, _dtype_code(self.dtype),
+                            RANK_POLICIES[rank_policy], self.A.data_ptr(), self.Bt.data_ptr(),
+                            self.slot_rank.data_ptr(), self.slot_scale.data_ptr())
+        return self
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+class Segments:
+    """Device arrays of the segment metadata for a batch of n_rows rows."""
+
+    def __init__(self, n_rows: int, n_slots: int, device, max_segments: Optional[int] = None):
+        cap = min(n_rows, n_slots + 1) if max_segments is None else max_segments
+        i32 = dict(dtype=torch.int32, device=device)
+        self.n_rows = n_rows
+        self.max_segments = cap
+        self.token_indices = torch.empty(max(n_rows, 1), **i32)
+        self.row_segment = torch.empty(max(n_rows, 1), **i32)
+        self.segment_offsets = torch.empty(cap + 1, **i32)
+        self.segment_slots = torch.empty(max(cap, 1), **i32)
+        self.segment_ranks = torch.empty(max(cap, 1), **i32)
+        self.segment_scales = torch.empty(max(cap, 1), dtype=torch.float32, device=device)
+        self.num_segments = torch.empty(1, **i32)
+        self.status = torch.empty(1, **i32)
+        self._c = LoraSegmentsC(n_rows, cap, self.token_indices.data_ptr(),
+                                self.row_segment.data_ptr(), self.segment_offsets.data_ptr(),
+                                self.segment_slots.data_ptr(), self.segment_ranks.data_ptr(),
+                                self.segment_scales.data_ptr(), self.num_segments.data_ptr(),
+                                self.status.data_ptr())
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+    def to_host(self) -> dict:
+        """Metadata as numpy arrays (synchronises)."""
+        S = int(self.num_segments.item())
+        return {
+            "num_segments": S,
+            "segment_offsets": self.segment_offsets[:S + 1].cpu().numpy(),
+            "segment_slots": self.segment_slots[:S].cpu().numpy(),
+            "segment_ranks": self.segment_ranks[:S].cpu().numpy(),
+            "segment_scales": self.segment_scales[:S].cpu().numpy(),
+            "token_indices": self.token_indices[:self.n_rows].cpu().numpy(),
+            "row_segment": self.row_segment[:self.n_rows].cpu().numpy(),
+            "status": int(self.status.item()),
+        }
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def lora_build_segments(row_slot: torch.Tensor, pool: Pool, seg: Segments, stream=None) -> None:
+    if row_slot.dtype != torch.int32 or (row_slot.numel() and not row_slot.is_contiguous()):
+        raise ValueError("row_slot: contiguous int32")
+    if row_slot.numel() != seg.n_rows:
+        raise ValueError("row_slot length != seg.n_rows")
+    _check(lib().lora_build_segments(_ptr(row_slot), pool.c, seg.c, _stream(stream)))
+
+
+def lora_shrink(X: torch.Tensor, seg: Segments, pool: Pool, H: torch.Tensor, stream=None) -> None:
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    if X.shape[0] != seg.n_rows or X.dtype != pool.dtype:
+        raise ValueError("X: [n_rows, d_in] of the pool dtype")
+    _check(lib().lora_shrink(_ptr(X), _ld(X), seg.c, pool.c, _ptr(H), _stream(stream)))
+
+
+def lora_expand(H: torch.Tensor, seg: Segments, pool: Pool, Y: torch.Tensor, stream=None) -> None:
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    if Y.shape[0] != seg.n_rows or Y.dtype != pool.dtype:
+        raise ValueError("Y: [n_rows, d_out] of the pool dtype")
+    _check(lib().lora_expand(_ptr(H), seg.c, pool.c, _ptr(Y), _ld(Y), _stream(stream)))
+
+
+def lora_base_gemm(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor, stream=None) -> None:
+    if not (X.dtype == W.dtype == Y.dtype):
+        raise ValueError("X, W, Y must share a dtype")
+    n, d_in = X.shape
+    d_out = W.shape[0]
+    if W.shape[1] != d_in or tuple(Y.shape) != (n, d_out):
+        raise ValueError("shapes: X [n, d_in], W [d_out, d_in], Y [n, d_out]")
+    _check(lib().lora_base_gemm(_ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(Y), _ld(Y), n, d_in, d_out,
+                                _dtype_code(X.dtype), _stream(stream)))
+
+
+def lora_linear_fused(X: torch.Tensor, W: torch.Tensor, H: torch.Tensor, seg: Segments, pool: Pool,
+                      Y: torch.Tensor, stream=None) -> None:
+    if not (X.dtype == W.dtype == Y.dtype == pool.dtype):
+        raise ValueError("X, W, Y must share the pool dtype")
+    if X.shape[0] != seg.n_rows or tuple(W.shape) != (pool.d_out, pool.d_in) \
+            or tuple(Y.shape) != (seg.n_rows, pool.d_out):
+        raise ValueError("shapes: X [n, d_in], W [d_out, d_in], Y [n, d_out]")
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    _check(lib().lora_linear_fused(_ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(H), seg.c, pool.c,
+                                   _ptr(Y), _ld(Y), _stream(stream)))

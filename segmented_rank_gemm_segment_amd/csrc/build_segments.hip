@@ -1,0 +1,218 @@
+// Segment metadata builder.
+//
+// Groups the token rows of a batch by adapter slot, as the adapter-batching
+// page (Multi-LoRA Serving, charlestar.github.io, section "Segmented Kernel
+// 需要哪些 Metadata") describes: one segment per distinct slot (base-only is
+// its own segment with rank 0 and scale 0), segments in order of first
+// appearance, rows ascending inside a segment, with segment_offsets,
+// adapter slots, ranks, scales and the token permutation.
+//
+// One workgroup of 1024 threads does the whole job in a single launch with
+// no host synchronisation: per-slot tables live in LDS, rows are visited in
+// chunks of 1024, and rows of one key inside a wavefront are grouped with a
+// ballot loop (one iteration per distinct key in the wave).  Positions come
+// from counts, never from the order in which atomics land, so the output is
+// deterministic.
+#include <climits>
+
+#include "lora_device.cuh"
+#include "lora_kernels.h"
+
+namespace lora {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxKeys = 4096;  // n_slots + 1 (slot keys plus the base-only key)
+
+struct BuildArgs {
+  const int32_t *row_slot;
+  int n, n_slots, r_max;
+  const int32_t *slot_rank;
+  const float *slot_scale;
+  int32_t *token_indices, *row_segment, *seg_off, *seg_slot, *seg_rank;
+  float *seg_scale;
+  int32_t *num_segments, *status;
+};
+
+__global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
+  __shared__ int s_first[kMaxKeys];  // first row of a key; later -(segment + 1)
+  __shared__ int s_cnt[kMaxKeys];    // rows of a key; later the per-key cursor
+  __shared__ int s_off[kMaxKeys + 1];// segment lengths, then exclusive offsets
+  __shared__ int s_lead_key[kThreads];
+  __shared__ int s_lead_cnt[kThreads];
+  __shared__ int s_lead_base[kThreads];
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_bad, s_total;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int K = a.n_slots + 1;
+  const int n = a.n;
+
+  for (int k = tid; k < K; k += kThreads) {
+    s_first[k] = INT_MAX;
+    s_cnt[k] = 0;
+  }
+  if (tid == 0) {
+    s_bad = 0;
+    s_total = 0;
+  }
+  __syncthreads();
+
+  // Pass 1: validate every row, keep its key (slot + 1, 0 = base-only) in
+  // row_segment for the later passes (same thread reads it back), and
+  // gather first row and row count per key.  One LDS atomic per group of
+  // equal keys in a wave; min/add commute, so the result is exact.
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int i = c0 + tid;
+    const bool valid = i < n;
+    int key = 0;
+    bool bad = false;
+    if (valid) {
+      const int slot = a.row_slot[i];
+      if (slot != -1) {
+        if (slot < -1 || slot >= a.n_slots) {
+          bad = true;
+        } else {
+          const int r = a.slot_rank[slot];
+          if (r < 0 || r > a.r_max) bad = true;
+          else key = slot + 1;
+        }
+      }
+      a.row_segment[i] = key;
+    }
+    const uint64_t badmask = __ballot(bad);
+    if (lane == 0 && badmask) atomicAdd(&s_bad, __popcll(badmask));
+    const uint64_t peers = match_key(key, valid);
+    if (valid && (peers & lanemask_lt()) == 0) {  // lowest lane = lowest row of the group
+      atomicMin(&s_first[key], i);
+      atomicAdd(&s_cnt[key], __popcll(peers));
+    }
+  }
+  __syncthreads();
+
+  // Pass 2: a row is the head of its segment iff it is its key's first row.
+  // Segment ids are the running count of heads, so segments come in order
+  // of first appearance.
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int i = c0 + tid;
+    const bool valid = i < n;
+    const int key = valid ? a.row_segment[i] : 0;
+    const bool head = valid && s_first[key] == i;
+    const uint64_t hm = __ballot(head);
+    if (lane == 0) s_wave[wave] = __popcll(hm);
+    __syncthreads();
+    int before = s_total;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    if (head) {
+      const int s = before + __popcll(hm & lanemask_lt());
+      const int slot = key - 1;
+      const int r = key == 0 ? 0 : a.slot_rank[slot];
+      a.seg_slot[s] = slot;
+      a.seg_rank[s] = r;
+      a.seg_scale[s] = r > 0 ? a.slot_scale[slot] : 0.0f;
+      s_off[s] = s_cnt[key];
+      s_first[key] = -(s + 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int w = 0; w < kWaves; ++w) t += s_wave[w];
+      s_total += t;
+    }
+    __syncthreads();
+  }
+  const int S = s_total;
+
+  // Pass 3: exclusive scan of the segment lengths; reset per-key cursors.
+  for (int k = tid; k < K; k += kThreads) s_cnt[k] = 0;
+  int carry = 0;
+  for (int c0 = 0; c0 < S; c0 += kThreads) {
+    const int s = c0 + tid;
+    const int v = s < S ? s_off[s] : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int before = carry;
+    int chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) before += s_wave[w];
+      chunk += s_wave[w];
+    }
+    if (s < S) {
+      const int excl = before + incl - v;
+      s_off[s] = excl;
+      a.seg_off[s] = excl;
+    }
+    carry += chunk;
+    __syncthreads();
+  }
+  if (tid == 0) s_off[S] = n;
+  __syncthreads();
+
+  // Pass 4: position of every row = segment offset + rows of the same key
+  // in earlier waves / chunks + rows of the same key in lower lanes.
+  // Wave 0 walks the 16 waves' group leaders in order, so the cross-wave
+  // part follows row order exactly.
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int i = c0 + tid;
+    const bool valid = i < n;
+    const int key = valid ? a.row_segment[i] : 0;
+    const uint64_t peers = match_key(key, valid);
+    const int local = __popcll(peers & lanemask_lt());
+    const bool leader = valid && local == 0;
+    s_lead_cnt[tid] = leader ? __popcll(peers) : 0;
+    s_lead_key[tid] = key;
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 0; w < kWaves; ++w) {
+        const int t = w * kWave + lane;
+        const int c = s_lead_cnt[t];
+        if (c > 0) {
+          const int k = s_lead_key[t];
+          const int b = s_cnt[k];
+          s_cnt[k] = b + c;
+          s_lead_base[t] = b;
+        }
+      }
+    }
+    __syncthreads();
+    if (valid) {
+      const int seg = -s_first[key] - 1;
+      const int lt = wave * kWave + (__ffsll((unsigned long long)peers) - 1);
+      const int pos = s_off[seg] + s_lead_base[lt] + local;
+      a.token_indices[pos] = i;
+      a.row_segment[i] = seg;
+    }
+    __syncthreads();
+  }
+
+  if (tid == 0) {
+    a.seg_off[S] = n;
+    *a.num_segments = S;
+    *a.status = s_bad;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
+                                 const int32_t *slot_rank, const float *slot_scale,
+                                 int32_t *token_indices, int32_t *row_segment, int32_t *seg_off,
+                                 int32_t *seg_slot, int32_t *seg_rank, float *seg_scale,
+                                 int32_t *num_segments, int32_t *status, hipStream_t stream) {
+  if (n_slots + 1 > kMaxKeys) return hipErrorInvalidValue;
+  BuildArgs a{row_slot, n, n_slots, r_max, slot_rank, slot_scale, token_indices, row_segment,
+              seg_off, seg_slot, seg_rank, seg_scale, num_segments, status};
+  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace lora

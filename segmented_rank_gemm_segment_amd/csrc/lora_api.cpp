@@ -1,0 +1,177 @@
+// C ABI of the multi-LoRA layer: host-side argument validation and launch.
+//
+// Validation happens before any HIP call, so every argument error returns
+// without touching device memory (and works on a machine with no GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/lora.h"
+#include "lora_kernels.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int32_t d) { return d == LORA_F32 || d == LORA_BF16; }
+
+lora_status check_pool(const lora_pool *pool) {
+  if (!pool) return LORA_ERR_NULL;
+  if (!valid_dtype(pool->dtype)) return LORA_ERR_DTYPE;
+  if (pool->r_max != 8 && pool->r_max != 16 && pool->r_max != 32 && pool->r_max != 64)
+    return LORA_ERR_RANK;
+  if (pool->rank_policy < LORA_RANK_EXACT || pool->rank_policy > LORA_RANK_PADDED)
+    return LORA_ERR_POLICY;
+  if (pool->n_slots < 1 || pool->n_slots > LORA_MAX_SLOTS) return LORA_ERR_SHAPE;
+  if (pool->d_in <= 0 || pool->d_out <= 0) return LORA_ERR_SHAPE;
+  if (pool->d_in % 8 || pool->d_out % 8) return LORA_ERR_ALIGN;
+  if (!pool->A || !pool->Bt || !pool->slot_rank || !pool->slot_scale) return LORA_ERR_NULL;
+  if (!aligned16(pool->A) || !aligned16(pool->Bt)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+int32_t seg_worst_case(int32_t n_rows, int32_t n_slots) {
+  return n_rows < n_slots + 1 ? n_rows : n_slots + 1;
+}
+
+lora_status check_segments(const lora_segments *seg, const lora_pool *pool) {
+  if (!seg) return LORA_ERR_NULL;
+  if (seg->n_rows < 0) return LORA_ERR_SHAPE;
+  if (seg->max_segments < 0) return LORA_ERR_SHAPE;
+  if (seg->max_segments < seg_worst_case(seg->n_rows, pool->n_slots)) return LORA_ERR_CAPACITY;
+  if (!seg->segment_offsets || !seg->segment_slots || !seg->segment_ranks ||
+      !seg->segment_scales || !seg->num_segments || !seg->status)
+    return LORA_ERR_NULL;
+  if (seg->n_rows > 0 && (!seg->token_indices || !seg->row_segment)) return LORA_ERR_NULL;
+  return LORA_OK;
+}
+
+lora_status check_matrix(const void *p, int64_t ld, int32_t width, int32_t rows) {
+  if (rows == 0) return LORA_OK;
+  if (!p) return LORA_ERR_NULL;
+  if (ld < width) return LORA_ERR_SHAPE;
+  if (ld % 8 || !aligned16(p)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+lora::SegView seg_view(const lora_segments *s) {
+  return lora::SegView{s->n_rows,        s->max_segments,  s->token_indices,
+                       s->row_segment,   s->segment_offsets, s->segment_slots,
+                       s->segment_ranks, s->segment_scales,  s->num_segments};
+}
+
+lora::PoolView pool_view(const lora_pool *p) {
+  return lora::PoolView{p->n_slots, p->r_max, p->d_in, p->d_out, p->dtype, p->rank_policy,
+                        p->A,       p->Bt};
+}
+
+lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char *lora_status_str(int32_t status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL: return "required pointer is NULL";
+    case LORA_ERR_SHAPE: return "size out of range or inconsistent";
+    case LORA_ERR_RANK: return "r_max must be 8, 16, 32 or 64";
+    case LORA_ERR_ALIGN: return "pointer not 16-byte aligned, or ld / d not a multiple of 8";
+    case LORA_ERR_DTYPE: return "unknown dtype";
+    case LORA_ERR_CAPACITY: return "segment arrays smaller than min(n_rows, n_slots + 1)";
+    case LORA_ERR_HIP: return "HIP runtime error at launch";
+    case LORA_ERR_POLICY: return "unknown rank policy";
+    default: return "unknown status";
+  }
+}
+
+lora_status lora_build_segments(const int32_t *row_slot, const lora_pool *pool,
+                                const lora_segments *seg, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  if (seg->n_rows > 0 && !row_slot) return LORA_ERR_NULL;
+  return hip_status(lora::launch_build_segments(
+      row_slot, seg->n_rows, pool->n_slots, pool->r_max, pool->slot_rank, pool->slot_scale,
+      seg->token_indices, seg->row_segment, seg->segment_offsets, seg->segment_slots,
+      seg->segment_ranks, seg->segment_scales, seg->num_segments, seg->status,
+      static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_shrink(const void *X, int64_t ldx, const lora_segments *seg,
+                        const lora_pool *pool, float *H, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  st = check_matrix(X, ldx, pool->d_in, seg->n_rows);
+  if (st != LORA_OK) return st;
+  if (seg->n_rows == 0) return LORA_OK;
+  if (!H) return LORA_ERR_NULL;
+  if (!aligned16(H)) return LORA_ERR_ALIGN;
+  return hip_status(lora::launch_shrink(X, ldx, seg_view(seg), pool_view(pool), H,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_expand(const float *H, const lora_segments *seg, const lora_pool *pool,
+                        void *Y, int64_t ldy, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, pool->d_out, seg->n_rows);
+  if (st != LORA_OK) return st;
+  if (seg->n_rows == 0) return LORA_OK;
+  if (!H) return LORA_ERR_NULL;
+  if (!aligned16(H)) return LORA_ERR_ALIGN;
+  return hip_status(lora::launch_expand(H, seg_view(seg), pool_view(pool), Y, ldy,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                           int64_t ldy, int32_t n_rows, int32_t d_in, int32_t d_out,
+                           int32_t dtype, void *stream) {
+  if (!valid_dtype(dtype)) return LORA_ERR_DTYPE;
+  if (n_rows < 0 || d_in <= 0 || d_out <= 0) return LORA_ERR_SHAPE;
+  if (d_in % 8 || d_out % 8) return LORA_ERR_ALIGN;
+  lora_status st = check_matrix(X, ldx, d_in, n_rows);
+  if (st != LORA_OK) return st;
+  st = check_matrix(W, ldw, d_in, d_out);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, d_out, n_rows);
+  if (st != LORA_OK) return st;
+  if (n_rows == 0) return LORA_OK;
+  return hip_status(lora::launch_gemm(X, ldx, W, ldw, Y, ldy, n_rows, d_in, d_out, dtype,
+                                      nullptr, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                              const float *H, const lora_segments *seg, const lora_pool *pool,
+                              void *Y, int64_t ldy, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  const int32_t n = seg->n_rows;
+  st = check_matrix(X, ldx, pool->d_in, n);
+  if (st != LORA_OK) return st;
+  st = check_matrix(W, ldw, pool->d_in, pool->d_out);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, pool->d_out, n);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  if (!H) return LORA_ERR_NULL;
+  if (!aligned16(H)) return LORA_ERR_ALIGN;
+  const lora::SegView sv = seg_view(seg);
+  const lora::PoolView pv = pool_view(pool);
+  return hip_status(lora::launch_gemm(X, ldx, W, ldw, Y, ldy, n, pool->d_in, pool->d_out,
+                                      pool->dtype, H, &sv, &pv,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

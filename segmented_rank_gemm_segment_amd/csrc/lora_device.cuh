@@ -1,0 +1,126 @@
+// Device-side helpers shared by the HIP kernels of the multi-LoRA layer.
+// gfx950 (CDNA4): 64-lane wavefronts, 160 KB LDS per CU, bf16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;  // storage bits
+typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE-754 binary32; widening is
+// a shift, narrowing rounds to nearest, ties to even, and keeps NaN quiet.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two packed bf16 (low half = first element) -> two floats.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// Element traits: 16-byte vectors hold 8 bf16 or 4 fp32.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void unpack(const uint4 &v, float *out) {
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float *in) {
+    uint4 v;
+    v.x = pack_bf16x2(in[0], in[1]);
+    v.y = pack_bf16x2(in[2], in[3]);
+    v.z = pack_bf16x2(in[4], in[5]);
+    v.w = pack_bf16x2(in[6], in[7]);
+    return v;
+  }
+  __device__ static __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ void store1(bf16_t *p, float f) { *p = (bf16_t)f32_to_bf16_rne(f); }
+};
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static __forceinline__ void unpack(const uint4 &v, float *out) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float *in) {
+    uint4 v;
+    v.x = __float_as_uint(in[0]); v.y = __float_as_uint(in[1]);
+    v.z = __float_as_uint(in[2]); v.w = __float_as_uint(in[3]);
+    return v;
+  }
+  __device__ static __forceinline__ float load1(const float *p) { return *p; }
+  __device__ static __forceinline__ void store1(float *p, float f) { *p = f; }
+};
+
+__device__ __forceinline__ uint4 ldg16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void stg16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Rank handling: the width a segment of true rank r is processed at.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rank_bucket(int r, int policy, int r_max) {
+  if (r <= 0) return 0;
+  int b;
+  if (policy == 2) {
+    b = r_max;                       // padded to the pool's maximum
+  } else if (policy == 1) {
+    b = r <= 16 ? 16 : 64;           // two buckets {8,16} and {32,64}
+  } else {
+    b = r <= 8 ? 8 : r <= 16 ? 16 : r <= 32 ? 32 : 64;
+  }
+  return b < r_max ? b : r_max;
+}
+
+// ---------------------------------------------------------------------------
+// Wave utilities.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Mask of the active lanes whose `key` equals this lane's (lanes with
+// valid == false take part in no group and get 0).  Loops once per distinct
+// key in the wave.
+__device__ __forceinline__ uint64_t match_key(int key, bool valid) {
+  uint64_t remaining = __ballot(valid);
+  uint64_t mine = 0;
+  while (remaining) {
+    const int leader = __ffsll((unsigned long long)remaining) - 1;
+    const int lk = __shfl(key, leader);
+    const uint64_t m = __ballot(valid && key == lk);
+    if (valid && key == lk) mine = m;
+    remaining &= ~m;
+  }
+  return mine;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+}  // namespace lora

@@ -1,0 +1,44 @@
+// Host-side launchers of the HIP kernels (internal to liblora).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+struct SegView {
+  int n_rows;
+  int max_segments;
+  const int32_t *token_indices;
+  const int32_t *row_segment;
+  const int32_t *seg_off;
+  const int32_t *seg_slot;
+  const int32_t *seg_rank;
+  const float *seg_scale;
+  const int32_t *num_segments;
+};
+
+struct PoolView {
+  int n_slots, r_max, d_in, d_out, dtype, policy;
+  const void *A;
+  const void *Bt;
+};
+
+hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
+                                 const int32_t *slot_rank, const float *slot_scale,
+                                 int32_t *token_indices, int32_t *row_segment, int32_t *seg_off,
+                                 int32_t *seg_slot, int32_t *seg_rank, float *seg_scale,
+                                 int32_t *num_segments, int32_t *status, hipStream_t stream);
+
+hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const PoolView &pool,
+                         float *H, hipStream_t stream);
+
+hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
+                         int64_t ldy, hipStream_t stream);
+
+// Y = X W^T (+ fused LoRA when seg/pool/H are given).
+hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                       int64_t ldy, int M, int K, int N, int dtype, const float *H,
+                       const SegView *seg, const PoolView *pool, hipStream_t stream);
+
+}  // namespace lora

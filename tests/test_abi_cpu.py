@@ -1,0 +1,162 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/lora.h declares, and rejects bad arguments on the host before
+any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import segmented_rank_gemm_segment_amd as srg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(srg.LIB_PATH):
+        from segmented_rank_gemm_segment_amd import build
+        build.build()
+    return srg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(lora_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
+              "lora_base_gemm", "lora_status_str", "lora_abi_version"):
+        assert n in names
+    assert set(names) == set(srg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", srg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.lora_abi_version() == srg.ABI_VERSION == 1
+    for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY):
+        s = L.lora_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert L.lora_status_str(12345).decode() == "unknown status"
+
+
+# fake, 16-byte aligned addresses: validation never dereferences them
+P = 0x10000
+
+
+def pool(**kw):
+    d = dict(n_slots=4, r_max=16, d_in=64, d_out=32, dtype=1, rank_policy=0,
+             A=P, Bt=P + 0x1000, slot_rank=P + 0x2000, slot_scale=P + 0x3000)
+    d.update(kw)
+    return srg.LoraPoolC(**d)
+
+
+def segs(**kw):
+    d = dict(n_rows=10, max_segments=5, token_indices=P + 0x4000, row_segment=P + 0x5000,
+             segment_offsets=P + 0x6000, segment_slots=P + 0x7000, segment_ranks=P + 0x8000,
+             segment_scales=P + 0x9000, num_segments=P + 0xA000, status=P + 0xB000)
+    d.update(kw)
+    return srg.LoraSegmentsC(**d)
+
+
+def shrink(L, p, s, X=P + 0xC000, ldx=64, H=P + 0xD000):
+    return L.lora_shrink(X, ldx, ctypes.byref(s), ctypes.byref(p), H, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(r_max=12), ERANK),
+    (dict(r_max=128), ERANK),
+    (dict(dtype=7), EDTYPE),
+    (dict(rank_policy=3), EPOLICY),
+    (dict(n_slots=0), ESHAPE),
+    (dict(n_slots=4096), ESHAPE),
+    (dict(d_in=0), ESHAPE),
+    (dict(d_in=60), EALIGN),
+    (dict(d_out=36), EALIGN),
+    (dict(A=0), ENULL),
+    (dict(slot_scale=0), ENULL),
+    (dict(Bt=P + 8), EALIGN),
+])
+def test_pool_validation(L, kw, code):
+    assert shrink(L, pool(**kw), segs()) == code
+    assert L.lora_build_segments(P, ctypes.byref(pool(**kw)), ctypes.byref(segs()), None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_rows=-1), ESHAPE),
+    (dict(max_segments=4), ECAP),           # worst case min(10, 4 + 1) = 5
+    (dict(token_indices=0), ENULL),
+    (dict(num_segments=0), ENULL),
+    (dict(status=0), ENULL),
+])
+def test_segment_validation(L, kw, code):
+    assert shrink(L, pool(), segs(**kw)) == code
+
+
+def test_capacity_bound_uses_rows_when_fewer():
+    # 3 rows can make at most 3 segments even with 4 slots + base
+    assert srg.lib().lora_shrink(P + 0xC000, 64, ctypes.byref(segs(n_rows=3, max_segments=2)),
+                                 ctypes.byref(pool()), P, None) == ECAP
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=0), ENULL),
+    (dict(X=P + 4), EALIGN),
+    (dict(ldx=60), ESHAPE),
+    (dict(ldx=68), EALIGN),
+    (dict(H=0), ENULL),
+    (dict(H=P + 8), EALIGN),
+])
+def test_shrink_matrix_validation(L, kw, code):
+    assert shrink(L, pool(), segs(), **kw) == code
+
+
+def test_empty_batch_is_a_noop_without_launch(L):
+    s = segs(n_rows=0, max_segments=0, token_indices=0, row_segment=0)
+    assert shrink(L, pool(), s, X=0, H=0) == OK
+    assert L.lora_expand(0, ctypes.byref(s), ctypes.byref(pool()), 0, 32, None) == OK
+    assert L.lora_linear_fused(0, 64, P, 64, 0, ctypes.byref(s), ctypes.byref(pool()), 0, 32,
+                               None) == OK
+    assert L.lora_base_gemm(0, 64, P, 64, 0, 32, 0, 64, 32, 1, None) == OK
+
+
+def test_expand_and_fused_validation(L):
+    p, s = pool(), segs()
+    assert L.lora_expand(P, ctypes.byref(s), ctypes.byref(p), P, 24, None) == ESHAPE   # ldy < d_out
+    assert L.lora_expand(P, ctypes.byref(s), ctypes.byref(p), 0, 32, None) == ENULL
+    assert L.lora_linear_fused(P, 64, 0, 64, P, ctypes.byref(s), ctypes.byref(p), P, 32,
+                               None) == ENULL       # W
+    assert L.lora_linear_fused(P, 64, P, 56, P, ctypes.byref(s), ctypes.byref(p), P, 32,
+                               None) == ESHAPE      # ldw < d_in
+    assert L.lora_linear_fused(P, 64, P, 64, 0, ctypes.byref(s), ctypes.byref(p), P, 32,
+                               None) == ENULL       # H
+
+
+def test_base_gemm_validation(L):
+    assert L.lora_base_gemm(P, 64, P, 64, P, 32, 10, 64, 32, 5, None) == EDTYPE
+    assert L.lora_base_gemm(P, 64, P, 64, P, 32, -1, 64, 32, 1, None) == ESHAPE
+    assert L.lora_base_gemm(P, 64, P, 64, P, 32, 10, 60, 32, 1, None) == EALIGN
+    assert L.lora_base_gemm(P, 64, 0, 64, P, 32, 10, 64, 32, 1, None) == ENULL
+    assert L.lora_base_gemm(P, 64, P, 64, P + 2, 32, 10, 64, 32, 1, None) == EALIGN
+
+
+def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(srg, "_lib", None)
+    monkeypatch.setattr(srg, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        srg.lib()

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Metadata and token mapping must match bit for bit; values within the
+normwise tolerance max|got - ref| / max|ref| <= 1e-2 for bf16 storage with
+fp32 accumulation and <= 1e-5 for fp32, applied separately to H, Y (fused
+and separate paths) and Delta Y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segmented_rank_gemm_segment_amd as srg
+import workloads as wl
+from gpu_harness import (DEV, base_rows_bitwise, check_metadata, check_values, run_hip,
+                         sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    srg.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- the configurations
+def test_cfg1_tiny_f32():
+    w = wl.make_config(1)
+    say("cfg1", w.n, w.d_in, w.d_out)
+    r = run_hip(w)
+    ref = check_metadata(w, r)
+    assert ref["segment_offsets"].tolist() == [0, 8, 12, 28, 32]
+    e = check_values(w, r)
+    base_rows_bitwise(w, r)
+    say("cfg1 errors", e)
+
+
+def test_cfg2_decode_bf16():
+    w = wl.make_config(2)
+    say("cfg2", w.n, w.d_in, w.d_out)
+    r = run_hip(w)
+    check_metadata(w, r)
+    e = check_values(w, r)
+    assert base_rows_bitwise(w, r) > 0
+    say("cfg2 errors", e)
+
+
+_CACHE = {}
+
+
+def _cfg4():
+    if "cfg4" not in _CACHE:
+        _CACHE["cfg4"] = wl.make_config(4)
+    return _CACHE["cfg4"]
+
+
+@pytest.mark.parametrize("policy", ["exact", "two_buckets", "padded"])
+def test_cfg4_skewed_decode_bf16(policy):
+    w = _cfg4()
+    say("cfg4", policy, w.n, w.d_in, w.d_out, w.n_slots)
+    r = run_hip(w, policy)
+    check_metadata(w, r)
+    e = check_values(w, r)
+    say("cfg4 errors", policy, e)
+
+
+def test_cfg3_prefill_structure_small():
+    """Configuration 3's structure (d 4096 -> 14336, ranks 8..64, request 7
+    base-only) with short, ragged requests so the oracle runs every row."""
+    w = wl._cfg3(lengths_override=[300, 17, 150, 1, 64, 200, 33, 90])
+    say("cfg3 small", w.n, w.d_in, w.d_out)
+    r = run_hip(w)
+    check_metadata(w, r)
+    e = check_values(w, r)
+    assert base_rows_bitwise(w, r) == 90
+    say("cfg3 small errors", e)
+
+
+def test_cfg3_prefill_full_sampled():
+    w = wl.make_config(3)
+    say("cfg3 full", w.n, w.d_in, w.d_out, w.meta)
+    r = run_hip(w, separate=False)
+    ref = check_metadata(w, r)
+    rows = sample_rows(w, ref, 512)
+    e = check_values(w, r, rows=rows)
+    assert torch.isfinite(r.Yf.float()).all()
+    say("cfg3 full errors (sampled rows)", len(rows), e)
+
+
+@pytest.mark.parametrize("proj", [p[0] for p in wl.CFG5_PROJECTIONS])
+def test_cfg5_projection_sampled(proj):
+    w = wl.cfg5_projection(proj)
+    say("cfg5", proj, w.n, w.d_in, w.d_out)
+    r = run_hip(w, separate=False)
+    ref = check_metadata(w, r)
+    rows = sample_rows(w, ref, 512, extra=range(2048, 2304))
+    e = check_values(w, r, rows=rows)
+    assert torch.isfinite(r.Yf.float()).all()
+    say("cfg5 errors", proj, len(rows), e)
+
+
+# ---------------------------------------------------------------- structure and edge cases
+CASES = [
+    # seed, n, d_in, d_out, n_slots, r_max, p_base, dtype, runs
+    (101, 1, 64, 72, 3, 8, 0.0, "bf16", False),
+    (102, 7, 136, 200, 5, 16, 0.3, "bf16", False),
+    (103, 300, 520, 264, 40, 64, 0.1, "bf16", False),
+    (104, 333, 256, 384, 6, 32, 0.2, "bf16", True),
+    (105, 1500, 128, 136, 9, 64, 0.05, "bf16", True),
+    (106, 257, 96, 88, 300, 16, 0.5, "bf16", False),
+    (107, 70, 64, 64, 4, 64, 0.1, "f32", True),
+    (108, 513, 200, 120, 17, 32, 0.1, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}" for c in CASES])
+@pytest.mark.parametrize("policy", ["exact", "padded"])
+def test_random_cases(case, policy):
+    seed, n, d_in, d_out, n_slots, r_max, p_base, dtype, runs = case
+    say("random", case, policy)
+    w = wl.make_random(seed, n, d_in, d_out, n_slots, r_max, p_base=p_base, dtype=dtype, runs=runs)
+    r = run_hip(w, policy)
+    check_metadata(w, r)
+    check_values(w, r)
+    base_rows_bitwise(w, r)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fingerprint_mapping_exact(dtype):
+    """Fingerprint adapters: the increment of a row on slot a is exactly
+    s_a (a + 1) x[a mod d_in] (exact in fp32 here), so the expand into zeros
+    must equal its rounding bit for bit in every column."""
+    w = wl.make_fingerprint(7, n=400, d_in=256, d_out=128, n_slots=60, r_max=32, dtype=dtype)
+    r = run_hip(w)
+    check_metadata(w, r)
+    check_values(w, r)
+    X = oracle.decode(w.X, dtype)
+    exp = np.zeros((w.n,), dtype=np.float64)
+    for i in range(w.n):
+        a = int(w.row_slot[i])
+        if a >= 0:
+            exp[i] = 16.0 / int(w.slot_rank[a]) * (a + 1) * X[i, a % w.d_in]
+    exp32 = exp.astype(np.float32)
+    assert np.array_equal(exp32.astype(np.float64), exp)
+    want = wl.bf16_bits_rne(exp32) if dtype == "bf16" else exp32.view(np.uint32)
+    if dtype == "bf16":
+        got = r.dY.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got = r.dY.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, np.repeat(want[:, None], w.d_out, axis=1))
+
+
+def test_invalid_rows_are_base_and_counted():
+    w = wl.make_random(21, n=200, d_in=64, d_out=64, n_slots=10, r_max=16, dtype="bf16")
+    w.slot_rank[3] = 40            # > r_max: every row on slot 3 is demoted
+    w.row_slot[5] = 10             # >= n_slots
+    w.row_slot[6] = -2
+    w.row_slot[7] = 1 << 20
+    r = run_hip(w)
+    ref = check_metadata(w, r)
+    assert ref["status"] >= 3 and r.meta["status"] == ref["status"]
+    check_values(w, r)
+    base_rows_bitwise(w, r)
+
+
+def test_empty_batch():
+    w = wl.make_random(22, n=0, d_in=64, d_out=64, n_slots=3, r_max=8, dtype="bf16")
+    r = run_hip(w)
+    assert r.meta["num_segments"] == 0 and r.meta["status"] == 0
+    assert r.seg.segment_offsets[0].item() == 0
+
+
+def test_all_rows_one_adapter_and_all_base():
+    w = wl.make_random(23, n=130, d_in=128, d_out=96, n_slots=5, r_max=64, dtype="bf16")
+    w.row_slot[:] = 2
+    r = run_hip(w)
+    m = check_metadata(w, r)
+    assert int(m["num_segments"]) == 1
+    check_values(w, r)
+    w.row_slot[:] = -1
+    r = run_hip(w)
+    check_metadata(w, r)
+    check_values(w, r)
+    assert torch.equal(r.Yf, r.Yb)
+
+
+def test_max_slots_pool():
+    n_slots = srg.MAX_SLOTS
+    w = wl.make_random(24, n=2000, d_in=64, d_out=64, n_slots=n_slots, r_max=8, dtype="bf16",
+                       p_base=0.05)
+    r = run_hip(w)
+    check_metadata(w, r)
+    check_values(w, r)
+
+
+def test_policies_give_identical_bits():
+    w = wl.make_random(25, n=600, d_in=256, d_out=192, n_slots=30, r_max=64, dtype="bf16")
+    outs = [run_hip(w, p) for p in ("exact", "two_buckets", "padded")]
+    for o in outs[1:]:
+        assert torch.equal(o.H.nan_to_num(0), outs[0].H.nan_to_num(0))
+        assert torch.equal(o.Yf, outs[0].Yf)
+        assert torch.equal(o.Ys, outs[0].Ys)
+
+
+def test_slot_relocation_and_determinism():
+    w = wl.make_random(26, n=500, d_in=192, d_out=128, n_slots=12, r_max=32, dtype="bf16")
+    a = run_hip(w)
+    b = run_hip(w)
+    assert torch.equal(a.Yf, b.Yf) and torch.equal(a.Ys, b.Ys)
+    perm = np.random.default_rng(3).permutation(w.n_slots)
+    c = wl.Workload(**{**w.__dict__})
+    c.A = np.empty_like(w.A)
+    c.Bt = np.empty_like(w.Bt)
+    c.slot_rank = np.empty_like(w.slot_rank)
+    for s in range(w.n_slots):
+        c.A[perm[s]] = w.A[s]
+        c.Bt[perm[s]] = w.Bt[s]
+        c.slot_rank[perm[s]] = w.slot_rank[s]
+    c.row_slot = np.where(w.row_slot < 0, -1, perm[np.maximum(w.row_slot, 0)]).astype(np.int32)
+    rc = run_hip(c)
+    assert torch.equal(rc.Yf, a.Yf) and torch.equal(rc.Ys, a.Ys)
+
+
+def test_row_permutation_permutes_output():
+    w = wl.make_random(27, n=300, d_in=128, d_out=128, n_slots=20, r_max=16, dtype="bf16")
+    a = run_hip(w)
+    perm = np.random.default_rng(4).permutation(w.n)
+    c = wl.Workload(**{**w.__dict__})
+    c.X = w.X[perm]
+    c.row_slot = w.row_slot[perm]
+    rc = run_hip(c)
+    tp = torch.as_tensor(perm, device=DEV)
+    assert torch.equal(rc.Yf, a.Yf[tp]) and torch.equal(rc.Ys, a.Ys[tp])
+
+
+def test_graph_replay_matches_eager():
+    """The whole step captured in a HIP graph: every replay (with eager work
+    and synchronisation between replays) equals the eager result bit for bit."""
+    w = wl.make_random(28, n=260, d_in=256, d_out=192, n_slots=40, r_max=16, dtype="bf16")
+    eager = run_hip(w, separate=False)
+    d = eager.d
+    pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha)
+    seg = srg.Segments(w.n, w.n_slots, DEV)
+    H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=DEV)
+    Y = torch.zeros((w.n, w.d_out), dtype=torch.bfloat16, device=DEV)
+    srg.lora_build_segments(d["row_slot"], pool, seg)     # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        srg.lora_build_segments(d["row_slot"], pool, seg)
+        srg.lora_shrink(d["X"], seg, pool, H)
+        srg.lora_linear_fused(d["X"], d["W"], H, seg, pool, Y)
+    for rep in range(4):
+        Y.fill_(0)
+        H.fill_(0)
+        seg.token_indices.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager.Yf), rep
+        assert torch.equal(seg.token_indices[:w.n].cpu(),
+                           torch.as_tensor(eager.meta["token_indices"])), rep
+        _ = (Y.float() * 2).sum().item()                   # eager work between replays

@@ -323,6 +323,9 @@ def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_m
     a row that picks up another slot's weights is off by a visible amount."""
     w = make_random(seed, n, d_in, d_out, n_slots, r_max, ranks=ranks, p_base=p_base,
                     dtype=dtype, pad="nan")
+    if dtype == "f32":
+        # keep x on the bf16 grid so that s_a (a + 1) x is exact in fp32 too
+        w.X = bf16_bits_to_f32(bf16_bits_rne(w.X))
     et = np.uint16 if dtype == "bf16" else np.float32
     for a in range(n_slots):
         r = int(w.slot_rank[a])
@@ -334,3 +337,29 @@ def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_m
         w.Bt[a, :r] = _encode(rowsB, dtype).astype(et)
     w.name = f"fingerprint_s{seed}"
     return w
+
+
+# --------------------------------------------------------------------------
+# torch views (device placement only)
+# --------------------------------------------------------------------------
+def to_torch(arr: np.ndarray, dtype: str, device="cpu"):
+    """numpy storage -> torch tensor of the same bits (bf16 from uint16)."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def device_tensors(w: Workload, device) -> Dict:
+    """X, W, A, Bt, row_slot, slot_rank of a workload on `device`."""
+    import torch
+    return {
+        "X": to_torch(w.X, w.dtype, device),
+        "W": to_torch(w.W, w.dtype, device),
+        "A": to_torch(w.A, w.dtype, device),
+        "Bt": to_torch(w.Bt, w.dtype, device),
+        "row_slot": torch.from_numpy(np.ascontiguousarray(w.row_slot, dtype=np.int32)).to(device),
+        "slot_rank": torch.from_numpy(np.ascontiguousarray(w.slot_rank, dtype=np.int32)).to(device),
+    }
