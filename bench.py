@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
-    p.add_argument("--path", choices=["fused", "separate"], default="fused")
+    p.add_argument("--path", choices=["auto", "fused", "separate"], default="auto",
+                   help="auto: time both step variants and report the faster")
     p.add_argument("--policy", choices=["exact", "two_buckets", "padded"], default="exact")
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="total size of the rotated copies of the layer tensors")
@@ -200,7 +201,7 @@ def time_calls(fn_seq, layers, iters, warmup, use_graph):
     return ev0.elapsed_time(ev1) * 1e-3 / iters, wall
 
 
-def measure(w, path, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
+def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
             device="cuda:0"):
     import torch
     L0 = Layer(w, policy, device)
@@ -210,13 +211,14 @@ def measure(w, path, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
         k_build(L)
         k_shrink(L)
     torch.cuda.synchronize()
-    step_s, wall = time_calls(STEP[path], layers, steps, warmup, use_graph)
+    step = {}
+    for p in paths:
+        step[p] = time_calls(STEP[p], layers, steps, warmup, use_graph)
     kl = kernel_loops or steps
     per_kernel = {}
     for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
-    return {"step_s": step_s, "wall_s": wall, "per_kernel_s": per_kernel, "copies": copies,
-            "layer_bytes": L0.nbytes}
+    return {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
 
 
 def kernel_table(fig, per_kernel, dtype):
@@ -292,15 +294,15 @@ def main():
 
     w = wl.make_config(args.config)
     fig = work_figures(w)
-    m = measure(w, args.path, args.policy, args.steps, args.warmup, args.rotate_mb,
+    paths = ["fused", "separate"] if args.path == "auto" else [args.path]
+    m = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
                 args.kernel_loops, not args.eager)
+    path = min(paths, key=lambda p: m["step"][p][0])
+    step_s, wall = m["step"][path]
     kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
-    main_k = "fused" if args.path == "fused" else max(("base", "expand", "shrink"),
-                                                      key=lambda k: m["per_kernel_s"][k])
-    if args.path == "fused":
-        main_k = max(("fused", "shrink", "build"), key=lambda k: m["per_kernel_s"][k])
+    cand = ("build", "shrink", "fused") if path == "fused" else ("build", "shrink", "base", "expand")
+    main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)
-    step_s = m["step_s"]
     sh, ex = m["per_kernel_s"]["shrink"], m["per_kernel_s"]["expand"]
     se_bytes = fig["bytes"]["shrink"] + fig["bytes"]["expand"]
     out = {
@@ -316,7 +318,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded normals; mapping per the workload recipe)",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "path": args.path,
+        "config": {"workload": WORKLOAD_NAMES[args.config], "path": path,
                    "rank_policy": args.policy, "rows": w.n, "lora_rows": fig["n_lora_rows"],
                    "distinct_adapters": fig["distinct_adapters"],
                    "rotated_copies": m["copies"], "launch": "eager" if args.eager else "hip_graph",
@@ -326,18 +328,20 @@ def main():
                           "hbm_frac": round(se_bytes / (sh + ex) / 1e9 / HBM_PEAK_GBS, 4),
                           "us": round((sh + ex) * 1e6, 3)},
         "kernels": kt,
-        "host_wall_s": round(m["wall_s"], 4),
+        "step_us_by_path": {p: round(m["step"][p][0] * 1e6, 3) for p in paths},
+        "host_wall_s": round(wall, 4),
     }
     if not args.no_prefill and args.config != 3:
         w3 = wl.make_config(3)
         f3 = work_figures(w3)
         st3 = max(5, args.steps // 10)
-        m3 = measure(w3, "fused", args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
+        m3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
                      not args.eager)
         k3 = kernel_table(f3, m3["per_kernel_s"], "bf16")
         out["prefill"] = {
-            "workload": WORKLOAD_NAMES[3], "rows": w3.n, "tokens_s": round(w3.n / m3["step_s"], 1),
-            "ms_per_step": round(m3["step_s"] * 1e3, 4),
+            "workload": WORKLOAD_NAMES[3], "rows": w3.n,
+            "tokens_s": round(w3.n / m3["step"]["fused"][0], 1),
+            "ms_per_step": round(m3["step"]["fused"][0] * 1e3, 4), "path": "fused",
             "fused_gemm": roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
             "shrink_expand": {"GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
                                             (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1)},

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "liblora.so")
 SOURCES = ["build_segments.hip", "shrink_expand.hip", "gemm.hip", "lora_api.cpp"]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 # Packed fp32 VALU forms stay off in every device pass.
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -35,23 +35,70 @@ struct BuildArgs {
   int32_t *num_segments, *status;
 };
 
+// Keys of the first kRegChunks chunks of rows stay in registers between the
+// passes; rows past that keep theirs in row_segment (read back by the same
+// thread).  Slot tables are staged in LDS once.
+constexpr int kRegChunks = 4;
+
+struct Tables {
+  int *first, *cnt, *off, *rank, *lead_key, *lead_cnt, *lead_base, *wave;
+  float *scale;
+};
+
+// Key of row i: validated slot + 1; 0 = base-only (also for a bad slot or
+// rank, counted in *bad).
+__device__ __forceinline__ int row_key(int slot, const BuildArgs &a, const Tables &t, bool &bad) {
+  if (slot == -1) return 0;
+  if (slot < -1 || slot >= a.n_slots) {
+    bad = true;
+    return 0;
+  }
+  const int r = t.rank[slot];
+  if (r < 0 || r > a.r_max) {
+    bad = true;
+    return 0;
+  }
+  return slot + 1;
+}
+
 __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   __shared__ int s_first[kMaxKeys];  // first row of a key; later -(segment + 1)
   __shared__ int s_cnt[kMaxKeys];    // rows of a key; later the per-key cursor
   __shared__ int s_off[kMaxKeys + 1];// segment lengths, then exclusive offsets
+  __shared__ int s_rank[kMaxKeys];   // slot_rank staged
+  __shared__ float s_scale[kMaxKeys];// slot_scale staged
   __shared__ int s_lead_key[kThreads];
   __shared__ int s_lead_cnt[kThreads];
   __shared__ int s_lead_base[kThreads];
   __shared__ int s_wave[kWaves];
   __shared__ int s_bad, s_total;
 
+  // the block is launched with 64..1024 threads (enough for the batch);
+  // rows are visited in chunks of one block
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int nwaves = nthr / kWave;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int K = a.n_slots + 1;
   const int n = a.n;
+  const int nchunks = (n + nthr - 1) / nthr;
+  const Tables t{s_first, s_cnt, s_off, s_rank, s_lead_key, s_lead_cnt, s_lead_base, s_wave,
+                 s_scale};
 
-  for (int k = tid; k < K; k += kThreads) {
+  // Stage 0: one round of global loads: row slots of the register chunks and
+  // the slot tables.
+  int keyreg[kRegChunks];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int i = c * nthr + tid;
+    keyreg[c] = i < n ? a.row_slot[i] : -1;
+  }
+  for (int k = tid; k < a.n_slots; k += nthr) {
+    s_rank[k] = a.slot_rank[k];
+    s_scale[k] = a.slot_scale[k];
+  }
+  for (int k = tid; k < K; k += nthr) {
     s_first[k] = INT_MAX;
     s_cnt[k] = 0;
   }
@@ -61,28 +108,14 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // Pass 1: validate every row, keep its key (slot + 1, 0 = base-only) in
-  // row_segment for the later passes (same thread reads it back), and
-  // gather first row and row count per key.  One LDS atomic per group of
-  // equal keys in a wave; min/add commute, so the result is exact.
-  for (int c0 = 0; c0 < n; c0 += kThreads) {
-    const int i = c0 + tid;
+  // Pass 1: validate, remember keys, first row and row count per key.  One
+  // LDS atomic per group of equal keys in a wave; min/add commute, so the
+  // result does not depend on the order they land in.
+  auto pass1 = [&](int c, int slot) -> int {
+    const int i = c * nthr + tid;
     const bool valid = i < n;
-    int key = 0;
     bool bad = false;
-    if (valid) {
-      const int slot = a.row_slot[i];
-      if (slot != -1) {
-        if (slot < -1 || slot >= a.n_slots) {
-          bad = true;
-        } else {
-          const int r = a.slot_rank[slot];
-          if (r < 0 || r > a.r_max) bad = true;
-          else key = slot + 1;
-        }
-      }
-      a.row_segment[i] = key;
-    }
+    const int key = valid ? row_key(slot, a, t, bad) : 0;
     const uint64_t badmask = __ballot(bad);
     if (lane == 0 && badmask) atomicAdd(&s_bad, __popcll(badmask));
     const uint64_t peers = match_key(key, valid);
@@ -90,16 +123,23 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
       atomicMin(&s_first[key], i);
       atomicAdd(&s_cnt[key], __popcll(peers));
     }
+    return key;
+  };
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c < nchunks) keyreg[c] = pass1(c, keyreg[c]);
+  for (int c = kRegChunks; c < nchunks; ++c) {
+    const int i = c * nthr + tid;
+    const int key = pass1(c, i < n ? a.row_slot[i] : -1);
+    if (i < n) a.row_segment[i] = key;
   }
   __syncthreads();
 
   // Pass 2: a row is the head of its segment iff it is its key's first row.
-  // Segment ids are the running count of heads, so segments come in order
-  // of first appearance.
-  for (int c0 = 0; c0 < n; c0 += kThreads) {
-    const int i = c0 + tid;
+  // Segment ids are the running count of heads: first-appearance order.
+  auto pass2 = [&](int c, int key) {
+    const int i = c * nthr + tid;
     const bool valid = i < n;
-    const int key = valid ? a.row_segment[i] : 0;
     const bool head = valid && s_first[key] == i;
     const uint64_t hm = __ballot(head);
     if (lane == 0) s_wave[wave] = __popcll(hm);
@@ -109,40 +149,47 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
     if (head) {
       const int s = before + __popcll(hm & lanemask_lt());
       const int slot = key - 1;
-      const int r = key == 0 ? 0 : a.slot_rank[slot];
+      const int r = key == 0 ? 0 : s_rank[slot];
       a.seg_slot[s] = slot;
       a.seg_rank[s] = r;
-      a.seg_scale[s] = r > 0 ? a.slot_scale[slot] : 0.0f;
+      a.seg_scale[s] = r > 0 ? s_scale[slot] : 0.0f;
       s_off[s] = s_cnt[key];
       s_first[key] = -(s + 1);
     }
     __syncthreads();
     if (tid == 0) {
-      int t = 0;
-      for (int w = 0; w < kWaves; ++w) t += s_wave[w];
-      s_total += t;
+      int tot = 0;
+      for (int w = 0; w < nwaves; ++w) tot += s_wave[w];
+      s_total += tot;
     }
     __syncthreads();
+  };
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c < nchunks) pass2(c, keyreg[c]);
+  for (int c = kRegChunks; c < nchunks; ++c) {
+    const int i = c * nthr + tid;
+    pass2(c, i < n ? a.row_segment[i] : 0);
   }
   const int S = s_total;
 
   // Pass 3: exclusive scan of the segment lengths; reset per-key cursors.
-  for (int k = tid; k < K; k += kThreads) s_cnt[k] = 0;
+  for (int k = tid; k < K; k += nthr) s_cnt[k] = 0;
   int carry = 0;
-  for (int c0 = 0; c0 < S; c0 += kThreads) {
+  for (int c0 = 0; c0 < S; c0 += nthr) {
     const int s = c0 + tid;
     const int v = s < S ? s_off[s] : 0;
     int incl = v;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl, d);
-      if (lane >= d) incl += t;
+      const int u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
     }
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
     int before = carry;
     int chunk = 0;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < nwaves; ++w) {
       if (w < wave) before += s_wave[w];
       chunk += s_wave[w];
     }
@@ -157,29 +204,29 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   if (tid == 0) s_off[S] = n;
   __syncthreads();
 
-  // Pass 4: position of every row = segment offset + rows of the same key
-  // in earlier waves / chunks + rows of the same key in lower lanes.
-  // Wave 0 walks the 16 waves' group leaders in order, so the cross-wave
-  // part follows row order exactly.
-  for (int c0 = 0; c0 < n; c0 += kThreads) {
-    const int i = c0 + tid;
+  // Pass 4: position = segment offset + rows of the same key in earlier
+  // chunks and waves + rows of the same key in lower lanes.  Wave 0 walks
+  // the 16 waves' group leaders in order, so the cross-wave part follows
+  // row order exactly.
+  auto pass4 = [&](int c, int key) {
+    const int i = c * nthr + tid;
     const bool valid = i < n;
-    const int key = valid ? a.row_segment[i] : 0;
     const uint64_t peers = match_key(key, valid);
     const int local = __popcll(peers & lanemask_lt());
-    const bool leader = valid && local == 0;
-    s_lead_cnt[tid] = leader ? __popcll(peers) : 0;
+    s_lead_cnt[tid] = (valid && local == 0) ? __popcll(peers) : 0;
     s_lead_key[tid] = key;
     __syncthreads();
     if (wave == 0) {
-      for (int w = 0; w < kWaves; ++w) {
-        const int t = w * kWave + lane;
-        const int c = s_lead_cnt[t];
-        if (c > 0) {
-          const int k = s_lead_key[t];
+      // waves past the last row of the chunk hold no leaders
+      const int wend = min(nwaves, (n - c * nthr + kWave - 1) / kWave);
+      for (int w = 0; w < wend; ++w) {
+        const int u = w * kWave + lane;
+        const int cnt = s_lead_cnt[u];
+        if (cnt > 0) {
+          const int k = s_lead_key[u];
           const int b = s_cnt[k];
-          s_cnt[k] = b + c;
-          s_lead_base[t] = b;
+          s_cnt[k] = b + cnt;
+          s_lead_base[u] = b;
         }
       }
     }
@@ -192,6 +239,13 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
       a.row_segment[i] = seg;
     }
     __syncthreads();
+  };
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c < nchunks) pass4(c, keyreg[c]);
+  for (int c = kRegChunks; c < nchunks; ++c) {
+    const int i = c * nthr + tid;
+    pass4(c, i < n ? a.row_segment[i] : 0);
   }
 
   if (tid == 0) {
@@ -211,7 +265,10 @@ hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, in
   if (n_slots + 1 > kMaxKeys) return hipErrorInvalidValue;
   BuildArgs a{row_slot, n, n_slots, r_max, slot_rank, slot_scale, token_indices, row_segment,
               seg_off, seg_slot, seg_rank, seg_scale, num_segments, status};
-  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  // one wave per 64 rows up to 16 waves
+  int threads = ((n + kWave - 1) / kWave) * kWave;
+  threads = threads < kWave ? kWave : (threads > kThreads ? kThreads : threads);
+  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

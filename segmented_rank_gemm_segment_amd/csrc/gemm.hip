@@ -8,18 +8,21 @@
 // low-rank product into the base output follows the epilogue-fusion
 // structure of the ybb.press multi-LoRA serving article, section 5.3.
 //
-// bf16: MFMA v_mfma_f32_32x32x16_bf16 (gfx950), block tiles staged through
-// LDS with double buffering, one barrier per K step.  Both operands are
-// K-contiguous (X rows and nn.Linear W rows), so global loads are 16-byte
-// vectors along K and LDS rows are padded by 16 bytes, which keeps the
-// 16-byte fragment reads of 8 consecutive rows on distinct banks.
+// bf16: MFMA v_mfma_f32_32x32x16_bf16 (gfx950).  Both operands are
+// K-contiguous (X rows and nn.Linear W rows).  Tiles stream into LDS with
+// direct global->LDS loads through a multi-stage ring, so several K steps
+// are in flight per workgroup; LDS rows are XOR-swizzled in 16-byte chunks
+// so fragment reads are bank-conflict free.  Tiles are ordered per XCD.
 //
-// Fused epilogue: the rows of an output tile may belong to several segments.
-// For each distinct LoRA segment u in the tile, Bt_u[0:R][tile columns] is
-// staged in LDS (K-contiguous per column), the scaled H rows of u form the
-// A operand (split into a bf16 high part and a bf16 remainder, so H keeps
-// about 16 significant bits), and the MFMA result is added only to rows of
-// u.  Every row gets exactly its own segment's increment.
+// Fused LoRA: the rows of an output tile may belong to several segments.
+// Before the K loop, for each distinct LoRA segment u among a wavefront's
+// rows, the scaled H rows of u (split into a bf16 high part and a bf16
+// remainder, so H keeps about 16 significant bits) times Bt_u are
+// accumulated by MFMA into the zeroed accumulators, zero rows standing in
+// for rows of other segments.  Every row gets exactly its own segment's
+// increment, added in fp32 and rounded once with the base product.
+#include <climits>
+
 #include "lora_device.cuh"
 #include "lora_kernels.h"
 
@@ -44,192 +47,280 @@ struct GemmArgs {
   int r_max, policy;
 };
 
-constexpr int kBK = 64;
-constexpr int kLdsStride = kBK + 8;  // elements; +16 bytes per row
+// Tile configurations <BM, BN, waves along M, waves along N, LDS stages>:
+// small-M (decode-like) batches and large batches.
+#ifndef LORA_GEMM_SMALL
+#define LORA_GEMM_SMALL 64, 64, 2, 2, 6
+#endif
+#ifndef LORA_GEMM_LARGE
+#define LORA_GEMM_LARGE 256, 256, 2, 4, 2
+#endif
+#ifndef LORA_GEMM_SMALL_M
+#define LORA_GEMM_SMALL_M 512
+#endif
 
-template <int BM, int BN>
-constexpr int lds_bytes_main() { return 2 * (BM + BN) * kLdsStride * 2; }
-template <int BM, int BN>
-constexpr int lds_bytes_lora() { return 2 * BM * 4 + 16 + BN * (64 + 8) * 2; }
-template <int BM, int BN>
-constexpr int lds_bytes() {
-  return lds_bytes_main<BM, BN>() > lds_bytes_lora<BM, BN>() ? lds_bytes_main<BM, BN>()
-                                                             : lds_bytes_lora<BM, BN>();
+constexpr int kBK = 64;           // K per stage: one 128-byte row chunk per operand row
+constexpr int kLoraRS = 64 + 8;   // LDS row stride (elements) of the staged Bt tile
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4).  Each
+// instruction moves 64 lanes x 16 bytes into 1 KB of LDS starting at M0.
+// Issued through inline asm so that the compiler does not add conservative
+// waits on them; completion is tracked by hand with s_waitcnt vmcnt.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
+
+__device__ __forceinline__ void dma16(uint32_t m0, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding, then LDS-fence and barrier the workgroup.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int IPW>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  // this wave's DMAs of the `ahead` later stages may stay in flight
+  switch (ahead) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<(IPW < 63 ? IPW : 63)>(); break;
+    case 2: vm_wait<(2 * IPW < 63 ? 2 * IPW : 63)>(); break;
+    case 3: vm_wait<(3 * IPW < 63 ? 3 * IPW : 63)>(); break;
+    case 4: vm_wait<(4 * IPW < 63 ? 4 * IPW : 63)>(); break;
+    case 5: vm_wait<(5 * IPW < 63 ? 5 * IPW : 63)>(); break;
+    default: vm_wait<(6 * IPW < 63 ? 6 * IPW : 63)>(); break;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct TileCfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int T = NW * kWave;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW;  // 1 KB DMA instructions per wave
+  static constexpr int IPW = AI + BI;
+  static constexpr int STAGE = (BM + BN) * kBK * 2;        // bytes
+  static constexpr int LDS_MAIN = STAGES * STAGE;
+  static constexpr int LDS_LORA = 2 * BM * 4 + 16 + BN * kLoraRS * 2;
+  static constexpr int LDS = LDS_MAIN > LDS_LORA ? LDS_MAIN : LDS_LORA;
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA split");
+  static_assert(STAGES >= 2 && STAGES - 2 <= 6 && (STAGES - 2) * IPW <= 63, "pipeline depth");
+};
 
 __device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }
 
 // Row of element v (0..15) of a 32x32 MFMA accumulator held by lane l
-// (column is l % 32).
+// (its column is l % 32).
 __device__ __forceinline__ int acc_row(int v, int l) { return (v >> 2) * 8 + (l >> 5) * 4 + (v & 3); }
 
-template <int BM, int BN, int WM, int WN, bool LORA>
+// LDS layout of a stage: A rows [BM][64] then B rows [BN][64], 128 bytes a
+// row, 16-byte chunk c of row r stored at chunk c ^ (r & 7).  Fragment reads
+// of 8 consecutive rows at one logical chunk then hit 8 distinct bank groups.
+template <int BM, int BN, int WM, int WN, int STAGES, bool LORA>
 __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int T = WM * WN * kWave;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int AV = BM * (kBK / 8) / T;  // 16-byte vectors per thread per stage
-  constexpr int BV = BN * (kBK / 8) / T;
-  static_assert(FM >= 1 && FN >= 1 && AV >= 1 && BV >= 1, "tile");
-  static_assert(BM * (kBK / 8) % T == 0 && BN * (kBK / 8) % T == 0, "tile");
-
-  __shared__ __align__(16) unsigned char smem[lds_bytes<BM, BN>()];
-  bf16_t *sA = reinterpret_cast<bf16_t *>(smem);
-  bf16_t *sB = sA + 2 * BM * kLdsStride;
+  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  __shared__ __align__(16) unsigned char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
   const int wid = tid / kWave;
   const int wm = wid / WN, wn = wid % WN;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
   const int M = g.M, N = g.N, K = g.K;
 
-  u32x4 ra[AV], rb[BV];
-  auto gload = [&](int k0) {
+  // XCD-aware tile order: consecutive workgroup ids go to different XCDs
+  // (round robin over 8), so give each XCD a contiguous range of the
+  // grouped tile order (groups of 8 M-tiles sweeping N), keeping operand
+  // tiles shared by neighbours inside one L2.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  constexpr int GROUP = 8;
+  const int grp = t / (GROUP * tiles_n);
+  const int first_m = grp * GROUP;
+  const int gcnt = min(GROUP, tiles_m - first_m);
+  const int tin = t - grp * GROUP * tiles_n;
+  const int m0 = (first_m + tin % gcnt) * BM;
+  const int n0 = (tin / gcnt) * BN;
+
+  // DMA sources: lane l fills row l/8 of its 8-row group at physical chunk
+  // l%8, i.e. logical chunk (l%8) ^ (l/8).  Rows past M / N are clamped to
+  // the last valid row (their results are never stored).
+  const int r8 = l >> 3;
+  const int lc = (l & 7) ^ r8;
+  const bf16_t *asrc[C::AI];
+  const bf16_t *bsrc[C::BI];
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = tid + i * T;
-      const int row = v >> 3, ch = v & 7;
-      const int gm = m0 + row, gk = k0 + ch * 8;
-      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const u32x4 *>(g.X + (int64_t)gm * g.ldx + gk)
-                                 : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < C::AI; ++i) {
+    const int gm = min(m0 + (wid * C::AI + i) * 8 + r8, M - 1);
+    asrc[i] = g.X + (int64_t)gm * g.ldx + lc * 8;
+  }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = tid + i * T;
-      const int row = v >> 3, ch = v & 7;
-      const int gn = n0 + row, gk = k0 + ch * 8;
-      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const u32x4 *>(g.W + (int64_t)gn * g.ldw + gk)
-                                 : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < C::BI; ++i) {
+    const int gn = min(n0 + (wid * C::BI + i) * 8 + r8, N - 1);
+    bsrc[i] = g.W + (int64_t)gn * g.ldw + lc * 8;
+  }
+  const uint32_t sbase = lds_offset(smem);
+  const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * C::AI * 1024);
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + BM * 128 + wid * C::BI * 1024);
+
+  auto issue = [&](int stage, int k0) {
+    // a chunk past K reads the row's first chunk instead (in bounds) and is
+    // zeroed in LDS before use
+    const int kofs = (k0 + lc * 8 < K) ? k0 : -lc * 8;
+#pragma unroll
+    for (int i = 0; i < C::AI; ++i) dma16(a_dst + stage * C::STAGE + i * 1024, asrc[i] + kofs);
+#pragma unroll
+    for (int i = 0; i < C::BI; ++i) dma16(b_dst + stage * C::STAGE + i * 1024, bsrc[i] + kofs);
   };
-  auto sstore = [&](int buf) {
-    bf16_t *a = sA + buf * BM * kLdsStride;
-    bf16_t *b = sB + buf * BN * kLdsStride;
+  auto zero_tail = [&](int stage, int k0) {
+    if (k0 + lc * 8 >= K) {
+      unsigned char *st = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = tid + i * T;
-      *reinterpret_cast<u32x4 *>(a + (v >> 3) * kLdsStride + (v & 7) * 8) = ra[i];
-    }
+      for (int i = 0; i < C::AI; ++i)
+        *reinterpret_cast<u32x4 *>(st + (wid * C::AI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = tid + i * T;
-      *reinterpret_cast<u32x4 *>(b + (v >> 3) * kLdsStride + (v & 7) * 8) = rb[i];
+      for (int i = 0; i < C::BI; ++i)
+        *reinterpret_cast<u32x4 *>(st + BM * 128 + (wid * C::BI + i) * 1024 + l * 16) =
+            u32x4{0, 0, 0, 0};
     }
   };
 
-  f32x16 acc[FM][FN];
+  f32x16 acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // per-lane fragment offsets inside a stage
+  int a_row_off[C::FM], b_row_off[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) a_row_off[i] = (wm * C::TM + i * 32 + (l & 31)) * 128;
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) b_row_off[j] = BM * 128 + (wn * C::TN + j * 32 + (l & 31)) * 128;
+  int chunk_off[kBK / 16];
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) chunk_off[kk] = (((kk * 2 + (l >> 5)) ^ (l & 7)) * 16);
+
   const int KT = (K + kBK - 1) / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * kBK);
-    const bf16_t *a = sA + cur * BM * kLdsStride + (wm * TM + (l & 31)) * kLdsStride + (l >> 5) * 8;
-    const bf16_t *b = sB + cur * BN * kLdsStride + (wn * TN + (l & 31)) * kLdsStride + (l >> 5) * 8;
+  const bool ktail = (K % kBK) != 0;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      mfma_bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(a + i * 32 * kLdsStride + kk * 16));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(b + j * 32 * kLdsStride + kk * 16));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
-  }
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s * kBK);
 
   if constexpr (LORA) {
-    // LDS reuse: row -> LoRA segment of the tile, distinct segment list,
-    // staged Bt tile [BN][RS] (K-contiguous per output column).
-    int *s_rowseg = reinterpret_cast<int *>(smem);
-    int *s_useg = s_rowseg + BM;
-    int *s_nu = s_useg + BM;
-    bf16_t *sBt = reinterpret_cast<bf16_t *>(smem + 2 * BM * 4 + 16);
-    constexpr int RS = 64 + 8;
-    for (int i = tid; i < BM; i += T) {
-      const int row = m0 + i;
+    // LoRA increment first, straight into the zeroed accumulators, while the
+    // first stages are in flight.  Per distinct LoRA segment among this
+    // wave's rows (ascending segment id): A operand = s_u H[row][k] for rows
+    // of u (bf16 high part + bf16 remainder), 0 for other rows; B operand =
+    // Bt_u[k][col] gathered with coalesced 2-byte loads.  Rows outside u get
+    // exact zeros, so base-only rows stay bit-identical to the plain GEMM.
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    constexpr int RPL = (TM + kWave - 1) / kWave;   // tile rows per lane
+    int useg[RPL];
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+      const int rr = l + kWave * q;
+      const int row = m0 + wm * TM + rr;
       int u = -1;
-      if (row < M) {
-        const int s = g.row_segment[row];
-        if (g.seg_rank[s] > 0) u = s;
+      if (rr < TM && row < M) {
+        const int sg = g.row_segment[row];
+        if (g.seg_rank[sg] > 0) u = sg;
       }
-      s_rowseg[i] = u;
+      useg[q] = u;
     }
-    if (tid == 0) *s_nu = 0;
-    __syncthreads();
-    for (int i = tid; i < BM; i += T) {
-      const int u = s_rowseg[i];
-      if (u >= 0) {
-        bool first = true;
-        for (int j = i - 1; j >= 0; --j)
-          if (s_rowseg[j] == u) { first = false; break; }
-        if (first) s_useg[atomicAdd(s_nu, 1)] = u;
-      }
-    }
-    __syncthreads();
-    const int nu = *s_nu;
-    for (int ui = 0; ui < nu; ++ui) {
-      const int u = s_useg[ui];
+    int prev = -1;
+    while (true) {
+      int cand = INT_MAX;
+#pragma unroll
+      for (int q = 0; q < RPL; ++q)
+        if (useg[q] > prev && useg[q] < cand) cand = useg[q];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
+      if (cand == INT_MAX) break;
+      const int u = cand;
       const int slot = g.seg_slot[u];
       const int r = g.seg_rank[u];
       const float sc = g.seg_scale[u];
       const int R = rank_bucket(r, g.policy, g.r_max);
-      const int Rp = (R + 15) & ~15;
-      // stage Bt_slot[0:Rp][n0:n0+BN]; rows >= r (and columns >= N) are zero
-      for (int v = tid; v < Rp * (BN / 8); v += T) {
-        const int k = v / (BN / 8);
-        const int c8 = (v - k * (BN / 8)) * 8;
-        const int gcol = n0 + c8;
-        u32x4 raw = {0, 0, 0, 0};
-        if (k < R && gcol < N) {
-          raw = *reinterpret_cast<const u32x4 *>(g.Bt + ((int64_t)slot * g.r_max + k) * N + gcol);
-          asm volatile("" : "+v"(raw));
-        }
-        if (k >= r) raw = u32x4{0, 0, 0, 0};
+      const int KS = (R + 15) / 16;
+      const bf16_t *bt = g.Bt + (int64_t)slot * g.r_max * N;
+      // B operands Bt_u[k][col] for every (column fragment, K step), loaded
+      // once per segment.  Branch-free: the index is clamped into the slot
+      // (rows < R, columns < N) and out-of-range values are masked, so the
+      // loads of a segment issue together.  Rank rows in [r, R) are read as
+      // a width-R kernel would, then zeroed.
+      u32x4 bop[FN][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sBt[(c8 + 2 * e) * RS + k] = (bf16_t)(raw[e] & 0xffffu);
-          sBt[(c8 + 2 * e + 1) * RS + k] = (bf16_t)(raw[e] >> 16);
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * TN + j * 32 + (l & 31);
+        const bool col_ok = col < N;
+        const int colc = min(col, N - 1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk < KS) {
+            const int kb = kk * 16 + (l >> 5) * 8;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              uint32_t w2 = 0;
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const int k = kb + e2 * 2 + h2;
+                const uint32_t v = bt[(uint32_t)(min(k, R - 1) * N + colc)];
+                w2 |= ((col_ok && k < r) ? v : 0u) << (16 * h2);
+              }
+              bop[j][kk][e2] = w2;
+            }
+          }
         }
       }
-      __syncthreads();
-      const int KS = Rp / 16;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int lrow = wm * TM + i * 32 + (l & 31);
-        const bool in_u = s_rowseg[lrow] == u;
-        const float *hrow = g.H + (int64_t)(m0 + lrow) * g.r_max;
+        __builtin_amdgcn_sched_barrier(0);
+        const int rr = i * 32 + (l & 31);
+        const bool in_u = __shfl(useg[(i * 32) / kWave], rr % kWave) == u;
+        // rows past M are clamped for the address only (never in u)
+        const float *hrow = g.H + (int64_t)min(m0 + wm * TM + rr, M - 1) * g.r_max;
         mfma_bf16x8 ahi[4], alo[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk < KS) {
+            const int kb = kk * 16 + (l >> 5) * 8;
+            const int kc = min(kb, g.r_max - 8);
+            const float4 h0 = *reinterpret_cast<const float4 *>(hrow + kc);
+            const float4 h1 = *reinterpret_cast<const float4 *>(hrow + kc + 4);
+            const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
             u32x4 phi, plo;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
               uint32_t hw = 0, lw = 0;
 #pragma unroll
               for (int h2 = 0; h2 < 2; ++h2) {
-                const int kidx = kk * 16 + (l >> 5) * 8 + e2 * 2 + h2;
-                const float h = (in_u && kidx < r) ? sc * hrow[kidx] : 0.f;
-                const uint32_t hb = f32_to_bf16_rne(h);
-                const uint32_t lb = f32_to_bf16_rne(h - bf16_to_f32(hb));
+                const int e = e2 * 2 + h2;
+                // H entries of u's rows are written for k < r; everything
+                // else (other rows, k >= r) is masked by select, never used
+                const float hv = (in_u && kb + e < r) ? sc * h[e] : 0.f;
+                const uint32_t hb = f32_to_bf16_rne(hv);
+                const uint32_t lb = f32_to_bf16_rne(hv - bf16_to_f32(hb));
                 hw |= hb << (16 * h2);
                 lw |= lb << (16 * h2);
               }
@@ -242,38 +333,53 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          f32x16 t;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) t[v] = 0.f;
-          const bf16_t *bcol = sBt + (wn * TN + j * 32 + (l & 31)) * RS + (l >> 5) * 8;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             if (kk < KS) {
-              const mfma_bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4 *>(bcol + kk * 16));
-              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[kk], bv, t, 0, 0, 0);
-              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[kk], bv, t, 0, 0, 0);
+              const mfma_bf16x8 bv = as_bf16x8(bop[j][kk]);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[kk], bv, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[kk], bv, acc[i][j], 0, 0, 0);
             }
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int lr = wm * TM + i * 32 + acc_row(v, l);
-            if (s_rowseg[lr] == u) acc[i][j][v] += t[v];
           }
         }
       }
-      __syncthreads();
+      prev = u;
+    }
+  }
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int ahead = min(STAGES - 2, KT - 1 - kt);
+    wait_ahead<C::IPW>(ahead);
+    if (ktail && kt == KT - 1) zero_tail(kt % STAGES, kt * kBK);
+    lgkm_barrier();
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * kBK);
+    const unsigned char *st = smem + (kt % STAGES) * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      mfma_bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off[i] + chunk_off[kk]));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off[j] + chunk_off[kk]));
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
 
   // store: bf16 round to nearest even, once
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * TN + j * 32 + (l & 31);
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = n0 + wn * C::TN + j * 32 + (l & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * TM + i * 32 + acc_row(v, l);
+        const int row = m0 + wm * C::TM + i * 32 + acc_row(v, l);
         if (row < M && col < N) g.Y[(int64_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_rne(acc[i][j][v]);
       }
     }
@@ -363,14 +469,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
-  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+  const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid(((ntiles + 7) / 8) * 8);
   dim3 block(WM * WN * kWave);
   if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, STAGES, true>), grid, block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, STAGES, false>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -392,8 +499,8 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
       g.r_max = pool->r_max;
       g.policy = pool->policy;
     }
-    if (M <= 512) return launch_bf16<64, 64, 2, 2>(g, lora, stream);
-    return launch_bf16<128, 128, 2, 2>(g, lora, stream);
+    if (M <= LORA_GEMM_SMALL_M) return launch_bf16<LORA_GEMM_SMALL>(g, lora, stream);
+    return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
   }
   GemmF32Args g{(const float *)X, ldx, (const float *)W, ldw, (float *)Y, ldy, M, K, N,
                 H, nullptr, nullptr, nullptr, nullptr, nullptr, 0};

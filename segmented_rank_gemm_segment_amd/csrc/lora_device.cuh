@@ -108,8 +108,8 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid) {
   uint64_t remaining = __ballot(valid);
   uint64_t mine = 0;
   while (remaining) {
-    const int leader = __ffsll((unsigned long long)remaining) - 1;
-    const int lk = __shfl(key, leader);
+    const int leader = __ffsll((unsigned long long)remaining) - 1;  // wave-uniform
+    const int lk = __builtin_amdgcn_readlane(key, leader);
     const uint64_t m = __ballot(valid && key == lk);
     if (valid && key == lk) mine = m;
     remaining &= ~m;

@@ -8,13 +8,13 @@
 // H_a = X_a A_a^T and Delta Y_a = s_a H_a B_a^T scattered back to the
 // original rows).
 //
-// Both kernels are bandwidth-bound segmented GEMV/skinny GEMMs.  Work items
-// are (segment, block of up to kRowBlk rows of that segment); a fixed grid
-// walks them with a stride so no host synchronisation is needed to size it.
-// Every adapter row is read with 16-byte coalesced loads along d (A rows
-// along d_in, Bt rows along d_out); the rank-r reduction of the shrink is a
-// wavefront butterfly.  Each token row lives in exactly one segment, so Y is
-// updated without atomics and the result is deterministic.
+// Both are bandwidth-bound segmented GEMV / skinny products.  Work items are
+// (segment, block of up to kRowBlk rows of that segment); a fixed grid walks
+// them with a stride, so no host synchronisation sizes the launch.  Adapter
+// rows are read once per work item with 16-byte coalesced loads along d, and
+// every load of a work item is issued before its arithmetic, so a work item
+// costs about one memory round trip.  Each token row lives in exactly one
+// segment, so Y is updated without atomics and results are deterministic.
 #include "lora_device.cuh"
 #include "lora_kernels.h"
 
@@ -22,143 +22,228 @@ namespace lora {
 namespace {
 
 constexpr int kRowBlk = 64;   // rows of one segment per work item
-constexpr int kSub = 8;       // rows processed together inside a work item
 
-// Keep a loaded value alive (rank rows past r inside the processed width are
-// read, as a padded kernel would, but contribute nothing).
-__device__ __forceinline__ void keep(uint4 &v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-}
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // ----------------------------------------------------------------------------
-// shrink: one wavefront per rank row k of a work item; lanes stride d_in with
-// 16-byte vectors; blockIdx.x picks a group of waves-per-block rank rows.
+// shrink: one wavefront per rank row k; lanes cover d_in in chunks of
+// kCV 16-byte vectors per lane, adapter row chunk held in registers while
+// kRows token rows stream past it; butterfly reduction over the wave.
 // ----------------------------------------------------------------------------
-template <typename T, int kWaves>
+template <typename T, int kWaves, int kRows>
 __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
     const int32_t *num_segments, int r_max, int d_in, int policy, int blocks_per_seg,
-    float *__restrict__ H) {
+    int cap_items, float *__restrict__ H) {
   constexpr int V = Elem<T>::kVec;
+  constexpr int kCV = 8;
+  constexpr int kChunk = kCV * kWave * V;  // elements of d_in per pass
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int k = blockIdx.x * kWaves + wave;
   const int S = *num_segments;
-  const int items = S * blocks_per_seg;
-  for (int item = blockIdx.y; item < items; item += gridDim.y) {
+  for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
     const int s = item / blocks_per_seg;
     const int b = item - s * blocks_per_seg;
+    // metadata of segment s is read before S is known (s < capacity keeps it
+    // in bounds), so both loads travel together
     const int r = seg_rank[s];
+    const int o0 = seg_off[s], o1 = seg_off[s + 1];
+    const int slot = seg_slot[s];
+    if (s >= S) break;
     const int R = rank_bucket(r, policy, r_max);
     if (k >= R) continue;
-    const int p0 = seg_off[s] + b * kRowBlk;
-    const int p1 = min(seg_off[s + 1], p0 + kRowBlk);
+    const int p0 = o0 + b * kRowBlk;
+    const int p1 = min(o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
-    const int slot = seg_slot[s];
     const T *arow = A + ((int64_t)slot * r_max + k) * d_in;
-    for (int q0 = p0; q0 < p1; q0 += kSub) {
-      const int nq = min(kSub, p1 - q0);
-      int rows[kSub];
+    for (int q0 = p0; q0 < p1; q0 += kRows) {
+      const int nq = min(kRows, p1 - q0);
+      const T *xrow[kRows];
 #pragma unroll
-      for (int q = 0; q < kSub; ++q) rows[q] = token_indices[q0 + min(q, nq - 1)];
-      float acc[kSub];
+      for (int q = 0; q < kRows; ++q)
+        xrow[q] = X + (int64_t)token_indices[q0 + min(q, nq - 1)] * ldx;
+      float acc[kRows];
 #pragma unroll
-      for (int q = 0; q < kSub; ++q) acc[q] = 0.f;
-      for (int c = lane * V; c < d_in; c += kWave * V) {
-        float av[V];
-        Elem<T>::unpack(ldg16(arow + c), av);
+      for (int q = 0; q < kRows; ++q) acc[q] = 0.f;
+      for (int c0 = 0; c0 < d_in; c0 += kChunk) {
+        uint4 av[kCV];
+        uint4 xv[kRows][kCV];
 #pragma unroll
-        for (int q = 0; q < kSub; ++q) {
-          if (q < nq) {
-            float xv[V];
-            Elem<T>::unpack(ldg16(X + (int64_t)rows[q] * ldx + c), xv);
+        for (int v = 0; v < kCV; ++v) {
+          const int c = c0 + (v * kWave + lane) * V;
+          av[v] = c < d_in ? ldg16(arow + c) : zero4();
+        }
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc[q] = fmaf(av[e], xv[e], acc[q]);
+        for (int q = 0; q < kRows; ++q) {
+#pragma unroll
+          for (int v = 0; v < kCV; ++v) {
+            const int c = c0 + (v * kWave + lane) * V;
+            xv[q][v] = (q < nq && c < d_in) ? ldg16(xrow[q] + c) : zero4();
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < kCV; ++v) {
+          float af[V];
+          Elem<T>::unpack(av[v], af);
+#pragma unroll
+          for (int q = 0; q < kRows; ++q) {
+            float xf[V];
+            Elem<T>::unpack(xv[q][v], xf);
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[q] = fmaf(af[e], xf[e], acc[q]);
           }
         }
       }
 #pragma unroll
-      for (int q = 0; q < kSub; ++q) {
-        if (q < nq) {
-          const float v = wave_sum(acc[q]);
-          if (lane == 0 && k < r) H[(int64_t)rows[q] * r_max + k] = v;
-        }
+      for (int q = 0; q < kRows; ++q) {
+        const float v = wave_sum(acc[q]);
+        if (lane == 0 && q < nq && k < r) H[(int64_t)token_indices[q0 + q] * r_max + k] = v;
       }
     }
   }
 }
 
 // ----------------------------------------------------------------------------
-// expand: a thread owns V consecutive output columns; blockIdx.x picks the
-// column chunk.  H rows of the current sub-block are staged in LDS.
+// expand: a wavefront covers 16 column vectors x 4 rank quarters.  Rank rows
+// come in blocks of 4; lane (cv = l % 16, kq = l / 16) owns blocks kq,
+// kq + 4, ... below R of its column vector (held in registers for the whole
+// work item).  Where a rank row is summed never depends on R, so every rank
+// policy gives the same bits.  Rows are processed four at a time: every lane
+// loads the four rows' H values of its blocks (float4) and lane kq also
+// loads Y of row kq; the four quarters are combined with two xor-shuffles.
+// No LDS, no barriers.
 // ----------------------------------------------------------------------------
-template <typename T, int kThreads>
-__global__ __launch_bounds__(kThreads) void expand_kernel(
-    const float *__restrict__ H, const T *__restrict__ Bt, const int32_t *token_indices,
-    const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
-    const float *seg_scale, const int32_t *num_segments, int r_max, int d_out, int policy,
-    int blocks_per_seg, T *__restrict__ Y, int64_t ldy) {
+constexpr int kExpWaves = 4;
+constexpr int kExpSub = 4;    // rows per pass (one Y row per rank quarter)
+
+template <typename T, int R>
+__device__ __forceinline__ void expand_item(const float *__restrict__ H, const T *bt, int d_out,
+                                            bool active, int r, float sc, int p0, int p1,
+                                            const int32_t *token_indices, int r_max, T *Y,
+                                            int64_t ldy, int col, int lane) {
   constexpr int V = Elem<T>::kVec;
-  __shared__ float s_h[kSub][64];
-  __shared__ int s_rows[kSub];
-  const int col = (blockIdx.x * kThreads + threadIdx.x) * V;
-  const bool active = col < d_out;
-  const int S = *num_segments;
-  const int items = S * blocks_per_seg;
-  for (int item = blockIdx.y; item < items; item += gridDim.y) {
-    const int s = item / blocks_per_seg;
-    const int b = item - s * blocks_per_seg;
-    const int r = seg_rank[s];
-    const int R = rank_bucket(r, policy, r_max);
-    if (R == 0) continue;
-    const int p0 = seg_off[s] + b * kRowBlk;
-    const int p1 = min(seg_off[s + 1], p0 + kRowBlk);
-    if (p0 >= p1) continue;
-    const float sc = seg_scale[s];
-    const T *bt = Bt + (int64_t)seg_slot[s] * r_max * d_out + col;
-    for (int q0 = p0; q0 < p1; q0 += kSub) {
-      const int nq = min(kSub, p1 - q0);
-      __syncthreads();
-      if (threadIdx.x < kSub) s_rows[threadIdx.x] = token_indices[q0 + min((int)threadIdx.x, nq - 1)];
-      __syncthreads();
-      for (int t = threadIdx.x; t < kSub * R; t += kThreads) {
-        const int q = t / R, kk = t - q * R;
-        s_h[q][kk] = (q < nq && kk < r) ? H[(int64_t)s_rows[q] * r_max + kk] : 0.f;
+  constexpr int NB = (R + 15) / 16;   // rank blocks of 4 per lane (at most)
+  const int kq = lane >> 4;
+  uint4 braw[NB][4];
+  bool blk_ok[NB];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) {
+    const int k0 = 4 * (kq + 4 * jb);
+    blk_ok[jb] = k0 < R;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      // rank rows in [r, R) are read, as a kernel compiled for width R
+      // would, and masked below (the mask depends on r, so the load stays)
+      braw[jb][e] = (active && blk_ok[jb]) ? ldg16(bt + (int64_t)(k0 + e) * d_out) : zero4();
+  }
+  for (int q0 = p0; q0 < p1; q0 += kExpSub) {
+    const int nq = min(kExpSub, p1 - q0);
+    int rows[kExpSub];
+#pragma unroll
+    for (int q = 0; q < kExpSub; ++q) rows[q] = token_indices[q0 + min(q, nq - 1)];
+    float4 hv[kExpSub][NB];
+#pragma unroll
+    for (int q = 0; q < kExpSub; ++q)
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        // block start k0 < R <= r_max and r_max % 8 == 0: the float4 is in the row
+        const int k0 = 4 * (kq + 4 * jb);
+        hv[q][jb] = blk_ok[jb] ? *reinterpret_cast<const float4 *>(H + (int64_t)rows[q] * r_max + k0)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      __syncthreads();
-      if (!active) continue;
-      float acc[kSub][V];
+    const int myq = kq;  // Y row updated by this lane
+    const uint4 yraw = (active && myq < nq) ? ldg16(Y + (int64_t)rows[myq] * ldy + col) : zero4();
+    float acc[kExpSub][V];
 #pragma unroll
-      for (int q = 0; q < kSub; ++q)
+    for (int q = 0; q < kExpSub; ++q)
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc[q][e] = 0.f;
-      for (int kk = 0; kk < R; ++kk) {
-        uint4 raw = ldg16(bt + (int64_t)kk * d_out);
-        keep(raw);
+      for (int e = 0; e < V; ++e) acc[q][e] = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int k = 4 * (kq + 4 * jb) + e4;
+        const bool live = blk_ok[jb] && k < r;
         float bv[V];
-        Elem<T>::unpack(raw, bv);
-        const bool live = kk < r;
+        Elem<T>::unpack(braw[jb][e4], bv);
 #pragma unroll
         for (int e = 0; e < V; ++e) bv[e] = live ? bv[e] : 0.f;
 #pragma unroll
-        for (int q = 0; q < kSub; ++q) {
-          const float h = s_h[q][kk];
+        for (int q = 0; q < kExpSub; ++q) {
+          const float4 h4 = hv[q][jb];
+          const float hq = e4 == 0 ? h4.x : e4 == 1 ? h4.y : e4 == 2 ? h4.z : h4.w;
+          const float h = live ? hq : 0.f;
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[q][e] = fmaf(h, bv[e], acc[q][e]);
         }
       }
+    }
 #pragma unroll
-      for (int q = 0; q < kSub; ++q) {
-        if (q < nq) {
-          T *y = Y + (int64_t)s_rows[q] * ldy + col;
-          float yv[V];
-          Elem<T>::unpack(ldg16(y), yv);
+    for (int q = 0; q < kExpSub; ++q)
 #pragma unroll
-          for (int e = 0; e < V; ++e) yv[e] = fmaf(sc, acc[q][e], yv[e]);
-          stg16(y, Elem<T>::pack(yv));
-        }
+      for (int e = 0; e < V; ++e) {
+        acc[q][e] += __shfl_xor(acc[q][e], 16);
+        acc[q][e] += __shfl_xor(acc[q][e], 32);
       }
+    if (active && myq < nq) {
+      float yv[V];
+      Elem<T>::unpack(yraw, yv);
+      float out[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        // select this lane's row without dynamic register indexing
+        float a = 0.f;
+#pragma unroll
+        for (int q = 0; q < kExpSub; ++q) a = (q == myq) ? acc[q][e] : a;
+        out[e] = fmaf(sc, a, yv[e]);
+      }
+      stg16(Y + (int64_t)rows[myq] * ldy + col, Elem<T>::pack(out));
+    }
+  }
+}
+
+// RMAX = the pool's r_max: only rank buckets up to it are compiled in, so a
+// rank-16 pool does not pay the registers of the rank-64 case.
+template <typename T, int RMAX>
+__global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
+    const float *__restrict__ H, const T *__restrict__ Bt, const int32_t *token_indices,
+    const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
+    const float *seg_scale, const int32_t *num_segments, int r_max, int d_out, int policy,
+    int blocks_per_seg, int cap_items, T *__restrict__ Y, int64_t ldy) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int col = ((blockIdx.x * kExpWaves + wave) * 16 + (lane & 15)) * V;
+  const bool active = col < d_out;
+  const int S = *num_segments;
+  for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
+    const int s = item / blocks_per_seg;
+    const int b = item - s * blocks_per_seg;
+    // read before S is known (in bounds below the capacity) so the loads overlap
+    const int r = seg_rank[s];
+    const int o0 = seg_off[s], o1 = seg_off[s + 1];
+    const int slot = seg_slot[s];
+    const float sc = seg_scale[s];
+    if (s >= S) break;
+    const int R = rank_bucket(r, policy, r_max);
+    if (R == 0) continue;
+    const int p0 = o0 + b * kRowBlk;
+    const int p1 = min(o1, p0 + kRowBlk);
+    if (p0 >= p1) continue;
+    const T *bt = Bt + (int64_t)slot * r_max * d_out + (active ? col : 0);
+    if (R == 8) {
+      expand_item<T, 8>(H, bt, d_out, active, r, sc, p0, p1, token_indices, r_max, Y, ldy, col, lane);
+    } else if (RMAX >= 16 && R == 16) {
+      expand_item<T, (RMAX >= 16 ? 16 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
+                                            r_max, Y, ldy, col, lane);
+    } else if (RMAX >= 32 && R == 32) {
+      expand_item<T, (RMAX >= 32 ? 32 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
+                                            r_max, Y, ldy, col, lane);
+    } else if (RMAX >= 64) {
+      expand_item<T, (RMAX >= 64 ? 64 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
+                                            r_max, Y, ldy, col, lane);
     }
   }
 }
@@ -178,51 +263,60 @@ inline int grid_items(int bound_items) {
 hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const PoolView &pool,
                          float *H, hipStream_t stream) {
   constexpr int kW = 4;
+  constexpr int kRows = 4;
   const int n = seg.n_rows;
   const int bps = (n + kRowBlk - 1) / kRowBlk;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
-  // Upper bound on real items: every segment has >= 1 row, so
-  // sum_s ceil(n_s / kRowBlk) <= S + n / kRowBlk.
+  // Real items: every segment has >= 1 row, so sum_s ceil(n_s / kRowBlk) <= S + n / kRowBlk.
   const int real_bound = S_bound + n / kRowBlk;
   dim3 grid((pool.r_max + kW - 1) / kW, grid_items(real_bound));
   dim3 block(kW * kWave);
   if (pool.dtype == 1) {
-    hipLaunchKernelGGL((shrink_kernel<bf16_t, kW>), grid, block, 0, stream,
+    hipLaunchKernelGGL((shrink_kernel<bf16_t, kW, kRows>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, bps, H);
+                       pool.d_in, pool.policy, bps, S_bound * bps, H);
   } else {
-    hipLaunchKernelGGL((shrink_kernel<float, kW>), grid, block, 0, stream, (const float *)X,
-                       ldx, (const float *)pool.A, seg.token_indices, seg.seg_off, seg.seg_slot,
-                       seg.seg_rank, seg.num_segments, pool.r_max, pool.d_in, pool.policy, bps,
-                       H);
+    hipLaunchKernelGGL((shrink_kernel<float, kW, kRows>), grid, block, 0, stream,
+                       (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
+                       seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
+                       pool.d_in, pool.policy, bps, S_bound * bps, H);
   }
   return hipGetLastError();
 }
 
+template <typename T, int RMAX>
+void launch_expand_t(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
+                     int bps, int S_bound, int real_bound, hipStream_t stream) {
+  const int cols_per_block = kExpWaves * 16 * Elem<T>::kVec;
+  dim3 grid((pool.d_out + cols_per_block - 1) / cols_per_block, grid_items(real_bound));
+  hipLaunchKernelGGL((expand_kernel<T, RMAX>), grid, dim3(kExpWaves * kWave), 0, stream, H,
+                     (const T *)pool.Bt, seg.token_indices, seg.seg_off, seg.seg_slot,
+                     seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max, pool.d_out,
+                     pool.policy, bps, S_bound * bps, (T *)Y, ldy);
+}
+
+template <typename T>
+void launch_expand_r(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
+                     int bps, int S_bound, int real_bound, hipStream_t stream) {
+  switch (pool.r_max) {
+    case 8: launch_expand_t<T, 8>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
+    case 16: launch_expand_t<T, 16>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
+    case 32: launch_expand_t<T, 32>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
+    default: launch_expand_t<T, 64>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
+  }
+}
+
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream) {
-  constexpr int kT = 64;
   const int n = seg.n_rows;
   const int bps = (n + kRowBlk - 1) / kRowBlk;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
   const int real_bound = S_bound + n / kRowBlk;
-  dim3 block(kT);
-  if (pool.dtype == 1) {
-    const int cols_per_block = kT * Elem<bf16_t>::kVec;
-    dim3 grid((pool.d_out + cols_per_block - 1) / cols_per_block, grid_items(real_bound));
-    hipLaunchKernelGGL((expand_kernel<bf16_t, kT>), grid, block, 0, stream, H,
-                       (const bf16_t *)pool.Bt, seg.token_indices, seg.seg_off, seg.seg_slot,
-                       seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max, pool.d_out,
-                       pool.policy, bps, (bf16_t *)Y, ldy);
-  } else {
-    const int cols_per_block = kT * Elem<float>::kVec;
-    dim3 grid((pool.d_out + cols_per_block - 1) / cols_per_block, grid_items(real_bound));
-    hipLaunchKernelGGL((expand_kernel<float, kT>), grid, block, 0, stream, H,
-                       (const float *)pool.Bt, seg.token_indices, seg.seg_off, seg.seg_slot,
-                       seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max, pool.d_out,
-                       pool.policy, bps, (float *)Y, ldy);
-  }
+  if (pool.dtype == 1)
+    launch_expand_r<bf16_t>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream);
+  else
+    launch_expand_r<float>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream);
   return hipGetLastError();
 }
 
