@@ -48,8 +48,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
-    p.add_argument("--path", choices=["auto", "fused", "separate"], default="auto",
-                   help="auto: time both step variants and report the faster")
+    p.add_argument("--path", choices=["auto", "fused", "separate", "overlap"], default="auto",
+                   help="auto: time every step variant and report the fastest; overlap = "
+                        "separate with the base GEMM on a second stream beside build+shrink")
     p.add_argument("--policy", choices=["exact", "two_buckets", "padded"], default="exact")
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="total size of the rotated copies of the layer tensors")
@@ -57,6 +58,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     p.add_argument("--kernel-loops", type=int, default=None,
                    help="launches per kernel in the per-kernel timing (default: steps)")
     return p.parse_args()
@@ -154,7 +157,33 @@ def k_expand(L):
     srg.lora_expand(L.H, L.seg, L.pool, L.Y)
 
 
+class _Overlap:
+    """Base GEMM on a second stream, concurrent with build + shrink on the
+    launch stream; the expand waits for both (fork/join through events, so
+    it is captured into the same HIP graph as two branches)."""
+
+    def __init__(self):
+        import torch
+        self.side = torch.cuda.Stream()          # default priority
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+
+    def __call__(self, L):
+        import torch
+        main = torch.cuda.current_stream()
+        self.fork.record(main)
+        self.side.wait_event(self.fork)
+        with torch.cuda.stream(self.side):
+            k_base(L)
+        self.join.record(self.side)
+        k_build(L)
+        k_shrink(L)
+        main.wait_event(self.join)
+        k_expand(L)
+
+
 STEP = {"fused": (k_build, k_shrink, k_fused), "separate": (k_build, k_shrink, k_base, k_expand)}
+PATHS = ("fused", "separate", "overlap")
 KNAME = {k_build: "build", k_shrink: "shrink", k_fused: "fused", k_base: "base", k_expand: "expand"}
 
 
@@ -213,7 +242,8 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
     torch.cuda.synchronize()
     step = {}
     for p in paths:
-        step[p] = time_calls(STEP[p], layers, steps, warmup, use_graph)
+        seq = (_Overlap(),) if p == "overlap" else STEP[p]
+        step[p] = time_calls(seq, layers, steps, warmup, use_graph)
     kl = kernel_loops or steps
     per_kernel = {}
     for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
@@ -290,17 +320,29 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # reference for hardware byte counters: each copy reads and writes
+        # exactly MIB MiB
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
     srg.lib()
 
     w = wl.make_config(args.config)
     fig = work_figures(w)
-    paths = ["fused", "separate"] if args.path == "auto" else [args.path]
+    paths = list(PATHS) if args.path == "auto" else [args.path]
     m = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
                 args.kernel_loops, not args.eager)
     path = min(paths, key=lambda p: m["step"][p][0])
     step_s, wall = m["step"][path]
     kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
     cand = ("build", "shrink", "fused") if path == "fused" else ("build", "shrink", "base", "expand")
+    # (overlap: same kernels as separate, base GEMM concurrent with build + shrink)
     main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)
     sh, ex = m["per_kernel_s"]["shrink"], m["per_kernel_s"]["expand"]

@@ -23,13 +23,13 @@
 // increment, added in fp32 and rounded once with the base product.
 #include <climits>
 
+#include "lds_dma.cuh"
 #include "lora_device.cuh"
 #include "lora_kernels.h"
 
 namespace lora {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const bf16_t *X;
@@ -47,94 +47,51 @@ struct GemmArgs {
   int r_max, policy;
 };
 
-// Tile configurations <BM, BN, waves along M, waves along N, LDS stages>:
-// small-M (decode-like) batches and large batches.
+// Tile configurations <BM, BN, waves along M, waves along N, K per stage,
+// LDS stages>: small-M (decode-like) batches and large batches.
 #ifndef LORA_GEMM_SMALL
-#define LORA_GEMM_SMALL 64, 64, 2, 2, 6
+#define LORA_GEMM_SMALL 64, 64, 2, 2, 64, 6
 #endif
 #ifndef LORA_GEMM_LARGE
-#define LORA_GEMM_LARGE 256, 256, 2, 4, 2
+#define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2
 #endif
 #ifndef LORA_GEMM_SMALL_M
 #define LORA_GEMM_SMALL_M 512
 #endif
 
-constexpr int kBK = 64;           // K per stage: one 128-byte row chunk per operand row
-constexpr int kLoraRS = 64 + 8;   // LDS row stride (elements) of the staged Bt tile
-
-// ---------------------------------------------------------------------------
-// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4).  Each
-// instruction moves 64 lanes x 16 bytes into 1 KB of LDS starting at M0.
-// Issued through inline asm so that the compiler does not add conservative
-// waits on them; completion is tracked by hand with s_waitcnt vmcnt.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-__device__ __forceinline__ void dma16(uint32_t m0, const void *src) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
-               : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding, then LDS-fence and barrier the workgroup.
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void lgkm_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int IPW>
-__device__ __forceinline__ void wait_ahead(int ahead) {
-  // this wave's DMAs of the `ahead` later stages may stay in flight
-  switch (ahead) {
-    case 0: vm_wait<0>(); break;
-    case 1: vm_wait<(IPW < 63 ? IPW : 63)>(); break;
-    case 2: vm_wait<(2 * IPW < 63 ? 2 * IPW : 63)>(); break;
-    case 3: vm_wait<(3 * IPW < 63 ? 3 * IPW : 63)>(); break;
-    case 4: vm_wait<(4 * IPW < 63 ? 4 * IPW : 63)>(); break;
-    case 5: vm_wait<(5 * IPW < 63 ? 5 * IPW : 63)>(); break;
-    default: vm_wait<(6 * IPW < 63 ? 6 * IPW : 63)>(); break;
-  }
-}
-
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 struct TileCfg {
   static constexpr int NW = WM * WN;
   static constexpr int T = NW * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW;  // 1 KB DMA instructions per wave
+  static constexpr int CH = BK / 8;                 // 16-byte chunks per operand row
+  static constexpr int RB = BK * 2;                 // bytes per operand row in LDS
+  static constexpr int RPI = 1024 / RB;             // rows per 1 KB DMA instruction
+  static constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;  // DMA instructions per wave
   static constexpr int IPW = AI + BI;
-  static constexpr int STAGE = (BM + BN) * kBK * 2;        // bytes
-  static constexpr int LDS_MAIN = STAGES * STAGE;
-  static constexpr int LDS_LORA = 2 * BM * 4 + 16 + BN * kLoraRS * 2;
-  static constexpr int LDS = LDS_MAIN > LDS_LORA ? LDS_MAIN : LDS_LORA;
+  static constexpr int STAGE = (BM + BN) * RB;      // bytes
+  static constexpr int LDS = STAGES * STAGE;
+  static_assert(BK == 32 || BK == 64, "K per stage");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA split");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA split");
   static_assert(STAGES >= 2 && STAGES - 2 <= 6 && (STAGES - 2) * IPW <= 63, "pipeline depth");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  // physical chunk of logical chunk c in row r.  The gfx950 LDS serves a
+  // 16-byte read for 16 lanes at a time across 64 four-byte banks (256
+  // bytes), i.e. two 128-byte rows or four 64-byte rows per bank row; the
+  // XOR below gives 16 consecutive rows at one logical chunk 16 distinct
+  // 16-byte bank groups (measured: c ^ (r & 7) left 2-way conflicts).
+  __device__ static __forceinline__ int swz(int c, int r) {
+    return CH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+  }
 };
 
-__device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }
-
-// Row of element v (0..15) of a 32x32 MFMA accumulator held by lane l
-// (its column is l % 32).
-__device__ __forceinline__ int acc_row(int v, int l) { return (v >> 2) * 8 + (l >> 5) * 4 + (v & 3); }
-
-// LDS layout of a stage: A rows [BM][64] then B rows [BN][64], 128 bytes a
-// row, 16-byte chunk c of row r stored at chunk c ^ (r & 7).  Fragment reads
-// of 8 consecutive rows at one logical chunk then hit 8 distinct bank groups.
-template <int BM, int BN, int WM, int WN, int STAGES, bool LORA>
+// LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
+// chunks XOR-swizzled per row (TileCfg::swz).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool LORA>
 __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
   __shared__ __align__(16) unsigned char smem[C::LDS];
 
   const int tid = threadIdx.x;
@@ -160,47 +117,53 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
   const int m0 = (first_m + tin % gcnt) * BM;
   const int n0 = (tin / gcnt) * BN;
 
-  // DMA sources: lane l fills row l/8 of its 8-row group at physical chunk
-  // l%8, i.e. logical chunk (l%8) ^ (l/8).  Rows past M / N are clamped to
+  // DMA sources: lane l of an instruction fills tile row base + l / CH at
+  // physical chunk l % CH, i.e. logical chunk swz(l % CH, row) (a function
+  // of the row, so of the instruction too).  Rows past M / N are clamped to
   // the last valid row (their results are never stored).
-  const int r8 = l >> 3;
-  const int lc = (l & 7) ^ r8;
+  const int rr = l / C::CH;
+  int alc[C::AI], blc[C::BI];
   const bf16_t *asrc[C::AI];
   const bf16_t *bsrc[C::BI];
 #pragma unroll
   for (int i = 0; i < C::AI; ++i) {
-    const int gm = min(m0 + (wid * C::AI + i) * 8 + r8, M - 1);
-    asrc[i] = g.X + (int64_t)gm * g.ldx + lc * 8;
+    const int row = (wid * C::AI + i) * C::RPI + rr;
+    alc[i] = C::swz(l % C::CH, row);
+    asrc[i] = g.X + (int64_t)min(m0 + row, M - 1) * g.ldx + alc[i] * 8;
   }
 #pragma unroll
   for (int i = 0; i < C::BI; ++i) {
-    const int gn = min(n0 + (wid * C::BI + i) * 8 + r8, N - 1);
-    bsrc[i] = g.W + (int64_t)gn * g.ldw + lc * 8;
+    const int row = (wid * C::BI + i) * C::RPI + rr;
+    blc[i] = C::swz(l % C::CH, row);
+    bsrc[i] = g.W + (int64_t)min(n0 + row, N - 1) * g.ldw + blc[i] * 8;
   }
   const uint32_t sbase = lds_offset(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * C::AI * 1024);
-  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + BM * 128 + wid * C::BI * 1024);
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + BM * C::RB + wid * C::BI * 1024);
 
   auto issue = [&](int stage, int k0) {
     // a chunk past K reads the row's first chunk instead (in bounds) and is
     // zeroed in LDS before use
-    const int kofs = (k0 + lc * 8 < K) ? k0 : -lc * 8;
 #pragma unroll
-    for (int i = 0; i < C::AI; ++i) dma16(a_dst + stage * C::STAGE + i * 1024, asrc[i] + kofs);
+    for (int i = 0; i < C::AI; ++i)
+      dma16(a_dst + stage * C::STAGE + i * 1024,
+            asrc[i] + ((k0 + alc[i] * 8 < K) ? k0 : -alc[i] * 8));
 #pragma unroll
-    for (int i = 0; i < C::BI; ++i) dma16(b_dst + stage * C::STAGE + i * 1024, bsrc[i] + kofs);
+    for (int i = 0; i < C::BI; ++i)
+      dma16(b_dst + stage * C::STAGE + i * 1024,
+            bsrc[i] + ((k0 + blc[i] * 8 < K) ? k0 : -blc[i] * 8));
   };
   auto zero_tail = [&](int stage, int k0) {
-    if (k0 + lc * 8 >= K) {
-      unsigned char *st = smem + stage * C::STAGE;
+    unsigned char *st = smem + stage * C::STAGE;
 #pragma unroll
-      for (int i = 0; i < C::AI; ++i)
+    for (int i = 0; i < C::AI; ++i)
+      if (k0 + alc[i] * 8 >= K)
         *reinterpret_cast<u32x4 *>(st + (wid * C::AI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < C::BI; ++i)
-        *reinterpret_cast<u32x4 *>(st + BM * 128 + (wid * C::BI + i) * 1024 + l * 16) =
+    for (int i = 0; i < C::BI; ++i)
+      if (k0 + blc[i] * 8 >= K)
+        *reinterpret_cast<u32x4 *>(st + BM * C::RB + (wid * C::BI + i) * 1024 + l * 16) =
             u32x4{0, 0, 0, 0};
-    }
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -211,21 +174,23 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // per-lane fragment offsets inside a stage
+  // per-lane fragment offsets inside a stage (fragment rows start at
+  // multiples of 32, so the swizzle of row base + (l & 31) depends on l only)
   int a_row_off[C::FM], b_row_off[C::FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) a_row_off[i] = (wm * C::TM + i * 32 + (l & 31)) * 128;
+  for (int i = 0; i < C::FM; ++i) a_row_off[i] = (wm * C::TM + i * 32 + (l & 31)) * C::RB;
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) b_row_off[j] = BM * 128 + (wn * C::TN + j * 32 + (l & 31)) * 128;
-  int chunk_off[kBK / 16];
+  for (int j = 0; j < C::FN; ++j)
+    b_row_off[j] = BM * C::RB + (wn * C::TN + j * 32 + (l & 31)) * C::RB;
+  int chunk_off[BK / 16];
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) chunk_off[kk] = (((kk * 2 + (l >> 5)) ^ (l & 7)) * 16);
+  for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = C::swz(kk * 2 + (l >> 5), l & 31) * 16;
 
-  const int KT = (K + kBK - 1) / kBK;
-  const bool ktail = (K % kBK) != 0;
+  const int KT = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s * kBK);
+    if (s < KT) issue(s, s * BK);
 
   if constexpr (LORA) {
     // LoRA increment first, straight into the zeroed accumulators, while the
@@ -312,20 +277,14 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
             u32x4 phi, plo;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-              uint32_t hw = 0, lw = 0;
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                const int e = e2 * 2 + h2;
-                // H entries of u's rows are written for k < r; everything
-                // else (other rows, k >= r) is masked by select, never used
-                const float hv = (in_u && kb + e < r) ? sc * h[e] : 0.f;
-                const uint32_t hb = f32_to_bf16_rne(hv);
-                const uint32_t lb = f32_to_bf16_rne(hv - bf16_to_f32(hb));
-                hw |= hb << (16 * h2);
-                lw |= lb << (16 * h2);
-              }
+              // H entries of u's rows are written for k < r; everything
+              // else (other rows, k >= r) is masked by select, never used
+              const int e = e2 * 2;
+              const float v0 = (in_u && kb + e < r) ? sc * h[e] : 0.f;
+              const float v1 = (in_u && kb + e + 1 < r) ? sc * h[e + 1] : 0.f;
+              const uint32_t hw = pack_bf16x2(v0, v1);
               phi[e2] = hw;
-              plo[e2] = lw;
+              plo[e2] = pack_bf16x2(v0 - bf16_lo(hw), v1 - bf16_hi(hw));
             }
             ahi[kk] = as_bf16x8(phi);
             alo[kk] = as_bf16x8(plo);
@@ -350,12 +309,12 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = min(STAGES - 2, KT - 1 - kt);
     wait_ahead<C::IPW>(ahead);
-    if (ktail && kt == KT - 1) zero_tail(kt % STAGES, kt * kBK);
+    if (ktail && kt == KT - 1) zero_tail(kt % STAGES, kt * BK);
     lgkm_barrier();
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * kBK);
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
     const unsigned char *st = smem + (kt % STAGES) * C::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       mfma_bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
@@ -469,15 +428,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
   const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(((ntiles + 7) / 8) * 8);
   dim3 block(WM * WN * kWave);
   if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, STAGES, true>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, true>), grid, block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, STAGES, false>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, false>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 

@@ -16,15 +16,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  bf16 is the upper half of an IEEE-754 binary32; widening is
-// a shift, narrowing rounds to nearest, ties to even, and keeps NaN quiet.
+// a shift, narrowing rounds to nearest, ties to even.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
+
+// Round to nearest even with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Two packed bf16 (low half = first element) -> two floats.
@@ -32,7 +34,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  const hw_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
 }
 
 // Element traits: 16-byte vectors hold 8 bf16 or 4 fp32.

@@ -15,6 +15,9 @@
 // every load of a work item is issued before its arithmetic, so a work item
 // costs about one memory round trip.  Each token row lives in exactly one
 // segment, so Y is updated without atomics and results are deterministic.
+#include <climits>
+
+#include "lds_dma.cuh"
 #include "lora_device.cuh"
 #include "lora_kernels.h"
 
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
     const int32_t *num_segments, int r_max, int d_in, int policy, int blocks_per_seg,
-    int cap_items, float *__restrict__ H) {
+    int cap_items, int long_min, float *__restrict__ H) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kCV = 8;
   constexpr int kChunk = kCV * kWave * V;  // elements of d_in per pass
@@ -54,6 +57,7 @@ __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
     if (s >= S) break;
     const int R = rank_bucket(r, policy, r_max);
     if (k >= R) continue;
+    if (o1 - o0 >= long_min) continue;   // long segment: tiled MFMA kernel
     const int p0 = o0 + b * kRowBlk;
     const int p1 = min(o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
@@ -102,6 +106,125 @@ __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
         if (lane == 0 && q < nq && k < r) H[(int64_t)token_indices[q0 + q] * r_max + k] = v;
       }
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// shrink of long segments (prefill): a tiled MFMA product per segment,
+//   H[rows of s][0:64] = X[token_indices[rows]] A_slot[0:64]^T,
+// 64 rows x 64 rank columns per tile, K = d_in streamed through a 6-stage
+// LDS ring with direct global->LDS loads (the row gather is free: every
+// lane supplies its own source address).  Each X row is read once per
+// segment tile instead of once per rank row.  Rank rows past R are not
+// fetched (their loads re-read row R-1); columns k >= r are not stored.
+// ----------------------------------------------------------------------------
+constexpr int kLongRows = 128;   // segments at least this long take the MFMA path
+constexpr int kMfmaShrinkMinBatch = 2048;
+constexpr int kSM = 64, kSN = 64, kSStages = 6;
+
+__global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
+    const bf16_t *__restrict__ X, int64_t ldx, const bf16_t *__restrict__ A,
+    const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
+    const int32_t *seg_rank, const int32_t *num_segments, int r_max, int d_in, int policy,
+    int tiles_per_seg, int cap_items, float *__restrict__ H) {
+  constexpr int NW = 4;
+  constexpr int AI = kSM / 8 / NW, BI = kSN / 8 / NW, IPW = AI + BI;
+  constexpr int STAGE = (kSM + kSN) * 128;
+  constexpr int BK = 64;
+  __shared__ __align__(16) unsigned char smem[kSStages * STAGE];
+  const int tid = threadIdx.x;
+  const int l = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int wm = wid >> 1, wn = wid & 1;
+  // 128-byte LDS rows, chunk c of row r at c ^ ((r >> 1) & 7): 16
+  // consecutive rows at one chunk hit 16 distinct bank groups
+  const int r8 = l >> 3;
+  const uint32_t sbase = lds_offset(smem);
+  const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * AI * 1024);
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + kSM * 128 + wid * BI * 1024);
+  const int a_row_off = (wm * 32 + (l & 31)) * 128;
+  const int b_row_off = kSM * 128 + (wn * 32 + (l & 31)) * 128;
+  int chunk_off[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = (((kk * 2 + (l >> 5)) ^ ((l >> 1) & 7)) * 16);
+  int alc[AI], blc[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) alc[i] = (l & 7) ^ ((((wid * AI + i) * 8 + r8) >> 1) & 7);
+#pragma unroll
+  for (int i = 0; i < BI; ++i) blc[i] = (l & 7) ^ ((((wid * BI + i) * 8 + r8) >> 1) & 7);
+  const int KT = (d_in + BK - 1) / BK;
+  const bool ktail = (d_in % BK) != 0;
+  const int S = *num_segments;
+
+  for (int item = blockIdx.x; item < cap_items; item += gridDim.x) {
+    const int s = item / tiles_per_seg;
+    const int t = item - s * tiles_per_seg;
+    const int r = seg_rank[s];
+    const int o0 = seg_off[s], o1 = seg_off[s + 1];
+    const int slot = seg_slot[s];
+    if (s >= S) break;
+    const int R = rank_bucket(r, policy, r_max);
+    if (R == 0 || o1 - o0 < kLongRows) continue;
+    const int p0 = o0 + t * kSM;
+    if (p0 >= o1) continue;
+    const int p1 = min(o1, p0 + kSM);
+
+    const bf16_t *asrc[AI];
+    const bf16_t *bsrc[BI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int p = min(p0 + (wid * AI + i) * 8 + r8, p1 - 1);
+      asrc[i] = X + (int64_t)token_indices[p] * ldx + alc[i] * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int k = min((wid * BI + i) * 8 + r8, R - 1);
+      bsrc[i] = A + ((int64_t)slot * r_max + k) * d_in + blc[i] * 8;
+    }
+    auto issue = [&](int stage, int k0) {
+#pragma unroll
+      for (int i = 0; i < AI; ++i)
+        dma16(a_dst + stage * STAGE + i * 1024, asrc[i] + ((k0 + alc[i] * 8 < d_in) ? k0 : -alc[i] * 8));
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        dma16(b_dst + stage * STAGE + i * 1024, bsrc[i] + ((k0 + blc[i] * 8 < d_in) ? k0 : -blc[i] * 8));
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int st = 0; st < kSStages - 1; ++st)
+      if (st < KT) issue(st, st * BK);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_ahead<IPW>(min(kSStages - 2, KT - 1 - kt));
+      if (ktail && kt == KT - 1) {
+        unsigned char *st = smem + (kt % kSStages) * STAGE;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+          if (kt * BK + alc[i] * 8 >= d_in)
+            *reinterpret_cast<u32x4 *>(st + (wid * AI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+          if (kt * BK + blc[i] * 8 >= d_in)
+            *reinterpret_cast<u32x4 *>(st + kSM * 128 + (wid * BI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+      }
+      lgkm_barrier();
+      if (kt + kSStages - 1 < KT) issue((kt + kSStages - 1) % kSStages, (kt + kSStages - 1) * BK);
+      const unsigned char *st = smem + (kt % kSStages) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const mfma_bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off + chunk_off[kk]));
+        const mfma_bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off + chunk_off[kk]));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+      }
+    }
+    const int k = wn * 32 + (l & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int p = p0 + wm * 32 + acc_row(v, l);
+      if (p < p1 && k < r) H[(int64_t)token_indices[p] * r_max + k] = acc[v];
+    }
+    lgkm_barrier();  // the next item's loads reuse the stages
   }
 }
 
@@ -269,18 +392,34 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
   // Real items: every segment has >= 1 row, so sum_s ceil(n_s / kRowBlk) <= S + n / kRowBlk.
   const int real_bound = S_bound + n / kRowBlk;
+  // long segments (>= kLongRows rows) go to the tiled MFMA kernel in large
+  // (prefill-sized) batches; decode-sized batches keep every segment on the
+  // GEMV kernel and launch nothing more
+  const bool use_mfma = pool.dtype == 1 && n >= kMfmaShrinkMinBatch;
+  const int long_min = use_mfma ? kLongRows : INT_MAX;
   dim3 grid((pool.r_max + kW - 1) / kW, grid_items(real_bound));
   dim3 block(kW * kWave);
   if (pool.dtype == 1) {
     hipLaunchKernelGGL((shrink_kernel<bf16_t, kW, kRows>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, bps, S_bound * bps, H);
+                       pool.d_in, pool.policy, bps, S_bound * bps, long_min, H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float, kW, kRows>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, bps, S_bound * bps, H);
+                       pool.d_in, pool.policy, bps, S_bound * bps, long_min, H);
+  }
+  if (use_mfma) {
+    const int tps = (n + kSM - 1) / kSM;
+    // one workgroup per (segment, tile) item up to 2048, so a workgroup
+    // walks at most a few (mostly empty) items
+    const int items = S_bound * tps;
+    const int g = items < 2048 ? items : 2048;
+    hipLaunchKernelGGL(shrink_mfma_kernel, dim3(g), dim3(4 * kWave), 0, stream, (const bf16_t *)X,
+                       ldx, (const bf16_t *)pool.A, seg.token_indices, seg.seg_off, seg.seg_slot,
+                       seg.seg_rank, seg.num_segments, pool.r_max, pool.d_in, pool.policy, tps,
+                       S_bound * tps, H);
   }
   return hipGetLastError();
 }

@@ -113,6 +113,9 @@ CASES = [
     (106, 257, 96, 88, 300, 16, 0.5, "bf16", False),
     (107, 70, 64, 64, 4, 64, 0.1, "f32", True),
     (108, 513, 200, 120, 17, 32, 0.1, "f32", False),
+    # long segments (tiled shrink) with a ragged K tail, large-tile GEMM K tail
+    (109, 700, 200, 136, 7, 64, 0.1, "bf16", True),
+    (110, 2100, 328, 264, 5, 32, 0.2, "bf16", True),
 ]
 
 
@@ -264,3 +267,45 @@ def test_graph_replay_matches_eager():
         assert torch.equal(seg.token_indices[:w.n].cpu(),
                            torch.as_tensor(eager.meta["token_indices"])), rep
         _ = (Y.float() * 2).sum().item()                   # eager work between replays
+
+
+def test_two_stream_step_in_graph_matches_eager():
+    """Base GEMM on a second stream beside build + shrink, joined before the
+    expand, captured in one HIP graph: every replay equals the eager
+    separate path bit for bit."""
+    w = wl.make_random(29, n=256, d_in=512, d_out=384, n_slots=50, r_max=16, dtype="bf16")
+    eager = run_hip(w, fused=False)
+    d = eager.d
+    pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha)
+    seg = srg.Segments(w.n, w.n_slots, DEV)
+    H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=DEV)
+    Y = torch.zeros((w.n, w.d_out), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def step():
+        main = torch.cuda.current_stream()
+        fork.record(main)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            srg.lora_base_gemm(d["X"], d["W"], Y)
+        join.record(side)
+        srg.lora_build_segments(d["row_slot"], pool, seg)
+        srg.lora_shrink(d["X"], seg, pool, H)
+        main.wait_event(join)
+        srg.lora_expand(H, seg, pool, Y)
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(Y, eager.Ys)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        Y.fill_(0)
+        H.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager.Ys), rep
+        _ = (Y.float() + 1).sum().item()
