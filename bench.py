@@ -283,6 +283,39 @@ def roofline_for(kernel, fig, sec, dtype):
             "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def kernel_source_sha():
+    """sha256 over the HIP sources and headers the kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "segmented_rank_gemm_segment_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` on `config` from rocprofv3 FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch, each scaled by the reading of a plain
+    copy of known size), or None when no counters were taken for the current
+    kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_sha():
+        return None
+    k = t.get("configs", {}).get(str(config), {}).get(kernel)
+    if not k:
+        return None
+    return int(round((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024))
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on the whole headline batch, repeated for
     about `budget_s` seconds of host time."""
@@ -345,6 +378,7 @@ def main():
     # (overlap: same kernels as separate, base GEMM concurrent with build + shrink)
     main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)
+    roof["traffic"] = measured_traffic(args.config, main_k)
     sh, ex = m["per_kernel_s"]["shrink"], m["per_kernel_s"]["expand"]
     se_bytes = fig["bytes"]["shrink"] + fig["bytes"]["expand"]
     out = {
@@ -384,7 +418,8 @@ def main():
             "workload": WORKLOAD_NAMES[3], "rows": w3.n,
             "tokens_s": round(w3.n / m3["step"]["fused"][0], 1),
             "ms_per_step": round(m3["step"]["fused"][0] * 1e3, 4), "path": "fused",
-            "fused_gemm": roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
+            "fused_gemm": dict(roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
+                               traffic=measured_traffic(3, "fused")),
             "shrink_expand": {"GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
                                             (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1)},
             "kernels": k3,

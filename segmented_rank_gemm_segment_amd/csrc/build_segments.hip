@@ -111,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   // Pass 1: validate, remember keys, first row and row count per key.  One
   // LDS atomic per group of equal keys in a wave; min/add commute, so the
   // result does not depend on the order they land in.
-  auto pass1 = [&](int c, int slot) -> int {
+  uint64_t peersreg[kRegChunks];  // pass-1 groups of the register chunks, reused in pass 4
+  auto pass1 = [&](int c, int slot, uint64_t &peers_out) -> int {
     const int i = c * nthr + tid;
     const bool valid = i < n;
     bool bad = false;
@@ -123,14 +124,18 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
       atomicMin(&s_first[key], i);
       atomicAdd(&s_cnt[key], __popcll(peers));
     }
+    peers_out = peers;
     return key;
   };
 #pragma unroll
-  for (int c = 0; c < kRegChunks; ++c)
-    if (c < nchunks) keyreg[c] = pass1(c, keyreg[c]);
+  for (int c = 0; c < kRegChunks; ++c) {
+    peersreg[c] = 0;
+    if (c < nchunks) keyreg[c] = pass1(c, keyreg[c], peersreg[c]);
+  }
   for (int c = kRegChunks; c < nchunks; ++c) {
     const int i = c * nthr + tid;
-    const int key = pass1(c, i < n ? a.row_slot[i] : -1);
+    uint64_t unused;
+    const int key = pass1(c, i < n ? a.row_slot[i] : -1, unused);
     if (i < n) a.row_segment[i] = key;
   }
   __syncthreads();
@@ -208,10 +213,9 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   // chunks and waves + rows of the same key in lower lanes.  Wave 0 walks
   // the 16 waves' group leaders in order, so the cross-wave part follows
   // row order exactly.
-  auto pass4 = [&](int c, int key) {
+  auto pass4 = [&](int c, int key, uint64_t peers) {
     const int i = c * nthr + tid;
     const bool valid = i < n;
-    const uint64_t peers = match_key(key, valid);
     const int local = __popcll(peers & lanemask_lt());
     s_lead_cnt[tid] = (valid && local == 0) ? __popcll(peers) : 0;
     s_lead_key[tid] = key;
@@ -242,10 +246,11 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   };
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c)
-    if (c < nchunks) pass4(c, keyreg[c]);
+    if (c < nchunks) pass4(c, keyreg[c], peersreg[c]);
   for (int c = kRegChunks; c < nchunks; ++c) {
     const int i = c * nthr + tid;
-    pass4(c, i < n ? a.row_segment[i] : 0);
+    const int key = i < n ? a.row_segment[i] : 0;
+    pass4(c, key, match_key(key, i < n));
   }
 
   if (tid == 0) {

@@ -50,7 +50,7 @@ struct GemmArgs {
 // Tile configurations <BM, BN, waves along M, waves along N, K per stage,
 // LDS stages>: small-M (decode-like) batches and large batches.
 #ifndef LORA_GEMM_SMALL
-#define LORA_GEMM_SMALL 64, 64, 2, 2, 64, 6
+#define LORA_GEMM_SMALL 64, 64, 2, 2, 64, 4
 #endif
 #ifndef LORA_GEMM_LARGE
 #define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2
@@ -260,6 +260,8 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        // one fragment row's operands live at a time (a deeper software
+        // pipeline here spills and measured slower)
         __builtin_amdgcn_sched_barrier(0);
         const int rr = i * 32 + (l & 31);
         const bool in_u = __shfl(useg[(i * 32) / kWave], rr % kWave) == u;

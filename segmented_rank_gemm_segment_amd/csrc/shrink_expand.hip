@@ -37,7 +37,7 @@ template <typename T, int kWaves, int kRows>
 __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
-    const int32_t *num_segments, int r_max, int d_in, int policy, int blocks_per_seg,
+    const int32_t *num_segments, int r_max, int d_in, int policy, int seg_cap,
     int cap_items, int long_min, float *__restrict__ H) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kCV = 8;
@@ -46,15 +46,18 @@ __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
   const int wave = threadIdx.x / kWave;
   const int k = blockIdx.x * kWaves + wave;
   const int S = *num_segments;
+  // items are ordered block-major (item = b * seg_cap + s): the first row
+  // block of every segment comes first, so launch-order work is real work
+  // and later (mostly empty) blocks cost one metadata read each
   for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
-    const int s = item / blocks_per_seg;
-    const int b = item - s * blocks_per_seg;
+    const int b = item / seg_cap;
+    const int s = item - b * seg_cap;
     // metadata of segment s is read before S is known (s < capacity keeps it
     // in bounds), so both loads travel together
     const int r = seg_rank[s];
     const int o0 = seg_off[s], o1 = seg_off[s + 1];
     const int slot = seg_slot[s];
-    if (s >= S) break;
+    if (s >= S) continue;
     const int R = rank_bucket(r, policy, r_max);
     if (k >= R) continue;
     if (o1 - o0 >= long_min) continue;   // long segment: tiled MFMA kernel
@@ -334,22 +337,23 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     const float *__restrict__ H, const T *__restrict__ Bt, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
     const float *seg_scale, const int32_t *num_segments, int r_max, int d_out, int policy,
-    int blocks_per_seg, int cap_items, T *__restrict__ Y, int64_t ldy) {
+    int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int col = ((blockIdx.x * kExpWaves + wave) * 16 + (lane & 15)) * V;
   const bool active = col < d_out;
   const int S = *num_segments;
+  // block-major items (item = b * seg_cap + s), as in the shrink
   for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
-    const int s = item / blocks_per_seg;
-    const int b = item - s * blocks_per_seg;
+    const int b = item / seg_cap;
+    const int s = item - b * seg_cap;
     // read before S is known (in bounds below the capacity) so the loads overlap
     const int r = seg_rank[s];
     const int o0 = seg_off[s], o1 = seg_off[s + 1];
     const int slot = seg_slot[s];
     const float sc = seg_scale[s];
-    if (s >= S) break;
+    if (s >= S) continue;
     const int R = rank_bucket(r, policy, r_max);
     if (R == 0) continue;
     const int p0 = o0 + b * kRowBlk;
@@ -376,9 +380,12 @@ inline int seg_bound(int n_rows, int n_slots, int max_segments) {
   return b < max_segments ? b : max_segments;
 }
 
-inline int grid_items(int bound_items) {
-  const int cap = 4096;
-  return bound_items < cap ? (bound_items > 0 ? bound_items : 1) : cap;
+// Workgroup rows for `items` work items when each row has `x` workgroups:
+// one row per item, but at most ~16k workgroups in all (the rest stride).
+inline int grid_items(int items, int x) {
+  int cap = 16384 / (x > 0 ? x : 1);
+  cap = cap > 1 ? cap : 1;
+  return items < cap ? (items > 0 ? items : 1) : cap;
 }
 
 }  // namespace
@@ -397,18 +404,22 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
   // GEMV kernel and launch nothing more
   const bool use_mfma = pool.dtype == 1 && n >= kMfmaShrinkMinBatch;
   const int long_min = use_mfma ? kLongRows : INT_MAX;
-  dim3 grid((pool.r_max + kW - 1) / kW, grid_items(real_bound));
+  // one workgroup row per item up to the cap (empty items exit after one
+  // metadata read, in parallel rather than one after another)
+  (void)real_bound;
+  const int gx = (pool.r_max + kW - 1) / kW;
+  dim3 grid(gx, grid_items(S_bound * bps, gx));
   dim3 block(kW * kWave);
   if (pool.dtype == 1) {
     hipLaunchKernelGGL((shrink_kernel<bf16_t, kW, kRows>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, bps, S_bound * bps, long_min, H);
+                       pool.d_in, pool.policy, S_bound, S_bound * bps, long_min, H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float, kW, kRows>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, bps, S_bound * bps, long_min, H);
+                       pool.d_in, pool.policy, S_bound, S_bound * bps, long_min, H);
   }
   if (use_mfma) {
     const int tps = (n + kSM - 1) / kSM;
@@ -428,11 +439,13 @@ template <typename T, int RMAX>
 void launch_expand_t(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
                      int bps, int S_bound, int real_bound, hipStream_t stream) {
   const int cols_per_block = kExpWaves * 16 * Elem<T>::kVec;
-  dim3 grid((pool.d_out + cols_per_block - 1) / cols_per_block, grid_items(real_bound));
+  (void)real_bound;
+  const int gx = (pool.d_out + cols_per_block - 1) / cols_per_block;
+  dim3 grid(gx, grid_items(S_bound * bps, gx));
   hipLaunchKernelGGL((expand_kernel<T, RMAX>), grid, dim3(kExpWaves * kWave), 0, stream, H,
                      (const T *)pool.Bt, seg.token_indices, seg.seg_off, seg.seg_slot,
                      seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max, pool.d_out,
-                     pool.policy, bps, S_bound * bps, (T *)Y, ldy);
+                     pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
 }
 
 template <typename T>
