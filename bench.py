@@ -56,6 +56,8 @@ def parse():
                    help="total size of the rotated copies of the layer tensors")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-vendor", action="store_true",
+                   help="skip timing the base product through torch.matmul for comparison")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -157,6 +159,13 @@ def k_expand(L):
     srg.lora_expand(L.H, L.seg, L.pool, L.Y)
 
 
+def k_vendor_base(L):
+    """The same X W^T through torch.matmul (the vendor BLAS): timed for
+    comparison only, never part of a step."""
+    import torch
+    torch.matmul(L.X, L.W.t(), out=L.Y)
+
+
 class _Overlap:
     """Base GEMM on a second stream, concurrent with build + shrink on the
     launch stream; the expand waits for both (fork/join through events, so
@@ -231,7 +240,7 @@ def time_calls(fn_seq, layers, iters, warmup, use_graph):
 
 
 def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
-            device="cuda:0"):
+            device="cuda:0", vendor=False):
     import torch
     L0 = Layer(w, policy, device)
     copies = max(1, int(np.ceil(rotate_mb * 1e6 / L0.nbytes)))
@@ -248,7 +257,23 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
     per_kernel = {}
     for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
-    return {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
+    res = {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
+    if vendor:
+        k_vendor_base(layers[0])          # library set-up outside any capture
+        torch.cuda.synchronize()
+        res["vendor_base_s"], _ = time_calls((k_vendor_base,), layers, kl, max(3, warmup // 4),
+                                             use_graph)
+    return res
+
+
+def vendor_entry(fig, m):
+    """Context: the base product through the vendor BLAS on the same operands."""
+    if "vendor_base_s" not in m:
+        return None
+    t = m["vendor_base_s"]
+    return {"what": "torch.matmul(X, W.t()) (hipBLASLt), same shape, operands and launch mode",
+            "us": round(t * 1e6, 3), "TFLOP_s": round(fig["flops"]["base"] / t / 1e12, 2),
+            "ours_base_us": round(m["per_kernel_s"]["base"] * 1e6, 3)}
 
 
 def kernel_table(fig, per_kernel, dtype):
@@ -316,15 +341,8 @@ def measured_traffic(config, kernel):
     return int(round((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024))
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle as it stands, on the whole headline batch, repeated for
-    about `budget_s` seconds of host time."""
+def _oracle_rate(w, budget_s):
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
     runs, rows, t0 = 0, 0, time.perf_counter()
     while True:
         oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)
@@ -334,11 +352,29 @@ def cpu_baseline(w, budget_s=12.0):
         rows += w.n
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return {"value": round(rows / el, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{runs} full passes of the {w.n}-row batch (metadata + float64 row loop) in {el:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            return rows / el, runs, el
+
+
+def cpu_baseline(w, budget_s=12.0, single_core_s=6.0):
+    """The oracle as it stands, on the whole headline batch, repeated for
+    about `budget_s` seconds of host time on every core the BLAS uses, then
+    for about `single_core_s` seconds with one BLAS thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        threads = len(os.sched_getaffinity(0))
+    rate, runs, el = _oracle_rate(w, budget_s)
+    out = {"value": round(rate, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{runs} full passes of the {w.n}-row batch (metadata + float64 row loop) in {el:.1f} s",
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if threadpool_limits is not None and single_core_s > 0:
+        with threadpool_limits(limits=1):
+            r1, runs1, el1 = _oracle_rate(w, single_core_s)
+        out["single_core"] = {"value": round(r1, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"{runs1} full passes in {el1:.1f} s"}
+    return out
 
 
 def main():
@@ -370,7 +406,7 @@ def main():
     fig = work_figures(w)
     paths = list(PATHS) if args.path == "auto" else [args.path]
     m = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
-                args.kernel_loops, not args.eager)
+                args.kernel_loops, not args.eager, vendor=not args.no_vendor and w.dtype == "bf16")
     path = min(paths, key=lambda p: m["step"][p][0])
     step_s, wall = m["step"][path]
     kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
@@ -407,12 +443,14 @@ def main():
         "step_us_by_path": {p: round(m["step"][p][0] * 1e6, 3) for p in paths},
         "host_wall_s": round(wall, 4),
     }
+    if vendor_entry(fig, m):
+        out["vendor_base_gemm"] = vendor_entry(fig, m)
     if not args.no_prefill and args.config != 3:
         w3 = wl.make_config(3)
         f3 = work_figures(w3)
         st3 = max(5, args.steps // 10)
         m3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
-                     not args.eager)
+                     not args.eager, vendor=not args.no_vendor)
         k3 = kernel_table(f3, m3["per_kernel_s"], "bf16")
         out["prefill"] = {
             "workload": WORKLOAD_NAMES[3], "rows": w3.n,
@@ -424,6 +462,8 @@ def main():
                                             (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1)},
             "kernels": k3,
         }
+        if vendor_entry(f3, m3):
+            out["prefill"]["vendor_base_gemm"] = vendor_entry(f3, m3)
         del w3
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

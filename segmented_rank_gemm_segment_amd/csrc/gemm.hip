@@ -55,6 +55,9 @@ struct GemmArgs {
 #ifndef LORA_GEMM_LARGE
 #define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2
 #endif
+#ifndef LORA_GEMM_SGB
+#define LORA_GEMM_SGB 1
+#endif
 #ifndef LORA_GEMM_SMALL_M
 #define LORA_GEMM_SMALL_M 512
 #endif
@@ -188,8 +191,9 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
 
   const int KT = (K + BK - 1) / BK;
   const bool ktail = (K % BK) != 0;
+  // every buffer of the ring is free at the start: fill all of them
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (s < KT) issue(s, s * BK);
 
   if constexpr (LORA) {
@@ -308,28 +312,65 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
     }
   }
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = min(STAGES - 2, KT - 1 - kt);
-    wait_ahead<C::IPW>(ahead);
-    if (ktail && kt == KT - 1) zero_tail(kt % STAGES, kt * BK);
-    lgkm_barrier();
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
-    const unsigned char *st = smem + (kt % STAGES) * C::STAGE;
+  // Software pipeline over K.  Fragments of sub-step kk + 1 are read from
+  // LDS while the MFMAs of sub-step kk run.  Before the last sub-step of
+  // stage kt the workgroup waits for stage kt + 1 and passes one barrier
+  // (every wave has by then read all of stage kt into registers), refills
+  // stage kt's buffer with stage kt + STAGES, reads the first fragments of
+  // stage kt + 1, and only then issues the last MFMAs of stage kt, so the
+  // barrier overlaps with the matrix pipe draining.
+  constexpr int KK = BK / 16;
+  mfma_bf16x8 af[2][C::FM], bfr[2][C::FN];
+  auto load_frags = [&](int buf, const unsigned char *st, int kk) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      mfma_bf16x8 af[C::FM], bfr[C::FN];
+    for (int i = 0; i < C::FM; ++i)
+      af[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off[i] + chunk_off[kk]));
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off[i] + chunk_off[kk]));
+    for (int j = 0; j < C::FN; ++j)
+      bfr[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off[j] + chunk_off[kk]));
+  };
+  auto mfmas = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off[j] + chunk_off[kk]));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: one MFMA, then one LDS read, while reads remain
+  auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < C::FM * C::FN; ++q) {
+      if (LORA_GEMM_SGB) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (LORA_GEMM_SGB && q < C::FM + C::FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+  };
+
+  // stage 0 landed (the later stages may stay in flight)
+  wait_ahead<C::IPW>(min(STAGES - 1, KT - 1));
+  if (ktail && KT == 1) zero_tail(0, 0);
+  lgkm_barrier();
+  load_frags(0, smem, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const unsigned char *st = smem + (kt % STAGES) * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KK - 1; ++kk) {
+      load_frags((kk + 1) & 1, st, kk + 1);
+      mfmas(kk & 1);
+      interleave();
+    }
+    if (kt + 1 < KT) {
+      // stages issued so far: 0 .. min(kt - 1 + STAGES, KT - 1); the ones
+      // after kt + 1 may stay in flight
+      wait_ahead<C::IPW>(min(STAGES - 2, KT - 2 - kt));
+      if (ktail && kt + 1 == KT - 1) zero_tail((kt + 1) % STAGES, (kt + 1) * BK);
+      lgkm_barrier();
+      if (kt + STAGES < KT) issue(kt % STAGES, (kt + STAGES) * BK);
+    }
+    // unconditional, so the accumulators see one straight-line update (after
+    // the last stage this reads a settled buffer and the values go unused)
+    load_frags(KK & 1, smem + ((kt + 1) % STAGES) * C::STAGE, 0);
+    mfmas((KK - 1) & 1);
+    interleave();
   }
 
   // store: bf16 round to nearest even, once

@@ -120,6 +120,38 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid) {
   return mine;
 }
 
+// Per-segment metadata gathered with one vector load: lanes 0..5 read the
+// batch's segment count and segment s's rank, two offsets, slot and scale
+// (scale may be null), and every lane gets them by readlane.  One memory
+// round trip instead of a chain of dependent scalar loads.  s must index
+// the segment arrays in bounds (s < capacity); the caller compares s with S.
+struct SegMeta {
+  int S, r, o0, o1, slot;
+  float sc;
+};
+__device__ __forceinline__ SegMeta load_seg_meta(int s, const int32_t *num_segments,
+                                                 const int32_t *seg_rank, const int32_t *seg_off,
+                                                 const int32_t *seg_slot, const float *seg_scale) {
+  const int l = __lane_id();
+  const int32_t *scale_bits =
+      seg_scale != nullptr ? reinterpret_cast<const int32_t *>(seg_scale + s) : num_segments;
+  const int32_t *p = l == 0   ? num_segments
+                     : l == 1 ? seg_rank + s
+                     : l == 2 ? seg_off + s
+                     : l == 3 ? seg_off + s + 1
+                     : l == 4 ? seg_slot + s
+                              : scale_bits;
+  const int v = l < 6 ? *p : 0;
+  SegMeta m;
+  m.S = __builtin_amdgcn_readlane(v, 0);
+  m.r = __builtin_amdgcn_readlane(v, 1);
+  m.o0 = __builtin_amdgcn_readlane(v, 2);
+  m.o1 = __builtin_amdgcn_readlane(v, 3);
+  m.slot = __builtin_amdgcn_readlane(v, 4);
+  m.sc = __int_as_float(__builtin_amdgcn_readlane(v, 5));
+  return m;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);

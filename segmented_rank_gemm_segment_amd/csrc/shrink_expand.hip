@@ -45,68 +45,76 @@ __global__ __launch_bounds__(kWaves * kWave) void shrink_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int k = blockIdx.x * kWaves + wave;
-  const int S = *num_segments;
   // items are ordered block-major (item = b * seg_cap + s): the first row
   // block of every segment comes first, so launch-order work is real work
   // and later (mostly empty) blocks cost one metadata read each
   for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
     const int b = item / seg_cap;
     const int s = item - b * seg_cap;
-    // metadata of segment s is read before S is known (s < capacity keeps it
-    // in bounds), so both loads travel together
-    const int r = seg_rank[s];
-    const int o0 = seg_off[s], o1 = seg_off[s + 1];
-    const int slot = seg_slot[s];
-    if (s >= S) continue;
+    // s < capacity keeps the metadata read in bounds before S is known
+    const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, nullptr);
+    if (s >= m.S) continue;
+    const int r = m.r;
     const int R = rank_bucket(r, policy, r_max);
     if (k >= R) continue;
-    if (o1 - o0 >= long_min) continue;   // long segment: tiled MFMA kernel
-    const int p0 = o0 + b * kRowBlk;
-    const int p1 = min(o1, p0 + kRowBlk);
+    if (m.o1 - m.o0 >= long_min) continue;   // long segment: tiled MFMA kernel
+    const int p0 = m.o0 + b * kRowBlk;
+    const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
-    const T *arow = A + ((int64_t)slot * r_max + k) * d_in;
+    const T *arow = A + ((int64_t)m.slot * r_max + k) * d_in;
     for (int q0 = p0; q0 < p1; q0 += kRows) {
       const int nq = min(kRows, p1 - q0);
-      const T *xrow[kRows];
-#pragma unroll
-      for (int q = 0; q < kRows; ++q)
-        xrow[q] = X + (int64_t)token_indices[q0 + min(q, nq - 1)] * ldx;
+      // row indices of the group in one vector load (lane q: row q; lanes
+      // past the group repeat its last row), issued ahead of the adapter
+      // row, so waiting for them does not wait for the adapter row
+      const int tv = token_indices[q0 + min(lane, nq - 1)];
+      __builtin_amdgcn_sched_barrier(0);
       float acc[kRows];
 #pragma unroll
       for (int q = 0; q < kRows; ++q) acc[q] = 0.f;
       for (int c0 = 0; c0 < d_in; c0 += kChunk) {
+        // addresses past d_in are clamped into the row (d_in is a multiple
+        // of 8), so every load is unconditional; those values are zeroed
+        // where they are used, after all loads are in flight
         uint4 av[kCV];
-        uint4 xv[kRows][kCV];
 #pragma unroll
         for (int v = 0; v < kCV; ++v) {
           const int c = c0 + (v * kWave + lane) * V;
-          av[v] = c < d_in ? ldg16(arow + c) : zero4();
+          av[v] = ldg16(arow + min(c, d_in - V));
         }
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 xv[kRows][kCV];
 #pragma unroll
         for (int q = 0; q < kRows; ++q) {
+          const T *xrow = X + (int64_t)__builtin_amdgcn_readlane(tv, q) * ldx;
 #pragma unroll
           for (int v = 0; v < kCV; ++v) {
             const int c = c0 + (v * kWave + lane) * V;
-            xv[q][v] = (q < nq && c < d_in) ? ldg16(xrow[q] + c) : zero4();
+            xv[q][v] = ldg16(xrow + min(c, d_in - V));
           }
         }
+        __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use
 #pragma unroll
         for (int v = 0; v < kCV; ++v) {
+          const bool ok = c0 + (v * kWave + lane) * V < d_in;
           float af[V];
           Elem<T>::unpack(av[v], af);
+#pragma unroll
+          for (int e = 0; e < V; ++e) af[e] = ok ? af[e] : 0.f;
 #pragma unroll
           for (int q = 0; q < kRows; ++q) {
             float xf[V];
             Elem<T>::unpack(xv[q][v], xf);
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc[q] = fmaf(af[e], xf[e], acc[q]);
+            for (int e = 0; e < V; ++e) acc[q] = fmaf(af[e], ok ? xf[e] : 0.f, acc[q]);
           }
         }
       }
 #pragma unroll
       for (int q = 0; q < kRows; ++q) {
         const float v = wave_sum(acc[q]);
-        if (lane == 0 && q < nq && k < r) H[(int64_t)token_indices[q0 + q] * r_max + k] = v;
+        if (lane == 0 && q < nq && k < r)
+          H[(int64_t)__builtin_amdgcn_readlane(tv, q) * r_max + k] = v;
       }
     }
   }
@@ -252,6 +260,11 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
   constexpr int V = Elem<T>::kVec;
   constexpr int NB = (R + 15) / 16;   // rank blocks of 4 per lane (at most)
   const int kq = lane >> 4;
+  // the first group's row indices travel ahead of the adapter rows (one
+  // vector load: lane q holds row q, lanes past the group repeat its last
+  // row), so waiting for them does not wait for the adapter rows
+  int tv = token_indices[p0 + min(lane, min(kExpSub, p1 - p0) - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   uint4 braw[NB][4];
   bool blk_ok[NB];
 #pragma unroll
@@ -259,28 +272,57 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
     const int k0 = 4 * (kq + 4 * jb);
     blk_ok[jb] = k0 < R;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
       // rank rows in [r, R) are read, as a kernel compiled for width R
-      // would, and masked below (the mask depends on r, so the load stays)
-      braw[jb][e] = (active && blk_ok[jb]) ? ldg16(bt + (int64_t)(k0 + e) * d_out) : zero4();
+      // would; rows past the block are clamped into the slot.  Values are
+      // masked where they are used (rank rows >= r) and inactive columns
+      // are never stored.
+      braw[jb][e] = ldg16(bt + (int64_t)min(k0 + e, r_max - 1) * d_out);
+    }
   }
-  for (int q0 = p0; q0 < p1; q0 += kExpSub) {
+  __builtin_amdgcn_sched_barrier(0);
+  // one group of up to kExpSub rows whose indices are in tv
+  auto group = [&](int q0, int tv) __attribute__((always_inline)) {
     const int nq = min(kExpSub, p1 - q0);
     int rows[kExpSub];
 #pragma unroll
-    for (int q = 0; q < kExpSub; ++q) rows[q] = token_indices[q0 + min(q, nq - 1)];
+    for (int q = 0; q < kExpSub; ++q) rows[q] = __builtin_amdgcn_readlane(tv, q);
+    const int myq = kq;  // Y row updated by this lane
+    const int yrow = rows[0] * (myq == 0) + rows[1] * (myq == 1) + rows[2] * (myq == 2) +
+                     rows[3] * (myq == 3);
+    // inactive columns read column 0 of the row (in bounds) and never store.
+    // Issued by hand so it leaves with the H loads rather than next to the
+    // store (the compiler otherwise places it after the arithmetic); it is
+    // waited for explicitly before use.
+    u32x4 y4;
+    asm volatile("global_load_dwordx4 %0, %1, off"
+                 : "=v"(y4)
+                 : "v"(Y + (int64_t)yrow * ldy + (active ? col : 0))
+                 : "memory");
     float4 hv[kExpSub][NB];
 #pragma unroll
     for (int q = 0; q < kExpSub; ++q)
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
-        // block start k0 < R <= r_max and r_max % 8 == 0: the float4 is in the row
-        const int k0 = 4 * (kq + 4 * jb);
-        hv[q][jb] = blk_ok[jb] ? *reinterpret_cast<const float4 *>(H + (int64_t)rows[q] * r_max + k0)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        // block start k0 < R <= r_max and r_max % 8 == 0: the float4 is in
+        // the row; blocks past R read the row's last float4 and are zeroed
+        // (masked where used, by the same rank test as the adapter rows)
+        const int k0 = min(4 * (kq + 4 * jb), r_max - 4);
+        hv[q][jb] = *reinterpret_cast<const float4 *>(H + (int64_t)rows[q] * r_max + k0);
       }
-    const int myq = kq;  // Y row updated by this lane
-    const uint4 yraw = (active && myq < nq) ? ldg16(Y + (int64_t)rows[myq] * ldy + col) : zero4();
+    __builtin_amdgcn_sched_barrier(0);   // Y and H loads issued before any use
+    // the adapter rows are first needed here, after this group's loads are
+    // issued (the empty asm keeps their unpacking here: the compiler would
+    // otherwise hoist it, and the wait for them, above those loads)
+    uint4 bcur[NB][4];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bcur[jb][e] = braw[jb][e];
+        asm volatile("" : "+v"(bcur[jb][e].x), "+v"(bcur[jb][e].y), "+v"(bcur[jb][e].z),
+                     "+v"(bcur[jb][e].w));
+      }
     float acc[kExpSub][V];
 #pragma unroll
     for (int q = 0; q < kExpSub; ++q)
@@ -293,7 +335,7 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
         const int k = 4 * (kq + 4 * jb) + e4;
         const bool live = blk_ok[jb] && k < r;
         float bv[V];
-        Elem<T>::unpack(braw[jb][e4], bv);
+        Elem<T>::unpack(bcur[jb][e4], bv);
 #pragma unroll
         for (int e = 0; e < V; ++e) bv[e] = live ? bv[e] : 0.f;
 #pragma unroll
@@ -313,21 +355,27 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
         acc[q][e] += __shfl_xor(acc[q][e], 16);
         acc[q][e] += __shfl_xor(acc[q][e], 32);
       }
-    if (active && myq < nq) {
-      float yv[V];
-      Elem<T>::unpack(yraw, yv);
-      float out[V];
+    // the sum is formed in every lane (so the Y load above is not sunk into
+    // the guarded store) and stored by the lanes that own a row
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(y4) : : "memory");
+    float yv[V];
+    Elem<T>::unpack(make_uint4(y4.x, y4.y, y4.z, y4.w), yv);
+    float out[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        // select this lane's row without dynamic register indexing
-        float a = 0.f;
+    for (int e = 0; e < V; ++e) {
+      // select this lane's row without dynamic register indexing
+      float a = 0.f;
 #pragma unroll
-        for (int q = 0; q < kExpSub; ++q) a = (q == myq) ? acc[q][e] : a;
-        out[e] = fmaf(sc, a, yv[e]);
-      }
-      stg16(Y + (int64_t)rows[myq] * ldy + col, Elem<T>::pack(out));
+      for (int q = 0; q < kExpSub; ++q) a = (q == myq) ? acc[q][e] : a;
+      out[e] = fmaf(sc, a, yv[e]);
     }
-  }
+    const uint4 packed = Elem<T>::pack(out);
+    if (active && myq < nq) stg16(Y + (int64_t)yrow * ldy + col, packed);
+  };
+  // the first group straight after the adapter-row loads, the rest in a loop
+  group(p0, tv);
+  for (int q0 = p0 + kExpSub; q0 < p1; q0 += kExpSub)
+    group(q0, token_indices[q0 + min(lane, min(kExpSub, p1 - q0) - 1)]);
 }
 
 // RMAX = the pool's r_max: only rank buckets up to it are compiled in, so a
@@ -343,21 +391,19 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
   const int wave = threadIdx.x / kWave;
   const int col = ((blockIdx.x * kExpWaves + wave) * 16 + (lane & 15)) * V;
   const bool active = col < d_out;
-  const int S = *num_segments;
   // block-major items (item = b * seg_cap + s), as in the shrink
   for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
     const int b = item / seg_cap;
     const int s = item - b * seg_cap;
-    // read before S is known (in bounds below the capacity) so the loads overlap
-    const int r = seg_rank[s];
-    const int o0 = seg_off[s], o1 = seg_off[s + 1];
-    const int slot = seg_slot[s];
-    const float sc = seg_scale[s];
-    if (s >= S) continue;
+    // s < capacity keeps the metadata read in bounds before S is known
+    const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, seg_scale);
+    if (s >= m.S) continue;
+    const int r = m.r, slot = m.slot;
+    const float sc = m.sc;
     const int R = rank_bucket(r, policy, r_max);
     if (R == 0) continue;
-    const int p0 = o0 + b * kRowBlk;
-    const int p1 = min(o1, p0 + kRowBlk);
+    const int p0 = m.o0 + b * kRowBlk;
+    const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
     const T *bt = Bt + (int64_t)slot * r_max * d_out + (active ? col : 0);
     if (R == 8) {
@@ -405,21 +451,24 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
   const bool use_mfma = pool.dtype == 1 && n >= kMfmaShrinkMinBatch;
   const int long_min = use_mfma ? kLongRows : INT_MAX;
   // one workgroup row per item up to the cap (empty items exit after one
-  // metadata read, in parallel rather than one after another)
+  // metadata read, in parallel rather than one after another).  When long
+  // segments go to the MFMA kernel, the GEMV kernel only sees segments
+  // shorter than kLongRows, whose rows fit in the first few row blocks.
   (void)real_bound;
+  const int gemv_bps = use_mfma ? min(bps, (kLongRows + kRowBlk - 1) / kRowBlk) : bps;
   const int gx = (pool.r_max + kW - 1) / kW;
-  dim3 grid(gx, grid_items(S_bound * bps, gx));
+  dim3 grid(gx, grid_items(S_bound * gemv_bps, gx));
   dim3 block(kW * kWave);
   if (pool.dtype == 1) {
     hipLaunchKernelGGL((shrink_kernel<bf16_t, kW, kRows>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, S_bound, S_bound * bps, long_min, H);
+                       pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min, H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float, kW, kRows>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, S_bound, S_bound * bps, long_min, H);
+                       pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min, H);
   }
   if (use_mfma) {
     const int tps = (n + kSM - 1) / kSM;
