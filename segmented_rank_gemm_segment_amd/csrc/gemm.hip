@@ -47,13 +47,14 @@ struct GemmArgs {
   int r_max, policy;
 };
 
-// Tile configurations <BM, BN, waves along M, waves along N, K per stage,
-// LDS stages>: small-M (decode-like) batches and large batches.
+// Tile configurations <BM, BN, waves along M, waves along N, K per group
+// slice, LDS stages, K groups>: small-M (decode-like) batches and large
+// batches.
 #ifndef LORA_GEMM_SMALL
-#define LORA_GEMM_SMALL 64, 64, 2, 2, 64, 4
+#define LORA_GEMM_SMALL 64, 64, 2, 2, 64, 4, 2
 #endif
 #ifndef LORA_GEMM_LARGE
-#define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2
+#define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2, 1
 #endif
 #ifndef LORA_GEMM_SGB
 #define LORA_GEMM_SGB 1
@@ -62,24 +63,31 @@ struct GemmArgs {
 #define LORA_GEMM_SMALL_M 512
 #endif
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+// KG wave groups split each K step: group g takes the g-th BK-wide slice of
+// it with its own WM x WN waves and its own slice of the stage, and the
+// groups' partial sums are added through LDS at the end (KG = 1: one group).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
 struct TileCfg {
-  static constexpr int NW = WM * WN;
+  static constexpr int NWG = WM * WN;               // waves per group
+  static constexpr int NW = NWG * KG;
   static constexpr int T = NW * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int CH = BK / 8;                 // 16-byte chunks per operand row
   static constexpr int RB = BK * 2;                 // bytes per operand row in LDS
   static constexpr int RPI = 1024 / RB;             // rows per 1 KB DMA instruction
-  static constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;  // DMA instructions per wave
+  static constexpr int AI = BM / RPI / NWG, BI = BN / RPI / NWG;  // DMA instructions per wave
   static constexpr int IPW = AI + BI;
-  static constexpr int STAGE = (BM + BN) * RB;      // bytes
+  static constexpr int GSTAGE = (BM + BN) * RB;     // bytes of one group's slice
+  static constexpr int STAGE = KG * GSTAGE;         // bytes of a stage
+  static constexpr int KSTEP = KG * BK;             // K per stage
   static constexpr int LDS = STAGES * STAGE;
+  static constexpr int RED = (KG - 1) * NWG * FM * FN * 16 * kWave * 4;  // partial sums
   static_assert(BK == 32 || BK == 64, "K per stage");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA split");
+  static_assert(BM % (RPI * NWG) == 0 && BN % (RPI * NWG) == 0, "DMA split");
   static_assert(STAGES >= 2 && STAGES - 2 <= 6 && (STAGES - 2) * IPW <= 63, "pipeline depth");
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(LDS <= 160 * 1024 && RED <= LDS, "LDS");
   // physical chunk of logical chunk c in row r.  The gfx950 LDS serves a
   // 16-byte read for 16 lanes at a time across 64 four-byte banks (256
   // bytes), i.e. two 128-byte rows or four 64-byte rows per bank row; the
@@ -92,15 +100,17 @@ struct TileCfg {
 
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool LORA>
-__global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
-  using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, bool LORA>
+__global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
+  using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG>;
   __shared__ __align__(16) unsigned char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
-  const int wid = tid / kWave;
+  const int kgrp = tid / (kWave * C::NWG);          // K group (wave-uniform)
+  const int wid = (tid / kWave) % C::NWG;           // wave within the group
   const int wm = wid / WN, wn = wid % WN;
+  const int kg0 = kgrp * BK;                        // the group's offset in a K step
   const int M = g.M, N = g.N, K = g.K;
 
   // XCD-aware tile order: consecutive workgroup ids go to different XCDs
@@ -141,8 +151,10 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
     bsrc[i] = g.W + (int64_t)min(n0 + row, N - 1) * g.ldw + blc[i] * 8;
   }
   const uint32_t sbase = lds_offset(smem);
-  const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * C::AI * 1024);
-  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + BM * C::RB + wid * C::BI * 1024);
+  const uint32_t a_dst =
+      __builtin_amdgcn_readfirstlane(sbase + kgrp * C::GSTAGE + wid * C::AI * 1024);
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + kgrp * C::GSTAGE + BM * C::RB +
+                                                        wid * C::BI * 1024);
 
   auto issue = [&](int stage, int k0) {
     // a chunk past K reads the row's first chunk instead (in bounds) and is
@@ -156,8 +168,17 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
       dma16(b_dst + stage * C::STAGE + i * 1024,
             bsrc[i] + ((k0 + blc[i] * 8 < K) ? k0 : -blc[i] * 8));
   };
+  // instruction q of a stage's DMA (A rows first, then B rows)
+  auto issue_one = [&](int q, int stage, int k0) __attribute__((always_inline)) {
+    if (q < C::AI)
+      dma16(a_dst + stage * C::STAGE + q * 1024,
+            asrc[q] + ((k0 + alc[q] * 8 < K) ? k0 : -alc[q] * 8));
+    else
+      dma16(b_dst + stage * C::STAGE + (q - C::AI) * 1024,
+            bsrc[q - C::AI] + ((k0 + blc[q - C::AI] * 8 < K) ? k0 : -blc[q - C::AI] * 8));
+  };
   auto zero_tail = [&](int stage, int k0) {
-    unsigned char *st = smem + stage * C::STAGE;
+    unsigned char *st = smem + stage * C::STAGE + kgrp * C::GSTAGE;
 #pragma unroll
     for (int i = 0; i < C::AI; ++i)
       if (k0 + alc[i] * 8 >= K)
@@ -181,22 +202,23 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
   // multiples of 32, so the swizzle of row base + (l & 31) depends on l only)
   int a_row_off[C::FM], b_row_off[C::FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) a_row_off[i] = (wm * C::TM + i * 32 + (l & 31)) * C::RB;
+  for (int i = 0; i < C::FM; ++i)
+    a_row_off[i] = kgrp * C::GSTAGE + (wm * C::TM + i * 32 + (l & 31)) * C::RB;
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
-    b_row_off[j] = BM * C::RB + (wn * C::TN + j * 32 + (l & 31)) * C::RB;
+    b_row_off[j] = kgrp * C::GSTAGE + BM * C::RB + (wn * C::TN + j * 32 + (l & 31)) * C::RB;
   int chunk_off[BK / 16];
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = C::swz(kk * 2 + (l >> 5), l & 31) * 16;
 
-  const int KT = (K + BK - 1) / BK;
-  const bool ktail = (K % BK) != 0;
+  const int KT = (K + C::KSTEP - 1) / C::KSTEP;
+  const bool ktail = (K % C::KSTEP) != 0;
   // every buffer of the ring is free at the start: fill all of them
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
-    if (s < KT) issue(s, s * BK);
+    if (s < KT) issue(s, s * C::KSTEP + kg0);
 
-  if constexpr (LORA) {
+  if (LORA && kgrp == 0) {
     // LoRA increment first, straight into the zeroed accumulators, while the
     // first stages are in flight.  Per distinct LoRA segment among this
     // wave's rows (ascending segment id): A operand = s_u H[row][k] for rows
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
 
   // stage 0 landed (the later stages may stay in flight)
   wait_ahead<C::IPW>(min(STAGES - 1, KT - 1));
-  if (ktail && KT == 1) zero_tail(0, 0);
+  if (ktail && KT == 1) zero_tail(0, kg0);
   lgkm_barrier();
   load_frags(0, smem, 0);
   for (int kt = 0; kt < KT; ++kt) {
@@ -362,15 +384,64 @@ __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(GemmArgs g) {
       // stages issued so far: 0 .. min(kt - 1 + STAGES, KT - 1); the ones
       // after kt + 1 may stay in flight
       wait_ahead<C::IPW>(min(STAGES - 2, KT - 2 - kt));
-      if (ktail && kt + 1 == KT - 1) zero_tail((kt + 1) % STAGES, (kt + 1) * BK);
+      if (ktail && kt + 1 == KT - 1) zero_tail((kt + 1) % STAGES, (kt + 1) * C::KSTEP + kg0);
       lgkm_barrier();
-      if (kt + STAGES < KT) issue(kt % STAGES, (kt + STAGES) * BK);
     }
-    // unconditional, so the accumulators see one straight-line update (after
-    // the last stage this reads a settled buffer and the values go unused)
+    // Last sub-step: its MFMAs with the refill of stage kt's buffer, one DMA
+    // instruction between MFMAs (a burst of DMAs would hold up the MFMAs),
+    // then the first fragments of stage kt + 1.  The MFMAs and fragment
+    // reads are unconditional so the accumulators see one straight-line
+    // update (after the last stage the reads hit a settled buffer and their
+    // values go unused).
+    const bool refill = kt + STAGES < KT;
+    const int k0n = (kt + STAGES) * C::KSTEP + kg0;
+#pragma unroll
+    for (int q = 0; q < C::FM * C::FN || q < C::IPW; ++q) {
+      if (q < C::IPW && refill) issue_one(q, kt % STAGES, k0n);
+      if (q < C::FM * C::FN) {
+        const int i = q / C::FN, j = q % C::FN;
+        constexpr int b = (KK - 1) & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc[i][j], 0, 0, 0);
+      }
+    }
     load_frags(KK & 1, smem + ((kt + 1) % STAGES) * C::STAGE, 0);
-    mfmas((KK - 1) & 1);
-    interleave();
+  }
+
+  if constexpr (KG > 1) {
+    // groups 1.. hand their partial sums to group 0 through LDS (every
+    // read of the ring and every DMA into it has finished: the last stage
+    // was waited for in full and the barrier drains the reads); group 0
+    // adds them in group order
+    lgkm_barrier();
+    float *red = reinterpret_cast<float *>(smem);
+    auto slot_of = [&](int gi, int i, int j, int v4) {
+      return (((gi * C::NWG + wid) * C::FM * C::FN + i * C::FN + j) * 4 + v4) * (kWave * 4) + l * 4;
+    };
+    if (kgrp > 0) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            *reinterpret_cast<f32x4 *>(red + slot_of(kgrp - 1, i, j, v4)) =
+                f32x4{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                      acc[i][j][4 * v4 + 3]};
+    }
+    lgkm_barrier();
+    if (kgrp > 0) return;
+#pragma unroll
+    for (int gi = 0; gi < KG - 1; ++gi)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 p = *reinterpret_cast<const f32x4 *>(red + slot_of(gi, i, j, v4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * v4 + e] += p[e];
+          }
   }
 
   // store: bf16 round to nearest even, once
@@ -471,15 +542,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
 hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
   const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(((ntiles + 7) / 8) * 8);
-  dim3 block(WM * WN * kWave);
+  dim3 block(WM * WN * KG * kWave);
   if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, true>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, true>), grid, block, 0,
+                       stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, false>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, false>), grid, block, 0,
+                       stream, g);
   return hipGetLastError();
 }
 
