@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 
@@ -79,6 +79,11 @@ typedef enum {
  *   Bt[n_slots][r_max][d_out]  row k = column k of B_a   (B_a in R^{d_out x r})
  * Rows k >= slot_rank[a] are padding and are never multiplied in.
  * slot_scale[a] is s_a = alpha_a / r_a (0 for a rank-0 slot).
+ * Optionally the pool also carries B in its own d_out-major layout,
+ *   B [n_slots][d_out][r_max]  row j = row j of B_a   (the layout of the
+ *                              adapter's up-projection weight),
+ * the same values as Bt.  lora_linear_fused then reads whole 16-byte runs of
+ * rank values per output column; with B NULL it gathers them from Bt.
  */
 typedef struct {
   int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
@@ -91,6 +96,7 @@ typedef struct {
   const void *Bt;            /* device */
   const int32_t *slot_rank;  /* device, [n_slots] */
   const float *slot_scale;   /* device, [n_slots] */
+  const void *B;             /* device, optional (NULL): [n_slots][d_out][r_max] */
 } lora_pool;
 
 /*

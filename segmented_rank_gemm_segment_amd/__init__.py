@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -47,6 +47,7 @@ class LoraPoolC(ctypes.Structure):
         ("Bt", ctypes.c_void_p),
         ("slot_rank", ctypes.c_void_p),
         ("slot_scale", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
     ]
 
 
@@ -155,15 +156,18 @@ class Pool:
     (rank-major; row k of Bt[a] is column k of B_a), ``slot_rank`` int32
     [n_slots] and per-slot alpha.  The per-slot scale alpha/r is stored as
     float32 (0 for rank 0) when the pool is created, as adapter loading does.
+    With ``natural_b`` (default) the pool also keeps B in its d_out-major
+    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM.
     """
 
     def __init__(self, A: torch.Tensor, Bt: torch.Tensor, slot_rank: torch.Tensor,
-                 slot_alpha, rank_policy: str = "exact"):
+                 slot_alpha, rank_policy: str = "exact", natural_b: bool = True):
         if A.dim() != 3 or Bt.dim() != 3 or A.shape[:2] != Bt.shape[:2]:
             raise ValueError("A [n_slots, r_max, d_in] and Bt [n_slots, r_max, d_out] expected")
         if A.dtype != Bt.dtype or not A.is_contiguous() or not Bt.is_contiguous():
             raise ValueError("A and Bt: same dtype, contiguous")
         self.A, self.Bt = A, Bt
+        self.B = Bt.transpose(1, 2).contiguous() if natural_b else None
         self.n_slots, self.r_max, self.d_in = A.shape
         self.d_out = Bt.shape[2]
         self.dtype = A.dtype
@@ -178,7 +182,8 @@ class Pool:
         self.rank_policy = rank_policy
         self._c = LoraPoolC(self.n_slots, self.r_max, self.d_in, self.d_out, _dtype_code(self.dtype),
                             RANK_POLICIES[rank_policy], self.A.data_ptr(), self.Bt.data_ptr(),
-                            self.slot_rank.data_ptr(), self.slot_scale.data_ptr())
+                            self.slot_rank.data_ptr(), self.slot_scale.data_ptr(),
+                            self.B.data_ptr() if self.B is not None else None)
         return self
 
     @property

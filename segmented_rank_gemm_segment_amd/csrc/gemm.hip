@@ -42,6 +42,7 @@ struct GemmArgs {
   // fused LoRA
   const float *H;
   const bf16_t *Bt;
+  const bf16_t *Bn;   // optional d_out-major copy of B ([slot][d_out][r_max]) or null
   const int32_t *row_segment, *seg_slot, *seg_rank;
   const float *seg_scale;
   int r_max, policy;
@@ -100,7 +101,9 @@ struct TileCfg {
 
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, bool LORA>
+// LORA: 0 = plain product; 1 = fused LoRA with B gathered from Bt; 2 = fused
+// LoRA with B read from its d_out-major copy.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG>;
   __shared__ __align__(16) unsigned char smem[C::LDS];
@@ -218,122 +221,6 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   for (int s = 0; s < STAGES; ++s)
     if (s < KT) issue(s, s * C::KSTEP + kg0);
 
-  if (LORA && kgrp == 0) {
-    // LoRA increment first, straight into the zeroed accumulators, while the
-    // first stages are in flight.  Per distinct LoRA segment among this
-    // wave's rows (ascending segment id): A operand = s_u H[row][k] for rows
-    // of u (bf16 high part + bf16 remainder), 0 for other rows; B operand =
-    // Bt_u[k][col] gathered with coalesced 2-byte loads.  Rows outside u get
-    // exact zeros, so base-only rows stay bit-identical to the plain GEMM.
-    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
-    constexpr int RPL = (TM + kWave - 1) / kWave;   // tile rows per lane
-    int useg[RPL];
-#pragma unroll
-    for (int q = 0; q < RPL; ++q) {
-      const int rr = l + kWave * q;
-      const int row = m0 + wm * TM + rr;
-      int u = -1;
-      if (rr < TM && row < M) {
-        const int sg = g.row_segment[row];
-        if (g.seg_rank[sg] > 0) u = sg;
-      }
-      useg[q] = u;
-    }
-    int prev = -1;
-    while (true) {
-      int cand = INT_MAX;
-#pragma unroll
-      for (int q = 0; q < RPL; ++q)
-        if (useg[q] > prev && useg[q] < cand) cand = useg[q];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
-      if (cand == INT_MAX) break;
-      const int u = cand;
-      const int slot = g.seg_slot[u];
-      const int r = g.seg_rank[u];
-      const float sc = g.seg_scale[u];
-      const int R = rank_bucket(r, g.policy, g.r_max);
-      const int KS = (R + 15) / 16;
-      const bf16_t *bt = g.Bt + (int64_t)slot * g.r_max * N;
-      // B operands Bt_u[k][col] for every (column fragment, K step), loaded
-      // once per segment.  Branch-free: the index is clamped into the slot
-      // (rows < R, columns < N) and out-of-range values are masked, so the
-      // loads of a segment issue together.  Rank rows in [r, R) are read as
-      // a width-R kernel would, then zeroed.
-      u32x4 bop[FN][4];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * TN + j * 32 + (l & 31);
-        const bool col_ok = col < N;
-        const int colc = min(col, N - 1);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          if (kk < KS) {
-            const int kb = kk * 16 + (l >> 5) * 8;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              uint32_t w2 = 0;
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                const int k = kb + e2 * 2 + h2;
-                const uint32_t v = bt[(uint32_t)(min(k, R - 1) * N + colc)];
-                w2 |= ((col_ok && k < r) ? v : 0u) << (16 * h2);
-              }
-              bop[j][kk][e2] = w2;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        // one fragment row's operands live at a time (a deeper software
-        // pipeline here spills and measured slower)
-        __builtin_amdgcn_sched_barrier(0);
-        const int rr = i * 32 + (l & 31);
-        const bool in_u = __shfl(useg[(i * 32) / kWave], rr % kWave) == u;
-        // rows past M are clamped for the address only (never in u)
-        const float *hrow = g.H + (int64_t)min(m0 + wm * TM + rr, M - 1) * g.r_max;
-        mfma_bf16x8 ahi[4], alo[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          if (kk < KS) {
-            const int kb = kk * 16 + (l >> 5) * 8;
-            const int kc = min(kb, g.r_max - 8);
-            const float4 h0 = *reinterpret_cast<const float4 *>(hrow + kc);
-            const float4 h1 = *reinterpret_cast<const float4 *>(hrow + kc + 4);
-            const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-            u32x4 phi, plo;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              // H entries of u's rows are written for k < r; everything
-              // else (other rows, k >= r) is masked by select, never used
-              const int e = e2 * 2;
-              const float v0 = (in_u && kb + e < r) ? sc * h[e] : 0.f;
-              const float v1 = (in_u && kb + e + 1 < r) ? sc * h[e + 1] : 0.f;
-              const uint32_t hw = pack_bf16x2(v0, v1);
-              phi[e2] = hw;
-              plo[e2] = pack_bf16x2(v0 - bf16_lo(hw), v1 - bf16_hi(hw));
-            }
-            ahi[kk] = as_bf16x8(phi);
-            alo[kk] = as_bf16x8(plo);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            if (kk < KS) {
-              const mfma_bf16x8 bv = as_bf16x8(bop[j][kk]);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[kk], bv, acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[kk], bv, acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-      prev = u;
-    }
-  }
-
   // Software pipeline over K.  Fragments of sub-step kk + 1 are read from
   // LDS while the MFMAs of sub-step kk run.  Before the last sub-step of
   // stage kt the workgroup waits for stage kt + 1 and passes one barrier
@@ -429,7 +316,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
                       acc[i][j][4 * v4 + 3]};
     }
     lgkm_barrier();
-    if (kgrp > 0) return;
+    if (kgrp == 0)
 #pragma unroll
     for (int gi = 0; gi < KG - 1; ++gi)
 #pragma unroll
@@ -443,6 +330,153 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
             for (int e = 0; e < 4; ++e) acc[i][j][4 * v4 + e] += p[e];
           }
   }
+
+  if constexpr (LORA != 0) {
+    // LoRA increment, after the K loop, one distinct LoRA segment u of the
+    // tile's rows at a time (ascending id).  The whole workgroup stages the
+    // operands of the small product s_u H_u B_u^T in LDS, in the layout of
+    // a K stage (rows of 128 bytes, same swizzle):
+    //   A_hi, A_lo [BM][64]: s_u H[row][k] split into a bf16 high part and
+    //                        a bf16 remainder (about 16 significant bits);
+    //                        rows outside u and k >= r are zero
+    //   Bs        [BN][64]: B_u[col][k], zero for k >= r
+    // and group 0's waves add A_hi Bs^T + A_lo Bs^T into their
+    // accumulators, KS = ceil(R/16) MFMA sub-steps each.  Rows outside u
+    // add exact zeros, so base-only rows stay bit-identical to the plain
+    // product.
+    constexpr int RBL = 128;                          // bytes per staged row
+    static_assert(3 * (BM > BN ? BM : BN) * RBL + 16 <= C::LDS, "LoRA staging");
+    static_assert(C::T >= BM, "one tile row per thread");
+    unsigned char *s_ahi = smem;
+    unsigned char *s_alo = smem + BM * RBL;
+    unsigned char *s_b = smem + 2 * BM * RBL;
+    int *s_next = reinterpret_cast<int *>(smem + 2 * BM * RBL + BN * RBL);
+    auto sw = [](int c, int r) { return ((c ^ ((r >> 1) & 7)) * 16); };
+    // this thread's tile row (threads past BM take no row)
+    int my_seg = -1;
+    if (tid < BM && m0 + tid < M) {
+      const int sg = g.row_segment[m0 + tid];
+      if (g.seg_rank[sg] > 0) my_seg = sg;
+    }
+    // previous readers of LDS (the K loop, the partial sums) are done
+    lgkm_barrier();
+    int prev = -1;
+    while (true) {
+      // next segment id above prev among the tile's rows: wave minimum,
+      // then a workgroup minimum through one LDS word
+      int cand = (my_seg > prev) ? my_seg : INT_MAX;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
+      if (tid == 0) *s_next = INT_MAX;
+      lgkm_barrier();
+      if (l == 0 && cand != INT_MAX) atomicMin(s_next, cand);
+      lgkm_barrier();
+      const int u = __builtin_amdgcn_readfirstlane(*s_next);
+      if (u == INT_MAX) break;
+      prev = u;
+      const int slot = g.seg_slot[u];
+      const int r = g.seg_rank[u];
+      const float sc = g.seg_scale[u];
+      const int R = rank_bucket(r, g.policy, g.r_max);
+      const int KS = (R + 15) / 16;
+      const int NC = 2 * KS;                          // 16-byte chunks per staged row
+      // A: (row, chunk) items
+      for (int it = tid; it < BM * NC; it += C::T) {
+        const int row = it / NC, c = it - (it / NC) * NC;
+        const int grow = m0 + row;
+        float h[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const bool in_u = grow < M && g.row_segment[grow] == u;
+        // chunks past r_max (k >= R >= r, only when r_max = 8) stay zero
+        if (in_u && c * 8 < g.r_max) {
+          const float *hp = g.H + (int64_t)grow * g.r_max + c * 8;
+          const float4 h0 = *reinterpret_cast<const float4 *>(hp);
+          const float4 h1 = *reinterpret_cast<const float4 *>(hp + 4);
+          h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+          h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+        }
+        u32x4 phi, plo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int k = c * 8 + e2 * 2;
+          const float v0 = (in_u && k < r) ? sc * h[e2 * 2] : 0.f;
+          const float v1 = (in_u && k + 1 < r) ? sc * h[e2 * 2 + 1] : 0.f;
+          const uint32_t hw = pack_bf16x2(v0, v1);
+          phi[e2] = hw;
+          plo[e2] = pack_bf16x2(v0 - bf16_lo(hw), v1 - bf16_hi(hw));
+        }
+        *reinterpret_cast<u32x4 *>(s_ahi + row * RBL + sw(c, row)) = phi;
+        *reinterpret_cast<u32x4 *>(s_alo + row * RBL + sw(c, row)) = plo;
+      }
+      // B: rank values of column col, k in chunk c, zero for k >= r
+      if constexpr (LORA == 2) {
+        const bf16_t *bn = g.Bn + (int64_t)slot * N * g.r_max;
+        for (int it = tid; it < BN * NC; it += C::T) {
+          const int col = it / NC, c = it - (it / NC) * NC;
+          const int colc = min(n0 + col, N - 1);     // columns past N: never stored
+          // a chunk past r_max (only when r_max = 8) is read from the
+          // column's first chunk and masked below
+          u32x4 v = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max +
+                                                      min(c * 8, g.r_max - 8));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int k = c * 8 + e2 * 2;
+            v[e2] &= (k < r ? 0x0000ffffu : 0u) | (k + 1 < r ? 0xffff0000u : 0u);
+          }
+          *reinterpret_cast<u32x4 *>(s_b + col * RBL + sw(c, col)) = v;
+        }
+      } else {
+        // from the rank-major Bt: 8 columns of one rank row per item,
+        // transposed into the column rows with 2-byte stores
+        const bf16_t *bt = g.Bt + (int64_t)slot * g.r_max * N;
+        constexpr int CC = BN / 8;
+        for (int it = tid; it < 8 * NC * CC; it += C::T) {
+          const int k = it / CC, cc = it - (it / CC) * CC;
+          const int col0 = n0 + cc * 8;
+          u32x4 v = u32x4{0, 0, 0, 0};
+          if (k < r) v = *reinterpret_cast<const u32x4 *>(bt + (int64_t)k * N + min(col0, N - 8));
+          const int c = k >> 3, kin = k & 7;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int col = cc * 8 + e;
+            const uint16_t hv = (uint16_t)(e & 1 ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+            *reinterpret_cast<uint16_t *>(s_b + col * RBL + sw(c, col) + kin * 2) = hv;
+          }
+        }
+      }
+      lgkm_barrier();
+      if (kgrp == 0) {
+        int ar[C::FM], br[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) ar[i] = (wm * C::TM + i * 32 + (l & 31)) * RBL;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) br[j] = (wn * C::TN + j * 32 + (l & 31)) * RBL;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk < KS) {
+            const int co = sw(kk * 2 + (l >> 5), l & 31);
+            mfma_bf16x8 bv[C::FN];
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+              bv[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_b + br[j] + co));
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+              const mfma_bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_ahi + ar[i] + co));
+              const mfma_bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_alo + ar[i] + co));
+#pragma unroll
+              for (int j = 0; j < C::FN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv[j], acc[i][j], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      // the staging area is rewritten for the next segment
+      lgkm_barrier();
+    }
+  }
+
+  if (KG > 1 && kgrp > 0) return;
 
   // store: bf16 round to nearest even, once
 #pragma unroll
@@ -547,11 +581,14 @@ hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
   const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(((ntiles + 7) / 8) * 8);
   dim3 block(WM * WN * KG * kWave);
-  if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, true>), grid, block, 0,
+  if (lora && g.Bn)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2>), grid, block, 0,
+                       stream, g);
+  else if (lora)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1>), grid, block, 0,
                        stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, false>), grid, block, 0,
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 0>), grid, block, 0,
                        stream, g);
   return hipGetLastError();
 }
@@ -564,9 +601,10 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
   const bool lora = seg != nullptr;
   if (dtype == 1) {
     GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
-               H, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+               H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
     if (lora) {
       g.Bt = (const bf16_t *)pool->Bt;
+      g.Bn = (const bf16_t *)pool->B;
       g.row_segment = seg->row_segment;
       g.seg_slot = seg->seg_slot;
       g.seg_rank = seg->seg_rank;

@@ -27,6 +27,7 @@ lora_status check_pool(const lora_pool *pool) {
   if (pool->d_in % 8 || pool->d_out % 8) return LORA_ERR_ALIGN;
   if (!pool->A || !pool->Bt || !pool->slot_rank || !pool->slot_scale) return LORA_ERR_NULL;
   if (!aligned16(pool->A) || !aligned16(pool->Bt)) return LORA_ERR_ALIGN;
+  if (pool->B && !aligned16(pool->B)) return LORA_ERR_ALIGN;
   return LORA_OK;
 }
 
@@ -62,7 +63,7 @@ lora::SegView seg_view(const lora_segments *s) {
 
 lora::PoolView pool_view(const lora_pool *p) {
   return lora::PoolView{p->n_slots, p->r_max, p->d_in, p->d_out, p->dtype, p->rank_policy,
-                        p->A,       p->Bt};
+                        p->A,       p->Bt,      p->B};
 }
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }

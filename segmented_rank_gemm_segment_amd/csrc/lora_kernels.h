@@ -22,6 +22,7 @@ struct PoolView {
   int n_slots, r_max, d_in, d_out, dtype, policy;
   const void *A;
   const void *Bt;
+  const void *B;   // optional d_out-major copy of B ([n_slots][d_out][r_max]) or null
 };
 
 hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,

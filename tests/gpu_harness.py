@@ -38,10 +38,10 @@ class Run:
 
 
 def run_hip(w: wl.Workload, policy: str = "exact", d=None, separate: bool = True,
-            fused: bool = True) -> Run:
+            fused: bool = True, natural_b: bool = True) -> Run:
     d = d or wl.device_tensors(w, DEV)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha, policy)
+    pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha, policy, natural_b=natural_b)
     seg = srg.Segments(w.n, w.n_slots, DEV)
     out = Run()
     out.pool, out.seg, out.d = pool, seg, d

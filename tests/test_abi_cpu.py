@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 1
+    assert L.lora_abi_version() == srg.ABI_VERSION == 2
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"

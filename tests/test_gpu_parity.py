@@ -208,6 +208,26 @@ def test_policies_give_identical_bits():
         assert torch.equal(o.Ys, outs[0].Ys)
 
 
+@pytest.mark.parametrize("case", [
+    # seed, n, d_in, d_out, n_slots, r_max  (small tiles / large tiles; r_max 8 edge)
+    (40, 300, 256, 200, 9, 64),
+    (41, 130, 128, 96, 5, 8),
+    (42, 900, 192, 264, 6, 32),
+    (43, 700, 136, 72, 4, 8),
+])
+def test_fused_b_layouts_give_identical_bits(case):
+    """The fused product reads B from its d_out-major copy when the pool has
+    one and gathers it from Bt otherwise: same staged values, same bits."""
+    seed, n, d_in, d_out, n_slots, r_max = case
+    say("b layouts", case)
+    w = wl.make_random(seed, n, d_in, d_out, n_slots, r_max, p_base=0.1, dtype="bf16", runs=True)
+    a = run_hip(w, separate=False, natural_b=True)
+    b = run_hip(w, separate=False, natural_b=False)
+    assert a.pool.B is not None and b.pool.B is None
+    assert torch.equal(a.Yf, b.Yf)
+    check_values(w, a)
+
+
 def test_slot_relocation_and_determinism():
     w = wl.make_random(26, n=500, d_in=192, d_out=128, n_slots=12, r_max=32, dtype="bf16")
     a = run_hip(w)
