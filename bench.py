@@ -312,14 +312,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
+def _code_only(text):
+    """C/C++ source without comments and blank space (comment edits do not
+    change the kernels the counters were taken on)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha():
-    """sha256 over the HIP sources and headers the kernels are built from."""
+    """sha256 over the code (comments dropped) of the HIP sources and
+    headers the kernels are built from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "segmented_rank_gemm_segment_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -15,12 +15,12 @@
 // so fragment reads are bank-conflict free.  Tiles are ordered per XCD.
 //
 // Fused LoRA: the rows of an output tile may belong to several segments.
-// Before the K loop, for each distinct LoRA segment u among a wavefront's
-// rows, the scaled H rows of u (split into a bf16 high part and a bf16
-// remainder, so H keeps about 16 significant bits) times Bt_u are
-// accumulated by MFMA into the zeroed accumulators, zero rows standing in
-// for rows of other segments.  Every row gets exactly its own segment's
-// increment, added in fp32 and rounded once with the base product.
+// After the K loop, for each distinct LoRA segment u among the tile's rows,
+// the scaled H rows of u (split into a bf16 high part and a bf16 remainder,
+// so H keeps about 16 significant bits) and B_u are staged in LDS and
+// multiplied by MFMA into the accumulators, zero rows standing in for rows
+// of other segments.  Every row gets exactly its own segment's increment,
+// added in fp32 and rounded once with the base product.
 #include <climits>
 
 #include "lds_dma.cuh"
