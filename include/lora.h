@@ -177,6 +177,32 @@ lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ld
                            int32_t d_out, int32_t dtype, void *stream);
 
 /*
+ * Pack one adapter into slot `slot` of the pool (LoRA/QLoRA 多租户GPU推理服务化实战,
+ * section 1.1 "Adapter的统一尺寸对齐": one preallocated buffer, each adapter packed
+ * into the slot its offset names; adapter-batching page, "动态加载是一个安全边界":
+ * rank and sizes bounded, a failed load leaves the old contents usable, the new
+ * slot published only when its weights are complete).
+ *   A_src [rank][d_in]   ld lda (a multiple of 8)  down-projection A_a, pool dtype
+ *   B_src [d_out][rank]  ld ldb (>= rank)          up-projection B_a, pool dtype
+ * both device memory.  Writes A rows [0, rank) and zeros up to r_max, Bt rows
+ * [0, rank) = B_src transposed and zeros up to r_max, the d_out-major B of the
+ * pool when it has one (zeros past rank), and then, by a second kernel on the
+ * same stream, slot_rank[slot] = rank and slot_scale[slot] = scale (the caller
+ * passes alpha / rank; 0 is stored for rank 0).  Work queued later on `stream`
+ * sees the whole new adapter.  rank = 0 empties the slot (its rows take the
+ * base-only path); A_src and B_src may then be NULL.  The caller must not pack
+ * a slot that queued or running work on other streams still reads (wait for
+ * it first).  The pool's slot_rank and slot_scale arrays are written.
+ * Errors (all before any write): NULL pool or sources, slot outside
+ * [0, n_slots) or rank outside [0, r_max] (LORA_ERR_SHAPE), lda < d_in or
+ * ldb < rank (LORA_ERR_SHAPE), lda not a multiple of 8 or A_src not 16-byte
+ * aligned (LORA_ERR_ALIGN).
+ */
+lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, float scale,
+                                const void *A_src, int64_t lda, const void *B_src, int64_t ldb,
+                                void *stream);
+
+/*
  * Base product with the LoRA expand fused into its epilogue:
  *   Y[i] = X[i] W^T + s_a H[i][0:r] B_a^T
  * (the second low-rank product added straight into the base output, as the

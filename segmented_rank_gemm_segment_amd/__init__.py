@@ -80,6 +80,7 @@ EXPORTS = (
     "lora_build_segments",
     "lora_shrink",
     "lora_expand",
+    "lora_pool_pack_slot",
     "lora_base_gemm",
     "lora_linear_fused",
 )
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.lora_shrink.argtypes = [vp, i64, SP, PP, vp, vp]
     L.lora_expand.restype = i32
     L.lora_expand.argtypes = [vp, SP, PP, vp, i64, vp]
+    L.lora_pool_pack_slot.restype = i32
+    L.lora_pool_pack_slot.argtypes = [PP, i32, i32, ctypes.c_float, vp, i64, vp, i64, vp]
     L.lora_base_gemm.restype = i32
     L.lora_base_gemm.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
     L.lora_linear_fused.restype = i32
@@ -176,7 +179,51 @@ class Pool:
         alpha = torch.as_tensor(slot_alpha, dtype=torch.float64).reshape(-1)
         scale = torch.where(rank_host > 0, alpha / rank_host.clamp(min=1), torch.zeros_like(alpha))
         self.slot_scale = scale.to(torch.float32).to(A.device).contiguous()
+        self.generation = [0] * self.n_slots
         self.set_policy(rank_policy)
+
+    @classmethod
+    def empty(cls, n_slots: int, r_max: int, d_in: int, d_out: int, dtype=torch.bfloat16,
+              device="cuda", rank_policy: str = "exact", natural_b: bool = True) -> "Pool":
+        """A pool of empty slots (rank 0, zero weights), filled by ``pack``."""
+        A = torch.zeros((n_slots, r_max, d_in), dtype=dtype, device=device)
+        Bt = torch.zeros((n_slots, r_max, d_out), dtype=dtype, device=device)
+        rank = torch.zeros(n_slots, dtype=torch.int32, device=device)
+        return cls(A, Bt, rank, 0.0, rank_policy, natural_b)
+
+    def pack(self, slot: int, A: torch.Tensor, B: torch.Tensor, alpha: float, stream=None) -> int:
+        """Load one adapter (A [r, d_in], B [d_out, r], the layouts of the
+        adapter's own weights) into ``slot`` with scale alpha / r, through
+        lora_pool_pack_slot on the device; host tensors are copied over
+        first (from pinned memory, asynchronously).  Returns the slot's new
+        generation.  r = 0 (A [0, d_in], B [d_out, 0]) empties the slot."""
+        r = int(A.shape[0])
+        if A.dim() != 2 or B.dim() != 2 or A.shape[1] != self.d_in or tuple(B.shape) != (self.d_out, r):
+            raise ValueError("A [r, d_in] and B [d_out, r] expected")
+        dev = self.A.device
+        st = torch.cuda.current_stream(dev) if stream is None else stream
+
+        def on_device(t):
+            t = t.to(dtype=self.dtype)
+            if t.device != dev:
+                t = t.contiguous()
+                if t.device.type == "cpu":
+                    t = t.pin_memory()
+                t = t.to(dev, non_blocking=True)
+            return t.contiguous()
+
+        Ad, Bd = on_device(A), on_device(B)
+        scale = float(torch.tensor(float(alpha) / r, dtype=torch.float32)) if r > 0 else 0.0
+        with torch.cuda.stream(st):
+            _check(lib().lora_pool_pack_slot(self.c, int(slot), r, scale,
+                                             _ptr(Ad) if r else None, _ld(Ad) if r else 0,
+                                             _ptr(Bd) if r else None, _ld(Bd) if r else 0,
+                                             _stream(st)))
+        # the copies stay alive until the queued kernels have read them
+        Ad.record_stream(st)
+        Bd.record_stream(st)
+        self.generation[slot] += 1
+        return self.generation[slot]
 
     def set_policy(self, rank_policy: str):
         self.rank_policy = rank_policy

@@ -133,6 +133,29 @@ lora_status lora_expand(const float *H, const lora_segments *seg, const lora_poo
                                         static_cast<hipStream_t>(stream)));
 }
 
+lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, float scale,
+                                const void *A_src, int64_t lda, const void *B_src, int64_t ldb,
+                                void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SHAPE;
+  if (rank < 0 || rank > pool->r_max) return LORA_ERR_SHAPE;
+  if (rank > 0) {
+    if (!A_src || !B_src) return LORA_ERR_NULL;
+    if (lda < pool->d_in || ldb < rank) return LORA_ERR_SHAPE;
+    if (lda % 8 || !aligned16(A_src)) return LORA_ERR_ALIGN;
+  } else {
+    // nothing is read; the pool's own arrays stand in for the sources
+    A_src = pool->A;
+    lda = pool->d_in;
+    B_src = pool->Bt;
+    ldb = 1;
+  }
+  return hip_status(lora::launch_pack_slot(
+      pool_view(pool), const_cast<int32_t *>(pool->slot_rank), const_cast<float *>(pool->slot_scale),
+      slot, rank, scale, A_src, lda, B_src, ldb, static_cast<hipStream_t>(stream)));
+}
+
 lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
                            int64_t ldy, int32_t n_rows, int32_t d_in, int32_t d_out,
                            int32_t dtype, void *stream) {

@@ -37,6 +37,11 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream);
 
+// Adapter weights into a slot, then the slot's rank and scale.
+hipError_t launch_pack_slot(const PoolView &pool, int32_t *slot_rank, float *slot_scale, int slot,
+                            int rank, float scale, const void *A_src, int64_t lda,
+                            const void *B_src, int64_t ldb, hipStream_t stream);
+
 // Y = X W^T (+ fused LoRA when seg/pool/H are given).
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
                        int64_t ldy, int M, int K, int N, int dtype, const float *H,

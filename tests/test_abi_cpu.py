@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
-              "lora_base_gemm", "lora_status_str", "lora_abi_version"):
+              "lora_base_gemm", "lora_pool_pack_slot", "lora_status_str", "lora_abi_version"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -133,6 +133,25 @@ def test_empty_batch_is_a_noop_without_launch(L):
     assert L.lora_linear_fused(0, 64, P, 64, 0, ctypes.byref(s), ctypes.byref(pool()), 0, 32,
                                None) == OK
     assert L.lora_base_gemm(0, 64, P, 64, 0, 32, 0, 64, 32, 1, None) == OK
+
+
+def test_pack_slot_validation(L):
+    """Every bad argument is rejected on the host (nothing is launched)."""
+    p = ctypes.byref(pool())                        # 4 slots, r_max 16, d_in 64, d_out 32
+    A, B = P + 0xC000, P + 0xD000
+    pack = L.lora_pool_pack_slot
+    assert pack(None, 0, 8, 2.0, A, 64, B, 8, None) == ENULL
+    assert pack(p, -1, 8, 2.0, A, 64, B, 8, None) == ESHAPE
+    assert pack(p, 4, 8, 2.0, A, 64, B, 8, None) == ESHAPE
+    assert pack(p, 0, 17, 1.0, A, 64, B, 17, None) == ESHAPE
+    assert pack(p, 0, -1, 1.0, A, 64, B, 8, None) == ESHAPE
+    assert pack(p, 0, 8, 2.0, None, 64, B, 8, None) == ENULL
+    assert pack(p, 0, 8, 2.0, A, 64, None, 8, None) == ENULL
+    assert pack(p, 0, 8, 2.0, A, 56, B, 8, None) == ESHAPE       # lda < d_in
+    assert pack(p, 0, 8, 2.0, A, 68, B, 8, None) == EALIGN       # lda % 8
+    assert pack(p, 0, 8, 2.0, A + 4, 64, B, 8, None) == EALIGN   # A not 16-byte aligned
+    assert pack(p, 0, 8, 2.0, A, 64, B, 7, None) == ESHAPE       # ldb < rank
+    assert pack(ctypes.byref(pool(A=0)), 0, 8, 2.0, A, 64, B, 8, None) == ENULL
 
 
 def test_expand_and_fused_validation(L):

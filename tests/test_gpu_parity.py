@@ -5,6 +5,8 @@ normwise tolerance max|got - ref| / max|ref| <= 1e-2 for bf16 storage with
 fp32 accumulation and <= 1e-5 for fp32, applied separately to H, Y (fused
 and separate paths) and Delta Y.
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -12,8 +14,8 @@ import torch
 import oracle
 import segmented_rank_gemm_segment_amd as srg
 import workloads as wl
-from gpu_harness import (DEV, base_rows_bitwise, check_metadata, check_values, run_hip,
-                         sample_rows, say)
+from gpu_harness import (DEV, TOL, base_rows_bitwise, check_metadata, check_values, normwise,
+                         run_hip, sample_rows, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -329,3 +331,87 @@ def test_two_stream_step_in_graph_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(Y, eager.Ys), rep
         _ = (Y.float() + 1).sum().item()
+
+
+# ---------------------------------------------------------------- adapter packing
+def _run_with_pool(w, pool):
+    """Every entry point on workload w's X, W and mapping, with a given pool."""
+    d = wl.device_tensors(w, DEV)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    seg = srg.Segments(w.n, w.n_slots, DEV)
+    srg.lora_build_segments(d["row_slot"], pool, seg)
+    H = torch.full((w.n, w.r_max), float("nan"), dtype=torch.float32, device=DEV)
+    srg.lora_shrink(d["X"], seg, pool, H)
+    Yf = torch.empty((w.n, w.d_out), dtype=dt, device=DEV)
+    srg.lora_linear_fused(d["X"], d["W"], H, seg, pool, Yf)
+    Ys = torch.empty((w.n, w.d_out), dtype=dt, device=DEV)
+    srg.lora_base_gemm(d["X"], d["W"], Ys)
+    srg.lora_expand(H, seg, pool, Ys)
+    torch.cuda.synchronize()
+    return Yf, Ys
+
+
+def _adapter(w, a):
+    """Slot a's adapter in its own layouts: A [r, d_in], B [d_out, r] (bit patterns)."""
+    r = int(w.slot_rank[a])
+    return w.A[a, :r].copy(), w.B[a, :, :r].copy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pack_slots_layout_and_parity(dtype):
+    """Adapters packed one by one into an empty pool give exactly the pool
+    layout (zeros past the rank) and the oracle's outputs; repacking a slot
+    switches the adapter; rank 0 empties it."""
+    ranks = [8, 32, 5, 16, 1, 24]
+    w = wl.make_random(60, n=200, d_in=136, d_out=72, n_slots=6, r_max=32, ranks=ranks,
+                       p_base=0.1, dtype=dtype, pad="zero")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    pool = srg.Pool.empty(6, 32, 136, 72, dtype=tdt, device=DEV)
+    for a in range(6):
+        Ah, Bh = _adapter(w, a)
+        At = wl.to_torch(Ah, dtype, "cpu" if a % 2 else DEV)   # host and device sources
+        Bt_ = wl.to_torch(Bh, dtype, "cpu" if a % 2 else DEV)
+        assert pool.pack(a, At, Bt_, float(w.slot_alpha[a])) == 1
+    torch.cuda.synchronize()
+    ref = wl.device_tensors(w, DEV)
+    assert torch.equal(pool.A, ref["A"])
+    assert torch.equal(pool.Bt, ref["Bt"])
+    assert torch.equal(pool.B, ref["Bt"].transpose(1, 2).contiguous())
+    assert torch.equal(pool.slot_rank.cpu(), torch.tensor(ranks, dtype=torch.int32))
+    exp_scale = torch.tensor([float(w.slot_alpha[a]) / r for a, r in enumerate(ranks)],
+                             dtype=torch.float64).to(torch.float32)
+    assert torch.equal(pool.slot_scale.cpu(), exp_scale)
+    tol = TOL[dtype]
+    Yr, _, _ = oracle.lora_forward(w.X, w.W, w.A, w.B, w.row_slot, w.slot_rank, w.slot_alpha,
+                                   w.r_max, w.dtype)
+    Yf, Ys = _run_with_pool(w, pool)
+    assert normwise(to_f64(Yf), Yr) <= tol and normwise(to_f64(Ys), Yr) <= tol
+
+    # repack slot 1 with slot 3's adapter (rank 16) and empty slot 2
+    A3, B3 = _adapter(w, 3)
+    assert pool.pack(1, wl.to_torch(A3, dtype, DEV), wl.to_torch(B3, dtype, DEV),
+                     float(w.slot_alpha[3])) == 2
+    empty_A = torch.zeros((0, 136), dtype=tdt)
+    empty_B = torch.zeros((72, 0), dtype=tdt)
+    assert pool.pack(2, empty_A, empty_B, 16.0) == 2
+    torch.cuda.synchronize()
+    w2 = copy.deepcopy(w)
+    w2.A[1] = w.A[3]
+    w2.Bt[1] = w.Bt[3]
+    w2.slot_rank[1] = 16
+    w2.A[2] = 0
+    w2.Bt[2] = 0
+    w2.slot_rank[2] = 0
+    ref2 = wl.device_tensors(w2, DEV)
+    assert torch.equal(pool.A, ref2["A"]) and torch.equal(pool.Bt, ref2["Bt"])
+    assert int(pool.slot_rank[2]) == 0 and float(pool.slot_scale[2]) == 0.0
+    Yr2, _, _ = oracle.lora_forward(w2.X, w2.W, w2.A, w2.B, w2.row_slot, w2.slot_rank,
+                                    w2.slot_alpha, w2.r_max, w2.dtype)
+    Yf2, Ys2 = _run_with_pool(w2, pool)
+    assert normwise(to_f64(Yf2), Yr2) <= tol and normwise(to_f64(Ys2), Yr2) <= tol
+    # rows of the emptied slot now equal the plain product
+    rows = torch.as_tensor(np.nonzero(w.row_slot == 2)[0], device=DEV)
+    Yb = torch.empty_like(Ys2)
+    srg.lora_base_gemm(wl.to_torch(w.X, dtype, DEV), wl.to_torch(w.W, dtype, DEV), Yb)
+    torch.cuda.synchronize()
+    assert torch.equal(Ys2[rows], Yb[rows]) and torch.equal(Yf2[rows], Yb[rows])
