@@ -214,6 +214,11 @@ def time_calls(fn_seq, layers, iters, warmup, use_graph):
     import torch
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if use_graph:
+        # one eager pass first, so that nothing a call sets up on first use
+        # happens during capture
+        for fn in fn_seq:
+            fn(layers[0])
+        torch.cuda.synchronize()
         gw = _graph(fn_seq, layers, max(1, warmup))
         gt = _graph(fn_seq, layers, iters, start=max(1, warmup))
         gw.replay()
