@@ -19,6 +19,9 @@ from .lora_oracle import (  # noqa: F401
     gather_bmm_forward,
     per_adapter_forward,
     merged_forward,
+    dora_column_scale,
+    dora_forward,
+    dora_factored_forward,
     lora_param_count,
     full_param_count,
 )

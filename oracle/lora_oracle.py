@@ -253,6 +253,100 @@ def merged_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype):
 
 
 # ---------------------------------------------------------------------------
+# DoRA: magnitude times normalised direction
+# ---------------------------------------------------------------------------
+# The ybb.press multi-LoRA serving article, section 9.2 (DoRA), writes the
+# adapted weight as a magnitude m times the direction W0 + BA divided by its
+# norm ||W0 + BA||_c, applied at inference by one extra vector normalisation
+# in a custom epilogue.  Readings (the page leaves them open):
+#
+# * the direction is the weight the layer applies, W0 + s_a B_a A_a (the
+#   merged form of the adapter-batching page, "为什么单 Adapter 可以 Merge");
+# * ||.||_c is the 2-norm of each output feature's weight vector, i.e. of
+#   each row of the nn.Linear weight [d_out, d_in], so m_a has d_out entries
+#   and the normalisation is a per-output-column factor (the only kind an
+#   epilogue can apply);
+# * an output feature whose direction row is exactly zero gets a zero row;
+# * a slot without a magnitude vector (None) is a plain LoRA adapter, and
+#   base-only rows and rank-0 slots keep the base weight W0.
+def _direction(W64, A, B, slot_rank, slot_alpha, dtype, a):
+    """V_a = W0 + s_a B_a A_a in float64 (W0 for a rank-0 slot)."""
+    r = int(slot_rank[a])
+    if r == 0:
+        return W64.copy()
+    return W64 + _scale(slot_alpha[a], r) * (decode(B[a, :, :r], dtype) @ decode(A[a, :r, :], dtype))
+
+
+def dora_column_scale(W, A, B, slot_rank, slot_alpha, magnitude, dtype, a):
+    """g_a[j] = m_a[j] / ||V_a[j, :]||_2 for every output feature j of slot a
+    (0 where the norm is 0; all ones when the slot has no magnitude).  The
+    DoRA output of a row on slot a is g_a times its plain LoRA output."""
+    W64 = decode(W, dtype)
+    if magnitude[a] is None:
+        return np.ones(W64.shape[0])
+    V = _direction(W64, A, B, slot_rank, slot_alpha, dtype, a)
+    norm = np.sqrt(np.sum(V * V, axis=1))
+    m = np.asarray(magnitude[a], dtype=np.float64)
+    return np.where(norm > 0.0, m / np.where(norm > 0.0, norm, 1.0), 0.0)
+
+
+def dora_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, magnitude, r_max, dtype,
+                 rows: Optional[Iterable[int]] = None):
+    """DoRA layer by its definition: for every adapter a among the requested
+    rows, build W'_a = m_a * V_a / ||V_a||_c row by row, then y_i = W'_a x_i
+    for the rows on a.  Base-only rows, rank-0 slots and slots without a
+    magnitude use W0 and W0 + s_a B_a A_a as the plain layer does.
+    ``magnitude`` is a list over slots of float arrays [d_out] or None.
+    Returns float64 Y for the requested rows, in request order."""
+    X64 = decode(X, dtype)
+    n = X64.shape[0]
+    rows = list(range(n)) if rows is None else [int(i) for i in rows]
+    keys, _ = validate_rows(row_slot, slot_rank, r_max)
+    W64 = decode(W, dtype)
+    Y = np.zeros((len(rows), W64.shape[0]))
+    req = np.array([keys[i] for i in rows], dtype=np.int64)
+    Xr = X64[rows] if rows else np.zeros((0, X64.shape[1]))
+    for a in sorted(set(req.tolist())):
+        mask = req == a
+        if a == -1 or int(slot_rank[a]) == 0:
+            Wp = W64
+        else:
+            V = _direction(W64, A, B, slot_rank, slot_alpha, dtype, a)
+            if magnitude[a] is None:
+                Wp = V
+            else:
+                m = np.asarray(magnitude[a], dtype=np.float64)
+                Wp = np.zeros_like(V)
+                for j in range(V.shape[0]):
+                    nj = np.sqrt(np.dot(V[j], V[j]))
+                    if nj > 0.0:
+                        Wp[j] = m[j] * V[j] / nj
+        Y[mask] = Xr[mask] @ Wp.T
+    return Y
+
+
+def dora_factored_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, magnitude, r_max, dtype,
+                          rows: Optional[Iterable[int]] = None):
+    """The same layer in the order an epilogue applies it: the plain LoRA
+    output y_i = W0 x_i + s_a B_a A_a x_i, then each output column j times
+    g_a[j] (``dora_column_scale``) on rows of a slot of rank > 0.  Equal to
+    ``dora_forward`` because the normalisation is a per-row factor of W'_a."""
+    Y, _, _ = lora_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype, rows=rows)
+    n = len(row_slot)
+    rows = list(range(n)) if rows is None else [int(i) for i in rows]
+    keys, _ = validate_rows(row_slot, slot_rank, r_max)
+    cache = {}
+    for t, i in enumerate(rows):
+        a = keys[i]
+        if a == -1 or int(slot_rank[a]) == 0:
+            continue
+        if a not in cache:
+            cache[a] = dora_column_scale(W, A, B, slot_rank, slot_alpha, magnitude, dtype, a)
+        Y[t] = Y[t] * cache[a]
+    return Y
+
+
+# ---------------------------------------------------------------------------
 # parameter arithmetic
 # ---------------------------------------------------------------------------
 def lora_param_count(r: int, d_in: int, d_out: int) -> int:

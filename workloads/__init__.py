@@ -339,6 +339,24 @@ def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_m
     return w
 
 
+def make_magnitude(seed: int, n_slots: int, d_out: int, scale: float, p_plain: float = 0.25,
+                   plain_slots=None):
+    """DoRA magnitude vectors, one per slot: float32 [d_out] drawn uniform in
+    [0.5 scale, 1.5 scale], or None (a plain LoRA slot) with probability
+    ``p_plain`` or for the slots listed in ``plain_slots``.  ``scale`` is the
+    caller's guess of a weight row's norm (e.g. w_std * sqrt(d_in)), so DoRA
+    outputs keep the size of the base outputs."""
+    rng = _rng(np.random.SeedSequence([seed, 0xD0]))
+    plain = rng.random(n_slots) < p_plain
+    if plain_slots is not None:
+        plain[list(plain_slots)] = True
+    out = []
+    for a in range(n_slots):
+        m = (rng.random(d_out, dtype=np.float32) + np.float32(0.5)) * np.float32(scale)
+        out.append(None if plain[a] else m.astype(np.float32))
+    return out
+
+
 # --------------------------------------------------------------------------
 # torch views (device placement only)
 # --------------------------------------------------------------------------
