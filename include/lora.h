@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 
@@ -84,6 +84,21 @@ typedef enum {
  *                              adapter's up-projection weight),
  * the same values as Bt.  lora_linear_fused then reads whole 16-byte runs of
  * rank values per output column; with B NULL it gathers them from Bt.
+ *
+ * DoRA (ybb.press multi-LoRA serving article, section 9.2: the adapted
+ * weight is a magnitude m times the direction W0 + BA over its norm, applied
+ * at inference by one extra normalisation in an epilogue).  With the
+ * optional fp32 array
+ *   dora_scale[n_slots][d_out]   g_a[j] = m_a[j] / ||W0[j,:] + s_a (B_a A_a)[j,:]||_2
+ * (0 where that norm is 0), every output element of a row on a slot of rank
+ * r > 0 is multiplied by g_a[j] after the LoRA term is added and before the
+ * rounding, in lora_expand and lora_linear_fused:
+ *   Y[i][j] = g_a[j] (X[i] W^T + s_a H[i][0:r] B_a^T)[j].
+ * The norm is taken over each output feature's weight row (the nn.Linear
+ * row), which is what makes it a per-column epilogue factor.  A slot whose
+ * g row is all ones is a plain LoRA adapter and gives plain LoRA's bits.
+ * Base-only rows and rank-0 slots are never rescaled.  g rows are written by
+ * lora_pool_dora_prepare (and set to ones by lora_pool_pack_slot).
  */
 typedef struct {
   int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
@@ -97,6 +112,7 @@ typedef struct {
   const int32_t *slot_rank;  /* device, [n_slots] */
   const float *slot_scale;   /* device, [n_slots] */
   const void *B;             /* device, optional (NULL): [n_slots][d_out][r_max] */
+  const float *dora_scale;   /* device, optional (NULL): fp32 [n_slots][d_out] DoRA g */
 } lora_pool;
 
 /*
@@ -159,7 +175,9 @@ lora_status lora_shrink(const void *X, int64_t ldx, const lora_segments *seg,
  * Expand and scatter-add, Y[i] += s_a H[i][0:r] B_a^T for every row i of a
  * segment of rank r > 0 (same section: Delta Y_a = s_a H_a B_a^T, added back
  * to the original rows).  Y [n_rows][d_out] (ld ldy), pool dtype; each Y
- * element is read, added in fp32 and rounded once.  Rows of base-only and
+ * element is read, added in fp32 and rounded once.  With pool->dora_scale
+ * the sum is multiplied by the slot's g before the rounding (see lora_pool):
+ * Y[i][j] = g_a[j] (Y[i][j] + s_a H[i][0:r] B_a^T[j]).  Rows of base-only and
  * rank-0 segments are not touched.  Each row belongs to exactly one segment,
  * so no atomics are used and the result is deterministic.
  */
@@ -188,8 +206,10 @@ lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ld
  * [0, rank) = B_src transposed and zeros up to r_max, the d_out-major B of the
  * pool when it has one (zeros past rank), and then, by a second kernel on the
  * same stream, slot_rank[slot] = rank and slot_scale[slot] = scale (the caller
- * passes alpha / rank; 0 is stored for rank 0).  Work queued later on `stream`
- * sees the whole new adapter.  rank = 0 empties the slot (its rows take the
+ * passes alpha / rank; 0 is stored for rank 0).  When the pool has a
+ * dora_scale array, the slot's row of it is set to ones with the weights (the
+ * new adapter starts as plain LoRA; lora_pool_dora_prepare makes it DoRA).
+ * Work queued later on `stream` sees the whole new adapter.  rank = 0 empties the slot (its rows take the
  * base-only path); A_src and B_src may then be NULL.  The caller must not pack
  * a slot that queued or running work on other streams still reads (wait for
  * it first).  The pool's slot_rank and slot_scale arrays are written.
@@ -203,6 +223,26 @@ lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t ran
                                 void *stream);
 
 /*
+ * DoRA column factors of one slot (ybb.press multi-LoRA serving article,
+ * section 9.2): for every output feature j,
+ *   dora_scale[slot][j] = magnitude[j] / ||W[j,:] + s (B_a A_a)[j,:]||_2
+ * with A_a, B_a, the rank r and s = slot_scale[slot] as the pool holds them
+ * when the call runs on `stream` (so it goes after lora_pool_pack_slot on
+ * the same stream); 0 where the norm is 0.  Sums of squares in fp32 from the
+ * stored weights.  W [d_out][d_in] (ld ldw) is the base weight, pool dtype;
+ * magnitude is device fp32 [d_out], or NULL for all ones (the slot then acts
+ * as a plain LoRA adapter).  For a rank-0 slot the factors are written but
+ * never applied.  Work queued later on `stream` sees the new factors.  The
+ * caller must not prepare a slot that work on other streams still reads.
+ * Errors (before any write): NULL pool, pool->dora_scale or W
+ * (LORA_ERR_NULL), slot outside [0, n_slots) or ldw < d_in (LORA_ERR_SHAPE),
+ * dora_scale or W not 16-byte aligned, ldw not a multiple of 8 or magnitude
+ * not 4-byte aligned (LORA_ERR_ALIGN).
+ */
+lora_status lora_pool_dora_prepare(const lora_pool *pool, int32_t slot, const void *W,
+                                   int64_t ldw, const float *magnitude, void *stream);
+
+/*
  * Base product with the LoRA expand fused into its epilogue:
  *   Y[i] = X[i] W^T + s_a H[i][0:r] B_a^T
  * (the second low-rank product added straight into the base output, as the
@@ -210,6 +250,8 @@ lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t ran
  * section 5.3, describes).  H comes from lora_shrink on the same metadata.
  * The fp32 accumulator is rounded to the output dtype once.  Rows of
  * base-only and rank-0 segments equal lora_base_gemm's output bit for bit.
+ * With pool->dora_scale, rows of rank > 0 are multiplied by their slot's g
+ * before the rounding (see lora_pool).
  */
 lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t ldw,
                               const float *H, const lora_segments *seg,

@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -48,6 +48,7 @@ class LoraPoolC(ctypes.Structure):
         ("slot_rank", ctypes.c_void_p),
         ("slot_scale", ctypes.c_void_p),
         ("B", ctypes.c_void_p),
+        ("dora_scale", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +82,7 @@ EXPORTS = (
     "lora_shrink",
     "lora_expand",
     "lora_pool_pack_slot",
+    "lora_pool_dora_prepare",
     "lora_base_gemm",
     "lora_linear_fused",
 )
@@ -109,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.lora_expand.argtypes = [vp, SP, PP, vp, i64, vp]
     L.lora_pool_pack_slot.restype = i32
     L.lora_pool_pack_slot.argtypes = [PP, i32, i32, ctypes.c_float, vp, i64, vp, i64, vp]
+    L.lora_pool_dora_prepare.restype = i32
+    L.lora_pool_dora_prepare.argtypes = [PP, i32, vp, i64, vp, vp]
     L.lora_base_gemm.restype = i32
     L.lora_base_gemm.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
     L.lora_linear_fused.restype = i32
@@ -160,11 +164,14 @@ class Pool:
     [n_slots] and per-slot alpha.  The per-slot scale alpha/r is stored as
     float32 (0 for rank 0) when the pool is created, as adapter loading does.
     With ``natural_b`` (default) the pool also keeps B in its d_out-major
-    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM.
+    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM.  With
+    ``dora`` it keeps DoRA column factors ``dora_scale`` float32 [n_slots,
+    d_out], all ones (plain LoRA) until ``dora_prepare`` sets a slot's.
     """
 
     def __init__(self, A: torch.Tensor, Bt: torch.Tensor, slot_rank: torch.Tensor,
-                 slot_alpha, rank_policy: str = "exact", natural_b: bool = True):
+                 slot_alpha, rank_policy: str = "exact", natural_b: bool = True,
+                 dora: bool = False):
         if A.dim() != 3 or Bt.dim() != 3 or A.shape[:2] != Bt.shape[:2]:
             raise ValueError("A [n_slots, r_max, d_in] and Bt [n_slots, r_max, d_out] expected")
         if A.dtype != Bt.dtype or not A.is_contiguous() or not Bt.is_contiguous():
@@ -173,6 +180,8 @@ class Pool:
         self.B = Bt.transpose(1, 2).contiguous() if natural_b else None
         self.n_slots, self.r_max, self.d_in = A.shape
         self.d_out = Bt.shape[2]
+        self.dora_scale = (torch.ones((self.n_slots, self.d_out), dtype=torch.float32,
+                                      device=A.device) if dora else None)
         self.dtype = A.dtype
         self.slot_rank = slot_rank.to(device=A.device, dtype=torch.int32).contiguous()
         rank_host = self.slot_rank.cpu().to(torch.float64)
@@ -184,12 +193,13 @@ class Pool:
 
     @classmethod
     def empty(cls, n_slots: int, r_max: int, d_in: int, d_out: int, dtype=torch.bfloat16,
-              device="cuda", rank_policy: str = "exact", natural_b: bool = True) -> "Pool":
+              device="cuda", rank_policy: str = "exact", natural_b: bool = True,
+              dora: bool = False) -> "Pool":
         """A pool of empty slots (rank 0, zero weights), filled by ``pack``."""
         A = torch.zeros((n_slots, r_max, d_in), dtype=dtype, device=device)
         Bt = torch.zeros((n_slots, r_max, d_out), dtype=dtype, device=device)
         rank = torch.zeros(n_slots, dtype=torch.int32, device=device)
-        return cls(A, Bt, rank, 0.0, rank_policy, natural_b)
+        return cls(A, Bt, rank, 0.0, rank_policy, natural_b, dora)
 
     def pack(self, slot: int, A: torch.Tensor, B: torch.Tensor, alpha: float, stream=None) -> int:
         """Load one adapter (A [r, d_in], B [d_out, r], the layouts of the
@@ -225,12 +235,34 @@ class Pool:
         self.generation[slot] += 1
         return self.generation[slot]
 
+    def dora_prepare(self, slot: int, W: torch.Tensor, magnitude: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+        """DoRA column factors of ``slot`` from its current weights and the
+        base weight W [d_out, d_in] (lora_pool_dora_prepare):
+        g[j] = magnitude[j] / ||W[j] + s (B A)[j]||, or all ones for
+        magnitude None.  Queue it after ``pack`` on the same stream."""
+        if self.dora_scale is None:
+            raise ValueError("pool was created without dora=True")
+        dev = self.A.device
+        st = torch.cuda.current_stream(dev) if stream is None else stream
+        m = None
+        if magnitude is not None:
+            if tuple(magnitude.shape) != (self.d_out,):
+                raise ValueError("magnitude [d_out] expected")
+            m = magnitude.to(device=dev, dtype=torch.float32).contiguous()
+        with torch.cuda.stream(st):
+            _check(lib().lora_pool_dora_prepare(self.c, int(slot), _ptr(W), _ld(W), _ptr(m),
+                                                _stream(st)))
+        if m is not None:
+            m.record_stream(st)
+
     def set_policy(self, rank_policy: str):
         self.rank_policy = rank_policy
         self._c = LoraPoolC(self.n_slots, self.r_max, self.d_in, self.d_out, _dtype_code(self.dtype),
                             RANK_POLICIES[rank_policy], self.A.data_ptr(), self.Bt.data_ptr(),
                             self.slot_rank.data_ptr(), self.slot_scale.data_ptr(),
-                            self.B.data_ptr() if self.B is not None else None)
+                            self.B.data_ptr() if self.B is not None else None,
+                            self.dora_scale.data_ptr() if self.dora_scale is not None else None)
         return self
 
     @property

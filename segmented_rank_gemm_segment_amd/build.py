@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora.so")
 
-SOURCES = ["build_segments.hip", "shrink_expand.hip", "gemm.hip", "pack_slot.hip",
+SOURCES = ["build_segments.hip", "shrink_expand.hip", "gemm.hip", "pack_slot.hip", "dora.hip",
            "lora_api.cpp"]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 

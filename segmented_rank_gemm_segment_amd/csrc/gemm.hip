@@ -46,6 +46,7 @@ struct GemmArgs {
   const int32_t *row_segment, *seg_slot, *seg_rank;
   const float *seg_scale;
   int r_max, policy;
+  const float *dora;   // optional DoRA column factors ([slot][N]) or null
 };
 
 // Tile configurations <BM, BN, waves along M, waves along N, K per group
@@ -102,8 +103,9 @@ struct TileCfg {
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz).
 // LORA: 0 = plain product; 1 = fused LoRA with B gathered from Bt; 2 = fused
-// LoRA with B read from its d_out-major copy.
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA>
+// LoRA with B read from its d_out-major copy.  DORA: rows of rank > 0 are
+// multiplied by their slot's column factors before the rounding.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, bool DORA>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG>;
   __shared__ __align__(16) unsigned char smem[C::LDS];
@@ -345,12 +347,14 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // add exact zeros, so base-only rows stay bit-identical to the plain
     // product.
     constexpr int RBL = 128;                          // bytes per staged row
-    static_assert(3 * (BM > BN ? BM : BN) * RBL + 16 <= C::LDS, "LoRA staging");
+    static_assert(3 * (BM > BN ? BM : BN) * RBL + 16 + 4 * BM <= C::LDS, "LoRA staging");
     static_assert(C::T >= BM, "one tile row per thread");
     unsigned char *s_ahi = smem;
     unsigned char *s_alo = smem + BM * RBL;
     unsigned char *s_b = smem + 2 * BM * RBL;
     int *s_next = reinterpret_cast<int *>(smem + 2 * BM * RBL + BN * RBL);
+    // DoRA: slot of each tile row (-1 = not rescaled), read by the store
+    int *s_rowslot = reinterpret_cast<int *>(smem + 2 * BM * RBL + BN * RBL + 16);
     auto sw = [](int c, int r) { return ((c ^ ((r >> 1) & 7)) * 16); };
     // this thread's tile row (threads past BM take no row)
     int my_seg = -1;
@@ -360,6 +364,9 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
     // previous readers of LDS (the K loop, the partial sums) are done
     lgkm_barrier();
+    if constexpr (DORA) {
+      if (tid < BM) s_rowslot[tid] = my_seg >= 0 ? g.seg_slot[my_seg] : -1;
+    }
     int prev = -1;
     while (true) {
       // next segment id above prev among the tile's rows: wave minimum,
@@ -478,18 +485,38 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   if (KG > 1 && kgrp > 0) return;
 
-  // store: bf16 round to nearest even, once
+  // store: bf16 round to nearest even, once.  DoRA: rows of rank > 0 are
+  // first multiplied by g[slot][col]; the tile's row -> slot table (-1 = not
+  // rescaled) was written before the segment loop, whose barriers order it
+  // before these reads.  Rows without a factor read slot 0's in bounds and
+  // multiply by 1.  One fragment row block at a time, so the factors of
+  // only one block are live.
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
+    int rs[16];
+    if constexpr (DORA) {
+      const int *s_rowslot = reinterpret_cast<const int *>(smem + 2 * BM * 128 + BN * 128 + 16);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) rs[v] = s_rowslot[wm * C::TM + i * 32 + acc_row(v, l)];
+    }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int col = n0 + wn * C::TN + j * 32 + (l & 31);
+      if constexpr (DORA) {
+        const int colc = min(col, N - 1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float f = g.dora[(int64_t)max(rs[v], 0) * N + colc];
+          acc[i][j][v] *= rs[v] >= 0 ? f : 1.f;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * C::TM + i * 32 + acc_row(v, l);
         if (row < M && col < N) g.Y[(int64_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_rne(acc[i][j][v]);
       }
     }
+    if constexpr (DORA) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -510,6 +537,7 @@ struct GemmF32Args {
   const int32_t *row_segment, *seg_slot, *seg_rank;
   const float *seg_scale;
   int r_max;
+  const float *dora;
 };
 
 template <bool LORA>
@@ -565,6 +593,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
           float d = 0.f;
           for (int k = 0; k < r; ++k) d = fmaf(hrow[k], bt[(int64_t)k * g.N + col], d);
           acc[i][j] += sc * d;
+          if (g.dora) acc[i][j] *= g.dora[(int64_t)g.seg_slot[s] * g.N + col];
         }
       }
     }
@@ -581,15 +610,22 @@ hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
   const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(((ntiles + 7) / 8) * 8);
   dim3 block(WM * WN * KG * kWave);
-  if (lora && g.Bn)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2>), grid, block, 0,
-                       stream, g);
+  const bool dora = lora && g.dora;
+  if (lora && g.Bn && dora)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, true>), grid, block,
+                       0, stream, g);
+  else if (lora && g.Bn)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, false>), grid, block,
+                       0, stream, g);
+  else if (lora && dora)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true>), grid, block,
+                       0, stream, g);
   else if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1>), grid, block, 0,
-                       stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false>), grid, block,
+                       0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 0>), grid, block, 0,
-                       stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 0, false>), grid, block,
+                       0, stream, g);
   return hipGetLastError();
 }
 
@@ -601,10 +637,11 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
   const bool lora = seg != nullptr;
   if (dtype == 1) {
     GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
-               H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+               H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr};
     if (lora) {
       g.Bt = (const bf16_t *)pool->Bt;
       g.Bn = (const bf16_t *)pool->B;
+      g.dora = pool->dora;
       g.row_segment = seg->row_segment;
       g.seg_slot = seg->seg_slot;
       g.seg_rank = seg->seg_rank;
@@ -616,9 +653,10 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
     return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
   }
   GemmF32Args g{(const float *)X, ldx, (const float *)W, ldw, (float *)Y, ldy, M, K, N,
-                H, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+                H, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
   if (lora) {
     g.Bt = (const float *)pool->Bt;
+    g.dora = pool->dora;
     g.row_segment = seg->row_segment;
     g.seg_slot = seg->seg_slot;
     g.seg_rank = seg->seg_rank;

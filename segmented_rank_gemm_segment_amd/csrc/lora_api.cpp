@@ -28,6 +28,7 @@ lora_status check_pool(const lora_pool *pool) {
   if (!pool->A || !pool->Bt || !pool->slot_rank || !pool->slot_scale) return LORA_ERR_NULL;
   if (!aligned16(pool->A) || !aligned16(pool->Bt)) return LORA_ERR_ALIGN;
   if (pool->B && !aligned16(pool->B)) return LORA_ERR_ALIGN;
+  if (pool->dora_scale && !aligned16(pool->dora_scale)) return LORA_ERR_ALIGN;
   return LORA_OK;
 }
 
@@ -63,7 +64,7 @@ lora::SegView seg_view(const lora_segments *s) {
 
 lora::PoolView pool_view(const lora_pool *p) {
   return lora::PoolView{p->n_slots, p->r_max, p->d_in, p->d_out, p->dtype, p->rank_policy,
-                        p->A,       p->Bt,      p->B};
+                        p->A,       p->Bt,      p->B,      p->dora_scale};
 }
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
@@ -154,6 +155,20 @@ lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t ran
   return hip_status(lora::launch_pack_slot(
       pool_view(pool), const_cast<int32_t *>(pool->slot_rank), const_cast<float *>(pool->slot_scale),
       slot, rank, scale, A_src, lda, B_src, ldb, static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_pool_dora_prepare(const lora_pool *pool, int32_t slot, const void *W,
+                                   int64_t ldw, const float *magnitude, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (!pool->dora_scale) return LORA_ERR_NULL;
+  if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SHAPE;
+  st = check_matrix(W, ldw, pool->d_in, pool->d_out);
+  if (st != LORA_OK) return st;
+  if (magnitude && (reinterpret_cast<uintptr_t>(magnitude) & 3u)) return LORA_ERR_ALIGN;
+  return hip_status(lora::launch_dora_prepare(pool_view(pool), pool->slot_rank, pool->slot_scale,
+                                              slot, W, ldw, magnitude,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,

@@ -23,6 +23,7 @@ struct PoolView {
   const void *A;
   const void *Bt;
   const void *B;   // optional d_out-major copy of B ([n_slots][d_out][r_max]) or null
+  const float *dora;   // optional DoRA column factors ([n_slots][d_out]) or null
 };
 
 hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
@@ -41,6 +42,11 @@ hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &poo
 hipError_t launch_pack_slot(const PoolView &pool, int32_t *slot_rank, float *slot_scale, int slot,
                             int rank, float scale, const void *A_src, int64_t lda,
                             const void *B_src, int64_t ldb, hipStream_t stream);
+
+// DoRA column factors of one slot from its current contents and W.
+hipError_t launch_dora_prepare(const PoolView &pool, const int32_t *slot_rank,
+                               const float *slot_scale, int slot, const void *W, int64_t ldw,
+                               const float *magnitude, hipStream_t stream);
 
 // Y = X W^T (+ fused LoRA when seg/pool/H are given).
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,

@@ -9,8 +9,9 @@
 // weights are complete.
 //
 // Here the weights are written first, by one kernel: A rows [0, rank) and
-// zeros up to r_max, Bt = B^T rows likewise, and the d_out-major copy of B
-// when the pool has one.  A second, one-thread kernel on the same stream then
+// zeros up to r_max, Bt = B^T rows likewise, the d_out-major copy of B when
+// the pool has one, and ones in the slot's DoRA column factors when the pool
+// has them (a fresh adapter is plain LoRA until its factors are prepared).  A second, one-thread kernel on the same stream then
 // writes the slot's rank and scale, so work queued after the call sees
 // either nothing of the new adapter (before) or all of it.  Every argument is
 // checked on the host before either kernel is queued.
@@ -23,12 +24,13 @@ namespace {
 constexpr int kThreads = 256;
 
 // Output vectors of V elements: region A [r_max][d_in], then Bt
-// [r_max][d_out], then B [d_out][r_max] (when present).
+// [r_max][d_out], then B [d_out][r_max] (when present), then the DoRA
+// factors [d_out] in float4 vectors (when present).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
-    T *__restrict__ A, T *__restrict__ Bt, T *__restrict__ Bn, int r_max, int d_in, int d_out,
-    int rank, const T *__restrict__ A_src, int64_t lda, const T *__restrict__ B_src,
-    int64_t ldb, int64_t nA, int64_t nBt, int64_t nB) {
+    T *__restrict__ A, T *__restrict__ Bt, T *__restrict__ Bn, float *__restrict__ D, int r_max,
+    int d_in, int d_out, int rank, const T *__restrict__ A_src, int64_t lda,
+    const T *__restrict__ B_src, int64_t ldb, int64_t nA, int64_t nBt, int64_t nB, int64_t nD) {
   constexpr int V = Elem<T>::kVec;
   const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (v < nA) {
@@ -62,6 +64,11 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
     uint4 out;
     __builtin_memcpy(&out, vals, sizeof(out));
     stg16(Bn + (int64_t)j * r_max + k0, out);
+    return;
+  }
+  if (v < nA + nBt + nB + nD) {
+    const int64_t w = v - nA - nBt - nB;
+    *reinterpret_cast<float4 *>(D + w * 4) = make_float4(1.f, 1.f, 1.f, 1.f);
   }
 }
 
@@ -83,12 +90,14 @@ hipError_t launch_pack_t(const PoolView &pool, int32_t *slot_rank, float *slot_s
   T *A = (T *)pool.A + (int64_t)slot * r_max * d_in;
   T *Bt = (T *)pool.Bt + (int64_t)slot * r_max * d_out;
   T *Bn = pool.B ? (T *)pool.B + (int64_t)slot * d_out * r_max : nullptr;
+  float *D = pool.dora ? const_cast<float *>(pool.dora) + (int64_t)slot * d_out : nullptr;
   const int64_t nA = r_max * d_in / V, nBt = r_max * d_out / V, nB = Bn ? d_out * r_max / V : 0;
-  const int64_t total = nA + nBt + nB;
+  const int64_t nD = D ? d_out / 4 : 0;
+  const int64_t total = nA + nBt + nB + nD;
   const int blocks = (int)((total + kThreads - 1) / kThreads);
   hipLaunchKernelGGL((pack_weights_kernel<T>), dim3(blocks), dim3(kThreads), 0, stream, A, Bt,
-                     Bn, pool.r_max, pool.d_in, pool.d_out, rank, (const T *)A_src, lda,
-                     (const T *)B_src, ldb, nA, nBt, nB);
+                     Bn, D, pool.r_max, pool.d_in, pool.d_out, rank, (const T *)A_src, lda,
+                     (const T *)B_src, ldb, nA, nBt, nB, nD);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(publish_slot_kernel, dim3(1), dim3(64), 0, stream, slot_rank, slot_scale,

@@ -6,7 +6,9 @@
 // for every row i of a segment with slot a and rank r_a > 0 (adapter-batching
 // page, Multi-LoRA Serving, section "Segmented Kernel 需要哪些 Metadata":
 // H_a = X_a A_a^T and Delta Y_a = s_a H_a B_a^T scattered back to the
-// original rows).
+// original rows).  With DoRA column factors in the pool (ybb.press
+// multi-LoRA serving article, section 9.2), the expand multiplies each sum
+// by g_a[j] before the rounding: Y[i][j] = g_a[j] (Y[i][j] + s_a ...).
 //
 // Both are bandwidth-bound segmented GEMV / skinny products.  Work items are
 // (segment, block of up to kRowBlk rows of that segment); a fixed grid walks
@@ -252,9 +254,10 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
 constexpr int kExpWaves = 4;
 constexpr int kExpSub = 4;    // rows per pass (one Y row per rank quarter)
 
-template <typename T, int R>
-__device__ __forceinline__ void expand_item(const float *__restrict__ H, const T *bt, int d_out,
-                                            bool active, int r, float sc, int p0, int p1,
+template <typename T, int R, bool DORA>
+__device__ __forceinline__ void expand_item(const float *__restrict__ H, const T *bt,
+                                            const float *gp, int d_out, bool active, int r,
+                                            float sc, int p0, int p1,
                                             const int32_t *token_indices, int r_max, T *Y,
                                             int64_t ldy, int col, int lane) {
   constexpr int V = Elem<T>::kVec;
@@ -278,6 +281,15 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
       // masked where they are used (rank rows >= r) and inactive columns
       // are never stored.
       braw[jb][e] = ldg16(bt + (int64_t)min(k0 + e, r_max - 1) * d_out);
+    }
+  }
+  // DoRA column factors of the lane's V columns (same for every row)
+  float gv[V];
+  if constexpr (DORA) {
+#pragma unroll
+    for (int e4 = 0; e4 < V; e4 += 4) {
+      const float4 t = *reinterpret_cast<const float4 *>(gp + e4);
+      gv[e4] = t.x; gv[e4 + 1] = t.y; gv[e4 + 2] = t.z; gv[e4 + 3] = t.w;
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -368,6 +380,7 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
 #pragma unroll
       for (int q = 0; q < kExpSub; ++q) a = (q == myq) ? acc[q][e] : a;
       out[e] = fmaf(sc, a, yv[e]);
+      if constexpr (DORA) out[e] *= gv[e];
     }
     const uint4 packed = Elem<T>::pack(out);
     if (active && myq < nq) stg16(Y + (int64_t)yrow * ldy + col, packed);
@@ -380,12 +393,12 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
 
 // RMAX = the pool's r_max: only rank buckets up to it are compiled in, so a
 // rank-16 pool does not pay the registers of the rank-64 case.
-template <typename T, int RMAX>
+template <typename T, int RMAX, bool DORA>
 __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
-    const float *__restrict__ H, const T *__restrict__ Bt, const int32_t *token_indices,
-    const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
-    const float *seg_scale, const int32_t *num_segments, int r_max, int d_out, int policy,
-    int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy) {
+    const float *__restrict__ H, const T *__restrict__ Bt, const float *__restrict__ dora,
+    const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
+    const int32_t *seg_rank, const float *seg_scale, const int32_t *num_segments, int r_max,
+    int d_out, int policy, int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -406,17 +419,19 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
     const T *bt = Bt + (int64_t)slot * r_max * d_out + (active ? col : 0);
+    const float *gp = DORA ? dora + (int64_t)slot * d_out + (active ? col : 0) : nullptr;
     if (R == 8) {
-      expand_item<T, 8>(H, bt, d_out, active, r, sc, p0, p1, token_indices, r_max, Y, ldy, col, lane);
+      expand_item<T, 8, DORA>(H, bt, gp, d_out, active, r, sc, p0, p1, token_indices, r_max, Y,
+                              ldy, col, lane);
     } else if (RMAX >= 16 && R == 16) {
-      expand_item<T, (RMAX >= 16 ? 16 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
-                                            r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 16 ? 16 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, Y, ldy, col, lane);
     } else if (RMAX >= 32 && R == 32) {
-      expand_item<T, (RMAX >= 32 ? 32 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
-                                            r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 32 ? 32 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, Y, ldy, col, lane);
     } else if (RMAX >= 64) {
-      expand_item<T, (RMAX >= 64 ? 64 : 8)>(H, bt, d_out, active, r, sc, p0, p1, token_indices,
-                                            r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 64 ? 64 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, Y, ldy, col, lane);
     }
   }
 }
@@ -491,10 +506,16 @@ void launch_expand_t(const float *H, const SegView &seg, const PoolView &pool, v
   (void)real_bound;
   const int gx = (pool.d_out + cols_per_block - 1) / cols_per_block;
   dim3 grid(gx, grid_items(S_bound * bps, gx));
-  hipLaunchKernelGGL((expand_kernel<T, RMAX>), grid, dim3(kExpWaves * kWave), 0, stream, H,
-                     (const T *)pool.Bt, seg.token_indices, seg.seg_off, seg.seg_slot,
-                     seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max, pool.d_out,
-                     pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
+  if (pool.dora)
+    hipLaunchKernelGGL((expand_kernel<T, RMAX, true>), grid, dim3(kExpWaves * kWave), 0, stream,
+                       H, (const T *)pool.Bt, pool.dora, seg.token_indices, seg.seg_off,
+                       seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
+                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
+  else
+    hipLaunchKernelGGL((expand_kernel<T, RMAX, false>), grid, dim3(kExpWaves * kWave), 0, stream,
+                       H, (const T *)pool.Bt, nullptr, seg.token_indices, seg.seg_off,
+                       seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
+                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
 }
 
 template <typename T>

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
-              "lora_base_gemm", "lora_pool_pack_slot", "lora_status_str", "lora_abi_version"):
+              "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_status_str",
+              "lora_abi_version"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 2
+    assert L.lora_abi_version() == srg.ABI_VERSION == 3
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
@@ -91,6 +92,7 @@ def shrink(L, p, s, X=P + 0xC000, ldx=64, H=P + 0xD000):
     (dict(A=0), ENULL),
     (dict(slot_scale=0), ENULL),
     (dict(Bt=P + 8), EALIGN),
+    (dict(dora_scale=P + 4), EALIGN),
 ])
 def test_pool_validation(L, kw, code):
     assert shrink(L, pool(**kw), segs()) == code
@@ -152,6 +154,24 @@ def test_pack_slot_validation(L):
     assert pack(p, 0, 8, 2.0, A + 4, 64, B, 8, None) == EALIGN   # A not 16-byte aligned
     assert pack(p, 0, 8, 2.0, A, 64, B, 7, None) == ESHAPE       # ldb < rank
     assert pack(ctypes.byref(pool(A=0)), 0, 8, 2.0, A, 64, B, 8, None) == ENULL
+
+
+def test_dora_prepare_validation(L):
+    """Every bad argument is rejected on the host (nothing is launched)."""
+    W = P + 0xC000
+    p = ctypes.byref(pool(dora_scale=P + 0xE000))      # 4 slots, d_in 64, d_out 32
+    prep = L.lora_pool_dora_prepare
+    assert prep(None, 0, W, 64, P, None) == ENULL
+    assert prep(ctypes.byref(pool()), 0, W, 64, P, None) == ENULL      # pool without factors
+    assert prep(p, -1, W, 64, P, None) == ESHAPE
+    assert prep(p, 4, W, 64, P, None) == ESHAPE
+    assert prep(p, 0, None, 64, P, None) == ENULL
+    assert prep(p, 0, W, 56, P, None) == ESHAPE                        # ldw < d_in
+    assert prep(p, 0, W, 68, P, None) == EALIGN                        # ldw % 8
+    assert prep(p, 0, W + 8, 64, P, None) == EALIGN
+    assert prep(p, 0, W, 64, P + 2, None) == EALIGN                    # magnitude
+    assert prep(ctypes.byref(pool(dora_scale=P + 4)), 0, W, 64, P, None) == EALIGN
+    assert prep(ctypes.byref(pool(r_max=12, dora_scale=P)), 0, W, 64, P, None) == ERANK
 
 
 def test_expand_and_fused_validation(L):
