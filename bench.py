@@ -15,6 +15,8 @@ Prints one JSON line (rank 0; one GPU):
                its mean HIP-event duration, against the MI355X peak
   kernels    = the same figures for every kernel of the step
   prefill    = the prefill workload's step (tokens/s, TFLOP/s, MFMA fraction)
+  dora       = the same step with every slot a DoRA adapter (column factors
+               in the epilogue), and the per-adapter factor preparation
   cpu_baseline = the float64 CPU oracle on a bounded sample of the headline
                workload, on this host's cores
 
@@ -56,6 +58,8 @@ def parse():
                    help="total size of the rotated copies of the layer tensors")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dora", action="store_true",
+                   help="skip the DoRA variant (column factors in the epilogue)")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the base product through torch.matmul for comparison")
     p.add_argument("--eager", action="store_true",
@@ -103,15 +107,30 @@ def work_figures(w):
 # ---------------------------------------------------------------------------
 # device state
 # ---------------------------------------------------------------------------
+DORA_SEED = 9
+
+
+def dora_magnitudes(w, device):
+    """Seeded DoRA magnitudes for every slot (float32 [d_out] on device)."""
+    import torch
+    import workloads as wl
+    mag = wl.make_magnitude(DORA_SEED, w.n_slots, w.d_out, 0.02 * np.sqrt(w.d_in), p_plain=0.0)
+    return [torch.from_numpy(m).to(device) for m in mag]
+
+
 class Layer:
-    def __init__(self, w, policy, device):
+    def __init__(self, w, policy, device, dora=False):
         import torch
         import segmented_rank_gemm_segment_amd as srg
         import workloads as wl
         d = wl.device_tensors(w, device)
         self.X, self.W, self.row_slot = d["X"], d["W"], d["row_slot"]
         self.alpha = w.slot_alpha
-        self.pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha, policy)
+        self.pool = srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha, policy, dora=dora)
+        self.mag = dora_magnitudes(w, device) if dora else None
+        if dora:
+            for a, m in enumerate(self.mag):
+                self.pool.dora_prepare(a, self.W, m)
         self.seg = srg.Segments(w.n, w.n_slots, device)
         dt = self.X.dtype
         self.H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=device)
@@ -128,7 +147,9 @@ class Layer:
         p = self.pool
         c.row_slot = self.row_slot.clone()
         c.pool = srg.Pool(p.A.clone(), p.Bt.clone(), p.slot_rank.clone(), self.alpha,
-                          p.rank_policy)
+                          p.rank_policy, dora=p.dora_scale is not None)
+        if p.dora_scale is not None:
+            c.pool.dora_scale.copy_(p.dora_scale)
         c.seg = srg.Segments(self.seg.n_rows, p.n_slots, device)
         c.H, c.Y = torch.zeros_like(self.H), torch.empty_like(self.Y)
         return c
@@ -245,9 +266,9 @@ def time_calls(fn_seq, layers, iters, warmup, use_graph):
 
 
 def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
-            device="cuda:0", vendor=False):
+            device="cuda:0", vendor=False, dora=False):
     import torch
-    L0 = Layer(w, policy, device)
+    L0 = Layer(w, policy, device, dora=dora)
     copies = max(1, int(np.ceil(rotate_mb * 1e6 / L0.nbytes)))
     layers = [L0] + [L0.clone(device) for _ in range(copies - 1)]
     for L in layers:                      # metadata/H valid for per-kernel loops
@@ -263,6 +284,15 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
     for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
     res = {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
+    if dora:
+        # DoRA column factors, one slot per call (a one-off per adapter load)
+        turn = [0]
+
+        def k_prepare(L):
+            a = turn[0] % w.n_slots
+            turn[0] += 1
+            L.pool.dora_prepare(a, L.W, L.mag[a])
+        res["prepare_s"], _ = time_calls((k_prepare,), layers, kl, max(3, warmup // 4), use_graph)
     if vendor:
         k_vendor_base(layers[0])          # library set-up outside any capture
         torch.cuda.synchronize()
@@ -392,6 +422,29 @@ def cpu_baseline(w, budget_s=12.0, single_core_s=6.0):
     return out
 
 
+def dora_entry(w, fig, m, paths, args):
+    """The headline workload with every slot a DoRA adapter: step and kernel
+    times against the plain pool's, and the column-factor preparation."""
+    md = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
+                 args.kernel_loops, not args.eager, dora=True)
+    e = 2 if w.dtype == "bf16" else 4
+    r_mean = float(np.mean(w.slot_rank))
+    prep_bytes = (w.d_out * w.d_in * e + r_mean * (w.d_in + w.d_out) * e + 2 * w.d_out * 4)
+    t = md["prepare_s"]
+    return {
+        "what": "same workload, every slot with DoRA column factors g = m / ||W0 + sBA||_c "
+                "applied before the rounding",
+        "step_us_by_path": {p: round(md["step"][p][0] * 1e6, 3) for p in paths},
+        "step_vs_plain": {p: round(md["step"][p][0] / m["step"][p][0], 4) for p in paths},
+        "kernels_us": {k: round(md["per_kernel_s"][k] * 1e6, 3) for k in ("fused", "expand")},
+        "kernels_vs_plain": {k: round(md["per_kernel_s"][k] / m["per_kernel_s"][k], 4)
+                             for k in ("fused", "expand")},
+        "prepare": {"us_per_adapter": round(t * 1e6, 3), "alg_bytes": int(prep_bytes),
+                    "GB_s": round(prep_bytes / t / 1e9, 1),
+                    "hbm_frac": round(prep_bytes / t / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -480,6 +533,19 @@ def main():
         if vendor_entry(f3, m3):
             out["prefill"]["vendor_base_gemm"] = vendor_entry(f3, m3)
         del w3
+    if not args.no_dora:
+        out["dora"] = dora_entry(w, fig, m, paths, args)
+        if "prefill" in out:
+            w3 = wl.make_config(3)
+            st3 = max(5, args.steps // 10)
+            md3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
+                          not args.eager, dora=True)
+            plain = out["prefill"]["kernels"]["fused"]["us"] * 1e-6
+            out["prefill"]["dora"] = {
+                "fused_us": round(md3["per_kernel_s"]["fused"] * 1e6, 3),
+                "fused_vs_plain": round(md3["per_kernel_s"]["fused"] / plain, 4),
+                "step_us": round(md3["step"]["fused"][0] * 1e6, 3)}
+            del w3
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -253,8 +253,8 @@ class Pool:
         with torch.cuda.stream(st):
             _check(lib().lora_pool_dora_prepare(self.c, int(slot), _ptr(W), _ld(W), _ptr(m),
                                                 _stream(st)))
-        if m is not None:
-            m.record_stream(st)
+        if m is not None and m is not magnitude:
+            m.record_stream(st)           # a copy made here: alive until read
 
     def set_policy(self, rank_policy: str):
         self.rank_policy = rank_policy
