@@ -135,6 +135,20 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   const int m0 = (first_m + tin % gcnt) * BM;
   const int n0 = (tin / gcnt) * BN;
 
+  // Small tiles (two K groups) finish row by row: thread tid owns tile row
+  // tid / (BN / 8) and 8 consecutive columns (see the end of the kernel).
+  // With the LoRA term, the row's segment id is loaded before the first
+  // DMA and its segment's rank, slot and scale right after the first stage
+  // has landed, so all three have long arrived by the epilogue.  The loads
+  // are issued by hand (the compiler would sink them to their uses) and
+  // waited for explicitly.
+  constexpr bool ROWEPI = KG > 1;
+  static_assert(!ROWEPI || C::T * 8 == BM * BN, "row epilogue: 8 outputs per thread");
+  const int e_row = tid / (BN / 8), e_c8 = (tid % (BN / 8)) * 8;
+  int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
+  if constexpr (ROWEPI && LORA != 0)
+    e_seg = gload_b32(g.row_segment + min(m0 + e_row, M - 1));
+
   // DMA sources: lane l of an instruction fills tile row base + l / CH at
   // physical chunk l % CH, i.e. logical chunk swz(l % CH, row) (a function
   // of the row, so of the instruction too).  Rows past M / N are clamped to
@@ -258,6 +272,13 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   // stage 0 landed (the later stages may stay in flight)
   wait_ahead<C::IPW>(min(STAGES - 1, KT - 1));
+  if constexpr (ROWEPI && LORA != 0) {
+    // the segment id was loaded before stage 0, so it has landed too
+    asm volatile("" : "+v"(e_seg));
+    e_r = gload_b32(g.seg_rank + e_seg);
+    e_slot = gload_b32(g.seg_slot + e_seg);
+    e_scb = gload_b32(g.seg_scale + e_seg);
+  }
   if (ktail && KT == 1) zero_tail(0, kg0);
   lgkm_barrier();
   load_frags(0, smem, 0);
@@ -294,6 +315,82 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       }
     }
     load_frags(KK & 1, smem + ((kt + 1) % STAGES) * C::STAGE, 0);
+  }
+
+  if constexpr (ROWEPI) {
+    // Row epilogue.  The K groups' partial tiles go to LDS row-major (every
+    // read of the ring and every DMA into it has finished: the last stage
+    // was waited for in full and the barrier drains the reads); each thread
+    // adds its row's 8 columns over the groups in group order.  A LoRA row
+    // of rank r > 0 then gets s_a sum_k H[row][k] Bt_a[k][cols] in fp32
+    // (k ascending, read in chunks of 8 rank rows; rows at or past r are
+    // read inside the slot and skipped), the DoRA factor when the pool has
+    // one, and one rounding; the 8 results leave in one 16-byte store.
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
+    lgkm_barrier();
+    float *red = reinterpret_cast<float *>(smem);
+    constexpr int RS = BN + 4;
+    static_assert(KG * BM * RS * 4 <= C::LDS, "row epilogue staging");
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          red[(kgrp * BM + wm * C::TM + i * 32 + acc_row(v, l)) * RS + wn * C::TN + j * 32 + (l & 31)] =
+              acc[i][j][v];
+    lgkm_barrier();
+    float o[8];
+    {
+      const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + e_row * RS + e_c8);
+      const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + e_row * RS + e_c8 + 4);
+      o[0] = p0[0]; o[1] = p0[1]; o[2] = p0[2]; o[3] = p0[3];
+      o[4] = p1[0]; o[5] = p1[1]; o[6] = p1[2]; o[7] = p1[3];
+    }
+#pragma unroll
+    for (int gi = 1; gi < KG; ++gi) {
+      const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + (gi * BM + e_row) * RS + e_c8);
+      const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + (gi * BM + e_row) * RS + e_c8 + 4);
+      o[0] += p0[0]; o[1] += p0[1]; o[2] += p0[2]; o[3] += p0[3];
+      o[4] += p1[0]; o[5] += p1[1]; o[6] += p1[2]; o[7] += p1[3];
+    }
+    const int grow = m0 + e_row, gcol = n0 + e_c8;
+    const bool live = grow < M && gcol < N;       // N % 8 == 0: all 8 columns or none
+    if constexpr (LORA != 0) {
+      if (live && e_r > 0) {
+        const bf16_t *bt = g.Bt + (int64_t)e_slot * g.r_max * N + gcol;
+        const float *hp = g.H + (int64_t)grow * g.r_max;
+        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int kc = 0; kc < e_r; kc += 8) {      // kc + 8 <= r_max: in the slot
+          const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
+          const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
+          const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          u32x4 b[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) b[q] = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(kc + q) * N);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const bool use = kc + q < e_r;
+            float bv[8];
+            Elem<bf16_t>::unpack(make_uint4(b[q][0], b[q][1], b[q][2], b[q][3]), bv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] = use ? fmaf(h[q], bv[e], d[e]) : d[e];
+          }
+        }
+        const float sc = __int_as_float(e_scb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(sc, d[e], o[e]);
+        if constexpr (DORA) {
+          const float *gp = g.dora + (int64_t)e_slot * N + gcol;
+          const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
+          const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+          o[0] *= g0[0]; o[1] *= g0[1]; o[2] *= g0[2]; o[3] *= g0[3];
+          o[4] *= g1[0]; o[5] *= g1[1]; o[6] *= g1[2]; o[7] *= g1[3];
+        }
+      }
+    }
+    if (live) stg16(g.Y + (int64_t)grow * g.ldy + gcol, Elem<bf16_t>::pack(o));
+    return;
   }
 
   if constexpr (KG > 1) {
@@ -333,7 +430,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           }
   }
 
-  if constexpr (LORA != 0) {
+  if constexpr (LORA != 0 && !ROWEPI) {
     // LoRA increment, after the K loop, one distinct LoRA segment u of the
     // tile's rows at a time (ascending id).  The whole workgroup stages the
     // operands of the small product s_u H_u B_u^T in LDS, in the layout of
