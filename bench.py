@@ -2,9 +2,9 @@
 """Benchmark of the segmented multi-LoRA linear layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch: segment-metadata
-build, shrink (H = X_a A_a^T), and the base GEMM with the LoRA expand fused
-into its epilogue (``--path separate``: base GEMM, then expand +
-scatter-add).  Inputs are resident in HBM before timing starts.  Each step
+build and shrink (H = X_a A_a^T; one launch for decode-sized batches,
+lora_build_shrink), and the base GEMM with the LoRA expand fused into its
+epilogue (``--path separate``: base GEMM, then expand + scatter-add).  Inputs are resident in HBM before timing starts.  Each step
 uses the next of several copies of the layer's tensors (like consecutive
 layers of a model), so that the 256 MB last-level cache cannot serve weights
 read in the previous step.
@@ -89,6 +89,8 @@ def work_figures(w):
         "distinct_adapters": len(distinct),
         "bytes": {
             "build": n * 4 + 2 * n * 4 + 2 * w.n_slots * 4,
+            "build_shrink": (n * 4 + 2 * n * 4 + 2 * w.n_slots * 4) + sum_r_distinct * di * e
+                            + n_lora * di * e + sum_r_rows * 4,
             "shrink": sum_r_distinct * di * e + n_lora * di * e + sum_r_rows * 4,
             "expand": sum_r_distinct * do * e + sum_r_rows * 4 + 2 * n_lora * do * e,
             "base": do * di * e + n * di * e + n * do * e,
@@ -96,6 +98,7 @@ def work_figures(w):
         },
         "flops": {
             "shrink": 2 * sum_r_rows * di,
+            "build_shrink": 2 * sum_r_rows * di,
             "expand": 2 * sum_r_rows * do,
             "base": 2 * n * di * do,
             "fused": 2 * n * di * do + 2 * sum_r_rows * do,
@@ -165,6 +168,11 @@ def k_shrink(L):
     srg.lora_shrink(L.X, L.seg, L.pool, L.H)
 
 
+def k_build_shrink(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_build_shrink(L.row_slot, L.X, L.pool, L.seg, L.H)
+
+
 def k_fused(L):
     import segmented_rank_gemm_segment_amd as srg
     srg.lora_linear_fused(L.X, L.W, L.H, L.seg, L.pool, L.Y)
@@ -212,9 +220,10 @@ class _Overlap:
         k_expand(L)
 
 
-STEP = {"fused": (k_build, k_shrink, k_fused), "separate": (k_build, k_shrink, k_base, k_expand)}
+STEP = {"fused": (k_build_shrink, k_fused), "separate": (k_build_shrink, k_base, k_expand)}
 PATHS = ("fused", "separate", "overlap")
-KNAME = {k_build: "build", k_shrink: "shrink", k_fused: "fused", k_base: "base", k_expand: "expand"}
+KNAME = {k_build: "build", k_shrink: "shrink", k_build_shrink: "build_shrink", k_fused: "fused",
+         k_base: "base", k_expand: "expand"}
 
 
 def _graph(fn_seq, layers, count, start=0):
@@ -281,7 +290,8 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
         step[p] = time_calls(seq, layers, steps, warmup, use_graph)
     kl = kernel_loops or steps
     per_kernel = {}
-    for fn in sorted(set(STEP["fused"] + STEP["separate"]), key=lambda f: KNAME[f]):
+    for fn in sorted(set(STEP["fused"] + STEP["separate"] + (k_build, k_shrink)),
+                     key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
     res = {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
     if dora:
@@ -478,7 +488,7 @@ def main():
     path = min(paths, key=lambda p: m["step"][p][0])
     step_s, wall = m["step"][path]
     kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
-    cand = ("build", "shrink", "fused") if path == "fused" else ("build", "shrink", "base", "expand")
+    cand = ("build_shrink", "fused") if path == "fused" else ("build_shrink", "base", "expand")
     # (overlap: same kernels as separate, base GEMM concurrent with build + shrink)
     main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)

@@ -172,6 +172,19 @@ lora_status lora_shrink(const void *X, int64_t ldx, const lora_segments *seg,
                         const lora_pool *pool, float *H, void *stream);
 
 /*
+ * Segment build and shrink in one call (the two sections above): the same
+ * outputs as lora_build_segments(row_slot, pool, seg) followed by
+ * lora_shrink(X, ldx, seg, pool, H), bit for bit, with the same arguments,
+ * layouts and errors.  For decode-sized batches (up to 512 rows) both run in
+ * one launch: one workgroup builds the metadata while the others compute H
+ * slot by slot from the per-row slot ids, so the shrink does not wait for
+ * the metadata.  Larger batches take the two launches.
+ */
+lora_status lora_build_shrink(const int32_t *row_slot, const void *X, int64_t ldx,
+                              const lora_pool *pool, const lora_segments *seg, float *H,
+                              void *stream);
+
+/*
  * Expand and scatter-add, Y[i] += s_a H[i][0:r] B_a^T for every row i of a
  * segment of rank r > 0 (same section: Delta Y_a = s_a H_a B_a^T, added back
  * to the original rows).  Y [n_rows][d_out] (ld ldy), pool dtype; each Y

@@ -80,6 +80,7 @@ EXPORTS = (
     "lora_status_str",
     "lora_build_segments",
     "lora_shrink",
+    "lora_build_shrink",
     "lora_expand",
     "lora_pool_pack_slot",
     "lora_pool_dora_prepare",
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.lora_build_segments.argtypes = [vp, PP, SP, vp]
     L.lora_shrink.restype = i32
     L.lora_shrink.argtypes = [vp, i64, SP, PP, vp, vp]
+    L.lora_build_shrink.restype = i32
+    L.lora_build_shrink.argtypes = [vp, vp, i64, PP, SP, vp, vp]
     L.lora_expand.restype = i32
     L.lora_expand.argtypes = [vp, SP, PP, vp, i64, vp]
     L.lora_pool_pack_slot.restype = i32
@@ -328,6 +331,22 @@ def lora_shrink(X: torch.Tensor, seg: Segments, pool: Pool, H: torch.Tensor, str
     if X.shape[0] != seg.n_rows or X.dtype != pool.dtype:
         raise ValueError("X: [n_rows, d_in] of the pool dtype")
     _check(lib().lora_shrink(_ptr(X), _ld(X), seg.c, pool.c, _ptr(H), _stream(stream)))
+
+
+def lora_build_shrink(row_slot: torch.Tensor, X: torch.Tensor, pool: Pool, seg: Segments,
+                      H: torch.Tensor, stream=None) -> None:
+    """lora_build_segments followed by lora_shrink, in one launch for
+    decode-sized batches."""
+    if row_slot.dtype != torch.int32 or (row_slot.numel() and not row_slot.is_contiguous()):
+        raise ValueError("row_slot: contiguous int32")
+    if row_slot.numel() != seg.n_rows:
+        raise ValueError("row_slot length != seg.n_rows")
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    if X.shape[0] != seg.n_rows or X.dtype != pool.dtype:
+        raise ValueError("X: [n_rows, d_in] of the pool dtype")
+    _check(lib().lora_build_shrink(_ptr(row_slot), _ptr(X), _ld(X), pool.c, seg.c, _ptr(H),
+                                   _stream(stream)))
 
 
 def lora_expand(H: torch.Tensor, seg: Segments, pool: Pool, Y: torch.Tensor, stream=None) -> None:

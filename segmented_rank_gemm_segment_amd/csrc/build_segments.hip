@@ -7,33 +7,24 @@
 // appearance, rows ascending inside a segment, with segment_offsets,
 // adapter slots, ranks, scales and the token permutation.
 //
-// One workgroup of 1024 threads does the whole job in a single launch with
-// no host synchronisation: per-slot tables live in LDS, rows are visited in
-// chunks of 1024, and rows of one key inside a wavefront are grouped with a
+// One workgroup does the whole job with no host synchronisation: per-slot
+// tables live in LDS (sized by the pool), rows are visited in chunks of one
+// workgroup, and rows of one key inside a wavefront are grouped with a
 // ballot loop (one iteration per distinct key in the wave).  Positions come
 // from counts, never from the order in which atomics land, so the output is
-// deterministic.
+// deterministic.  The same device routine runs as its own launch (up to
+// 1024 threads) or as block 0 of the combined build + shrink launch.
 #include <climits>
 
 #include "lora_device.cuh"
 #include "lora_kernels.h"
+#include "shrink_rows.cuh"
 
 namespace lora {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxKeys = 4096;  // n_slots + 1 (slot keys plus the base-only key)
-
-struct BuildArgs {
-  const int32_t *row_slot;
-  int n, n_slots, r_max;
-  const int32_t *slot_rank;
-  const float *slot_scale;
-  int32_t *token_indices, *row_segment, *seg_off, *seg_slot, *seg_rank;
-  float *seg_scale;
-  int32_t *num_segments, *status;
-};
 
 // Keys of the first kRegChunks chunks of rows stay in registers between the
 // passes; rows past that keep theirs in row_segment (read back by the same
@@ -61,22 +52,33 @@ __device__ __forceinline__ int row_key(int slot, const BuildArgs &a, const Table
   return slot + 1;
 }
 
-__global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
-  __shared__ int s_first[kMaxKeys];  // first row of a key; later -(segment + 1)
-  __shared__ int s_cnt[kMaxKeys];    // rows of a key; later the per-key cursor
-  __shared__ int s_off[kMaxKeys + 1];// segment lengths, then exclusive offsets
-  __shared__ int s_rank[kMaxKeys];   // slot_rank staged
-  __shared__ float s_scale[kMaxKeys];// slot_scale staged
-  __shared__ int s_lead_key[kThreads];
-  __shared__ int s_lead_cnt[kThreads];
-  __shared__ int s_lead_base[kThreads];
-  __shared__ int s_wave[kWaves];
-  __shared__ int s_bad, s_total;
+}  // namespace
 
-  // the block is launched with 64..1024 threads (enough for the batch);
-  // rows are visited in chunks of one block
+// LDS words the routine needs for a pool of n_slots and a block of nthr
+// threads.
+int build_lds_words(int n_slots, int nthr) {
+  const int K = n_slots + 1;
+  return 5 * K + 1 + 3 * nthr + nthr / kWave + 2;
+}
+
+// The whole build by one workgroup (blockDim.x = 64..1024 threads, a
+// multiple of 64) with `lds` pointing at build_lds_words(...) words.
+__device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *lds) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  const int Kw = a.n_slots + 1;
+  int *s_first = lds;                   // first row of a key; later -(segment + 1)
+  int *s_cnt = s_first + Kw;            // rows of a key; later the per-key cursor
+  int *s_off = s_cnt + Kw;              // segment lengths, then exclusive offsets (Kw + 1)
+  int *s_rank = s_off + Kw + 1;         // slot_rank staged
+  float *s_scale = reinterpret_cast<float *>(s_rank + Kw);  // slot_scale staged
+  int *s_lead_key = reinterpret_cast<int *>(s_scale + Kw);
+  int *s_lead_cnt = s_lead_key + nthr;
+  int *s_lead_base = s_lead_cnt + nthr;
+  int *s_wave = s_lead_base + nthr;
+  int &s_bad = s_wave[nthr / kWave];
+  int &s_total = s_wave[nthr / kWave + 1];
+
   const int nwaves = nthr / kWave;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -260,7 +262,106 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   }
 }
 
+namespace {
+
+__global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
+  extern __shared__ int lds[];
+  build_segments_block(a, lds);
+}
+
+// ----------------------------------------------------------------------------
+// Build + shrink in one launch, for decode-sized batches (every segment
+// short).  Block 0 builds the metadata; block 1 + ((rb * n_slots + slot) *
+// nkb + kb) computes H for rank rows [8 kb, 8 kb + 8) of `slot` and the
+// slot's rows [64 rb, 64 rb + 64) in row order.  Those blocks find their
+// rows by scanning the per-row slot ids (wave ballots, counts in LDS), so
+// they never wait for the metadata; each (row, rank row) sum is formed
+// exactly as the metadata-driven shrink forms it, so H has the same bits.
+// A row whose slot has a rank outside [0, r_max] is base-only (the build
+// counts it), and so is its slot here: no block of that slot writes H.
+// ----------------------------------------------------------------------------
+constexpr int kBSMaxRows = 512;            // batches up to this many rows
+constexpr int kBSThreads = kShW * kWave;
+constexpr int kBSChunks = kBSMaxRows / kBSThreads;
+
+template <typename T>
+__global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, const T *X,
+                                                                  int64_t ldx, const T *A,
+                                                                  int d_in, int policy, int nkb,
+                                                                  float *H) {
+  extern __shared__ int lds[];
+  if (blockIdx.x == 0) {
+    build_segments_block(a, lds);
+    return;
+  }
+  const int b = blockIdx.x - 1;
+  const int kb = b % nkb;
+  const int slot = (b / nkb) % a.n_slots;
+  const int rb = b / (nkb * a.n_slots);
+  const int k0 = kb * kShRB;
+  float (*s_part)[kShNP] = reinterpret_cast<float (*)[kShNP]>(lds);
+  int *s_wc = lds + kShW * kShNP;
+  int *s_rows = s_wc + kShW;                // [n]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // every load of the block's set-up at once: the slot's rank and the
+  // row slot ids (n <= kBSMaxRows)
+  const int r = a.slot_rank[slot];
+  int rs[kBSChunks];
+#pragma unroll
+  for (int c = 0; c < kBSChunks; ++c) {
+    const int i = c * kBSThreads + tid;
+    rs[c] = i < a.n ? a.row_slot[i] : -1;
+  }
+  if (r < 1 || r > a.r_max) return;         // rank-0 slot, or rows demoted by the build
+  const int R = rank_bucket(r, policy, a.r_max);
+  if (k0 >= R) return;
+  // rows of the slot in ascending order
+  int cnt = 0;
+#pragma unroll
+  for (int c = 0; c < kBSChunks; ++c) {
+    if (c * kBSThreads >= a.n) break;       // uniform
+    const bool match = rs[c] == slot;
+    const uint64_t m = __ballot(match);
+    if (lane == 0) s_wc[wave] = __popcll(m);
+    __syncthreads();
+    int before = cnt, total = 0;
+#pragma unroll
+    for (int w = 0; w < kShW; ++w) {
+      before += w < wave ? s_wc[w] : 0;
+      total += s_wc[w];
+    }
+    if (match) s_rows[before + __popcll(m & lanemask_lt())] = c * kBSThreads + tid;
+    cnt += total;
+    __syncthreads();
+  }
+  const int p0 = rb * kRowBlk, p1 = min(cnt, p0 + kRowBlk);
+  if (p0 >= p1) return;
+  shrink_rows<T>(X, ldx, A, slot, k0, min(kShRB, R - k0), r, a.r_max, d_in, s_rows, p0, p1, H,
+                 s_part);
+}
+
 }  // namespace
+
+hipError_t launch_build_shrink(const BuildArgs &a, const void *X, int64_t ldx,
+                               const PoolView &pool, float *H, hipStream_t stream) {
+  if (a.n < 1 || a.n > kBSMaxRows) return hipErrorNotSupported;
+  const int nkb = (pool.r_max + kShRB - 1) / kShRB;
+  const int nrb = (a.n + kRowBlk - 1) / kRowBlk;
+  const long blocks = 1 + (long)pool.n_slots * nkb * nrb;
+  if (blocks > 16384) return hipErrorNotSupported;
+  const int words_build = build_lds_words(a.n_slots, kBSThreads);
+  const int words_shrink = kShW * kShNP + kShW + a.n;
+  const size_t lds = (size_t)(words_build > words_shrink ? words_build : words_shrink) * 4;
+  if (pool.dtype == 1)
+    hipLaunchKernelGGL(build_shrink_kernel<bf16_t>, dim3((unsigned)blocks), dim3(kBSThreads), lds,
+                       stream, a, (const bf16_t *)X, ldx, (const bf16_t *)pool.A, pool.d_in,
+                       pool.policy, nkb, H);
+  else
+    hipLaunchKernelGGL(build_shrink_kernel<float>, dim3((unsigned)blocks), dim3(kBSThreads), lds,
+                       stream, a, (const float *)X, ldx, (const float *)pool.A, pool.d_in,
+                       pool.policy, nkb, H);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
                                  const int32_t *slot_rank, const float *slot_scale,
@@ -273,7 +374,8 @@ hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, in
   // one wave per 64 rows up to 16 waves
   int threads = ((n + kWave - 1) / kWave) * kWave;
   threads = threads < kWave ? kWave : (threads > kThreads ? kThreads : threads);
-  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(threads), 0, stream, a);
+  const size_t lds = (size_t)build_lds_words(n_slots, threads) * 4;
+  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(threads), lds, stream, a);
   return hipGetLastError();
 }
 

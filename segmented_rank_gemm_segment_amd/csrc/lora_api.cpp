@@ -104,6 +104,35 @@ lora_status lora_build_segments(const int32_t *row_slot, const lora_pool *pool,
       static_cast<hipStream_t>(stream)));
 }
 
+lora_status lora_build_shrink(const int32_t *row_slot, const void *X, int64_t ldx,
+                              const lora_pool *pool, const lora_segments *seg, float *H,
+                              void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  if (seg->n_rows > 0 && !row_slot) return LORA_ERR_NULL;
+  st = check_matrix(X, ldx, pool->d_in, seg->n_rows);
+  if (st != LORA_OK) return st;
+  if (seg->n_rows > 0) {
+    if (!H) return LORA_ERR_NULL;
+    if (!aligned16(H)) return LORA_ERR_ALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const lora::BuildArgs a{row_slot,           seg->n_rows,         pool->n_slots,
+                          pool->r_max,        pool->slot_rank,     pool->slot_scale,
+                          seg->token_indices, seg->row_segment,    seg->segment_offsets,
+                          seg->segment_slots, seg->segment_ranks,  seg->segment_scales,
+                          seg->num_segments,  seg->status};
+  const hipError_t e = lora::launch_build_shrink(a, X, ldx, pool_view(pool), H, s);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  // outside the one-launch case: the two calls in sequence
+  (void)hipGetLastError();
+  st = lora_build_segments(row_slot, pool, seg, stream);
+  if (st != LORA_OK || seg->n_rows == 0) return st;
+  return hip_status(lora::launch_shrink(X, ldx, seg_view(seg), pool_view(pool), H, s));
+}
+
 lora_status lora_shrink(const void *X, int64_t ldx, const lora_segments *seg,
                         const lora_pool *pool, float *H, void *stream) {
   lora_status st = check_pool(pool);

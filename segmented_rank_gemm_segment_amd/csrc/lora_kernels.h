@@ -26,6 +26,20 @@ struct PoolView {
   const float *dora;   // optional DoRA column factors ([n_slots][d_out]) or null
 };
 
+struct BuildArgs {
+  const int32_t *row_slot;
+  int n, n_slots, r_max;
+  const int32_t *slot_rank;
+  const float *slot_scale;
+  int32_t *token_indices, *row_segment, *seg_off, *seg_slot, *seg_rank;
+  float *seg_scale;
+  int32_t *num_segments, *status;
+};
+
+// LDS words the segment build needs for a pool of n_slots and a workgroup
+// of nthr threads.
+int build_lds_words(int n_slots, int nthr);
+
 hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
                                  const int32_t *slot_rank, const float *slot_scale,
                                  int32_t *token_indices, int32_t *row_segment, int32_t *seg_off,
@@ -34,6 +48,13 @@ hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, in
 
 hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const PoolView &pool,
                          float *H, hipStream_t stream);
+
+// Segment build and shrink as one launch when every segment is short: block
+// 0 builds the metadata while the other blocks compute H slot by slot from
+// the per-row slot ids.  Returns hipErrorNotSupported (nothing launched)
+// when the batch is outside that case.
+hipError_t launch_build_shrink(const BuildArgs &a, const void *X, int64_t ldx,
+                               const PoolView &pool, float *H, hipStream_t stream);
 
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream);

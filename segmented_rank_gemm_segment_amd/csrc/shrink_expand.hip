@@ -22,11 +22,10 @@
 #include "lds_dma.cuh"
 #include "lora_device.cuh"
 #include "lora_kernels.h"
+#include "shrink_rows.cuh"
 
 namespace lora {
 namespace {
-
-constexpr int kRowBlk = 64;   // rows of one segment per work item
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
@@ -41,49 +40,13 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // The partials are reduced over the lanes by a halving butterfly (after it,
 // lane l holds pair l % 32), then over the waves through LDS in wave order.
 // ----------------------------------------------------------------------------
-constexpr int kShW = 4;        // waves per workgroup
-constexpr int kShRQ = 4;       // token rows per group
-constexpr int kShRB = 8;       // rank rows per workgroup
-constexpr int kShCU = 2;       // chunks per wave in flight
-
-// One halving step of the butterfly: the lanes with bit H set keep the
-// upper half of the H * 2 live values, the others the lower half, and each
-// adds its partner's copy of the half it keeps.
-template <int H, int N>
-__device__ __forceinline__ void butterfly_step(float (&v)[N], int lane) {
-  const bool up = (lane & H) != 0;
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    const float keep = up ? v[i + H] : v[i];
-    const float send = up ? v[i] : v[i + H];
-    v[i] = keep + __shfl_xor(send, H);
-  }
-  if constexpr (H > 1) butterfly_step<H / 2>(v, lane);
-}
-
-// Sum of v[0..N) over the 64 lanes, one pair per lane: on return v[0] of
-// lane l holds the total of pair l % N (N a power of two, 2 <= N <= 32).
-template <int N>
-__device__ __forceinline__ void butterfly_reduce(float (&v)[N], int lane) {
-  butterfly_step<N / 2>(v, lane);
-  // lanes l, l ^ N, l ^ 2N, ... hold partial totals of the same pair
-#pragma unroll
-  for (int h = N; h < kWave; h *= 2) v[0] += __shfl_xor(v[0], h);
-}
-
 template <typename T>
 __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
     const int32_t *num_segments, int r_max, int d_in, int policy, int seg_cap,
     int cap_items, int long_min, float *__restrict__ H) {
-  constexpr int V = Elem<T>::kVec;
-  constexpr int CH = kWave * V;                 // elements per chunk
-  constexpr int NP = kShRQ * kShRB;             // (row, rank row) pairs
-  static_assert(NP <= 32 && (NP & (NP - 1)) == 0, "pairs per lane");
-  __shared__ float s_part[kShW][NP];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  __shared__ float s_part[kShW][kShNP];
   const int k0 = blockIdx.x * kShRB;
   // items are ordered block-major (item = b * seg_cap + s): the first row
   // block of every segment comes first, so launch-order work is real work
@@ -94,81 +57,14 @@ __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
     // s < capacity keeps the metadata read in bounds before S is known
     const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, nullptr);
     if (s >= m.S) continue;
-    const int r = m.r;
-    const int R = rank_bucket(r, policy, r_max);
+    const int R = rank_bucket(m.r, policy, r_max);
     if (k0 >= R) continue;
     if (m.o1 - m.o0 >= long_min) continue;   // long segment: tiled MFMA kernel
     const int p0 = m.o0 + b * kRowBlk;
     const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
-    // rank rows of this block inside the processed width R (R <= r_max, and
-    // k0 + kk < R keeps every adapter row inside the slot)
-    const int nk = min(kShRB, R - k0);
-    const T *a0 = A + ((int64_t)m.slot * r_max + k0) * d_in;
-    for (int q0 = p0; q0 < p1; q0 += kShRQ) {
-      const int nq = min(kShRQ, p1 - q0);
-      // row indices of the group in one vector load (lane q: row q; lanes
-      // past the group repeat its last row), issued ahead of the adapter
-      // rows so that waiting for them does not wait for those
-      const int tv = token_indices[q0 + min(lane, nq - 1)];
-      __builtin_amdgcn_sched_barrier(0);
-      float acc[NP];
-#pragma unroll
-      for (int i = 0; i < NP; ++i) acc[i] = 0.f;
-      for (int cb = wave * CH; cb < d_in; cb += kShW * CH * kShCU) {
-        // Every load is unconditional: addresses past d_in are clamped into
-        // the row (d_in % 8 == 0), rank rows past the block's width re-read
-        // its last row and rows past the group re-read its last row; all of
-        // those values are dropped where they are used.
-        uint4 av[kShCU][kShRB], xv[kShCU][kShRQ];
-#pragma unroll
-        for (int u = 0; u < kShCU; ++u) {
-          const int cc = min(cb + u * kShW * CH + lane * V, d_in - V);
-#pragma unroll
-          for (int kk = 0; kk < kShRB; ++kk)
-            av[u][kk] = ldg16(a0 + (int64_t)min(kk, nk - 1) * d_in + cc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kShCU; ++u) {
-          const int cc = min(cb + u * kShW * CH + lane * V, d_in - V);
-#pragma unroll
-          for (int q = 0; q < kShRQ; ++q)
-            xv[u][q] = ldg16(X + (int64_t)__builtin_amdgcn_readlane(tv, q) * ldx + cc);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use
-#pragma unroll
-        for (int u = 0; u < kShCU; ++u) {
-          const bool ok = cb + u * kShW * CH + lane * V < d_in;
-#pragma unroll
-          for (int q = 0; q < kShRQ; ++q) {
-            float xf[V];
-            Elem<T>::unpack(xv[u][q], xf);
-#pragma unroll
-            for (int e = 0; e < V; ++e) xf[e] = (ok && q < nq) ? xf[e] : 0.f;
-#pragma unroll
-            for (int kk = 0; kk < kShRB; ++kk) {
-              float af[V];
-              Elem<T>::unpack(av[u][kk], af);
-#pragma unroll
-              for (int e = 0; e < V; ++e) acc[q * kShRB + kk] = fmaf(af[e], xf[e], acc[q * kShRB + kk]);
-            }
-          }
-        }
-      }
-      butterfly_reduce<NP>(acc, lane);
-      if (lane < NP) s_part[wave][lane] = acc[0];
-      __syncthreads();
-      if (threadIdx.x < NP) {
-        const int q = threadIdx.x / kShRB, kk = threadIdx.x % kShRB;
-        float t = s_part[0][threadIdx.x];
-#pragma unroll
-        for (int w = 1; w < kShW; ++w) t += s_part[w][threadIdx.x];
-        const int row = __shfl(tv, q);
-        if (q < nq && k0 + kk < r) H[(int64_t)row * r_max + k0 + kk] = t;
-      }
-      __syncthreads();   // s_part is rewritten by the next group
-    }
+    shrink_rows<T>(X, ldx, A, m.slot, k0, min(kShRB, R - k0), m.r, r_max, d_in, token_indices,
+                   p0, p1, H, s_part);
   }
 }
 

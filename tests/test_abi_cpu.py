@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
-              "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_status_str",
+              "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
+              "lora_status_str",
               "lora_abi_version"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
@@ -172,6 +173,20 @@ def test_dora_prepare_validation(L):
     assert prep(p, 0, W, 64, P + 2, None) == EALIGN                    # magnitude
     assert prep(ctypes.byref(pool(dora_scale=P + 4)), 0, W, 64, P, None) == EALIGN
     assert prep(ctypes.byref(pool(r_max=12, dora_scale=P)), 0, W, 64, P, None) == ERANK
+
+
+def test_build_shrink_validation(L):
+    """The one-call build + shrink rejects what either call rejects."""
+    bs = L.lora_build_shrink
+    X, H = P + 0xC000, P + 0xD000
+    assert bs(P, X, 64, ctypes.byref(pool(r_max=12)), ctypes.byref(segs()), H, None) == ERANK
+    assert bs(P, X, 64, ctypes.byref(pool()), ctypes.byref(segs(max_segments=4)), H, None) == ECAP
+    assert bs(None, X, 64, ctypes.byref(pool()), ctypes.byref(segs()), H, None) == ENULL
+    assert bs(P, None, 64, ctypes.byref(pool()), ctypes.byref(segs()), H, None) == ENULL
+    assert bs(P, X, 60, ctypes.byref(pool()), ctypes.byref(segs()), H, None) == ESHAPE
+    assert bs(P, X + 4, 64, ctypes.byref(pool()), ctypes.byref(segs()), H, None) == EALIGN
+    assert bs(P, X, 64, ctypes.byref(pool()), ctypes.byref(segs()), None, None) == ENULL
+    assert bs(P, X, 64, ctypes.byref(pool()), ctypes.byref(segs()), H + 8, None) == EALIGN
 
 
 def test_expand_and_fused_validation(L):
