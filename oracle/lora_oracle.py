@@ -253,6 +253,49 @@ def merged_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype):
 
 
 # ---------------------------------------------------------------------------
+# quantized base weight (FP8 E4M3 codes, one scale per output row)
+# ---------------------------------------------------------------------------
+# The adapter-batching page (section "Quantized Base Model 与 LoRA 的 Dtype
+# 边界") lets the base weight be INT4/INT8/FP8 while A and B stay 16-bit, and
+# asks where the two paths add; the multi-tenant serving article (section 1.2)
+# dequantizes the base weight inside the kernel and keeps the alpha/r scaling
+# there too.  Readings: the base weight is W[j, c] = w_scale[j] * e4m3(Wq[j,
+# c]) with E4M3 as the OCP 8-bit floating point specification defines it;
+# the LoRA branch takes the same (unquantized) activations X; the two paths
+# add in full precision before the output is rounded once.
+def decode_fp8_e4m3(codes) -> np.ndarray:
+    """Exact float64 value of OCP FP8 E4M3 codes: 1 sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6;
+    S.1111.111 is NaN; there are no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * (m / 8.0) * np.exp2(-6.0)
+    v = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, v)
+
+
+def lora_forward_fp8w(X, Wq, w_scale, A, B, row_slot, slot_rank, slot_alpha, r_max: int,
+                      dtype: str, rows: Optional[Iterable[int]] = None):
+    """Y = X W^T + s_a (X_a A_a^T) B_a^T with the base weight given as E4M3
+    codes and per-row scales: W = w_scale[:, None] * e4m3(Wq), in float64.
+    The LoRA branch is ``lora_forward``'s (evaluated with a zero base weight,
+    so it does not depend on W).  Returns (Y, dY, H) like ``lora_forward``."""
+    d_out, d_in = np.shape(Wq)
+    zero_w = np.zeros((d_out, d_in), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    _, dY, H = lora_forward(X, zero_w, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype,
+                            rows=rows)
+    W64 = decode_fp8_e4m3(Wq) * np.asarray(w_scale, dtype=np.float64)[:, None]
+    X64 = decode(X, dtype)
+    n = X64.shape[0]
+    rows = list(range(n)) if rows is None else [int(i) for i in rows]
+    Xr = X64[rows] if rows else np.zeros((0, d_in))
+    return Xr @ W64.T + dY, dY, H
+
+
+# ---------------------------------------------------------------------------
 # DoRA: magnitude times normalised direction
 # ---------------------------------------------------------------------------
 # The ybb.press multi-LoRA serving article, section 9.2 (DoRA), writes the

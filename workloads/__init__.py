@@ -339,6 +339,25 @@ def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_m
     return w
 
 
+def fp8_e4m3_bits_rne(x32) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 bit patterns (uint8), round to nearest even,
+    saturating at +-448 (input encoding only; torch's conversion)."""
+    import torch
+    t = torch.from_numpy(np.clip(np.asarray(x32, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def make_fp8_weight(seed: int, d_out: int, d_in: int, w_std: float = 0.02):
+    """A quantized base weight: E4M3 codes of N(0, 1) draws [d_out, d_in]
+    (uint8) and one float32 scale per output row, uniform in
+    [0.5 w_std, 1.5 w_std], so the weight the codes stand for has about the
+    spread of the bf16 workloads' W."""
+    rng = _rng(np.random.SeedSequence([seed, 0xF8]))
+    codes = fp8_e4m3_bits_rne(rng.standard_normal((d_out, d_in), dtype=np.float32))
+    scale = ((rng.random(d_out, dtype=np.float32) + np.float32(0.5)) * np.float32(w_std))
+    return codes, scale.astype(np.float32)
+
+
 def make_magnitude(seed: int, n_slots: int, d_out: int, scale: float, p_plain: float = 0.25,
                    plain_slots=None):
     """DoRA magnitude vectors, one per slot: float32 [d_out] drawn uniform in
