@@ -270,6 +270,43 @@ lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t
                               const float *H, const lora_segments *seg,
                               const lora_pool *pool, void *Y, int64_t ldy, void *stream);
 
+/*
+ * Quantized base weight (adapter-batching page, section "Quantized Base
+ * Model 与 LoRA 的 Dtype 边界": the base weight may be INT4/INT8/FP8 while A
+ * and B stay 16-bit; LoRA/QLoRA 多租户GPU推理服务化实战, section 1.2: the
+ * base weight is dequantized inside the kernel, at register level, and the
+ * alpha/r scaling stays inside the fused kernel).  Here the base weight is
+ * FP8 E4M3 (the OCP 8-bit floating point format) with one float32 scale per
+ * output row:
+ *   W[j][c] = w_scale[j] * e4m3(Wq[j][c]),   Wq [d_out][d_in] bytes (ld ldw)
+ * and the answers to the page's questions are:
+ *   - the base GEMM reads Wq from HBM (one byte per weight), widens each
+ *     code to bf16 in registers (exact: every E4M3 value is a bf16 value),
+ *     multiplies by the bf16 activations on MFMA and accumulates in fp32;
+ *     w_scale[j] multiplies the fp32 accumulator of column j;
+ *   - the LoRA branch reuses the same, unquantized bf16 activations X
+ *     (lora_shrink / lora_build_shrink are unchanged); A and B are bf16
+ *     with scale s_a = alpha_a / r_a;
+ *   - the two paths add in fp32 after the weight scale and before the one
+ *     rounding to bf16 (and before a tensor-parallel reduction, which would
+ *     sum the rounded partial outputs).
+ * Requirements on top of the bf16 calls: X and Y bf16, d_in % 16 == 0,
+ * ldw % 16 == 0, Wq and w_scale 16-byte aligned (LORA_ERR_ALIGN), Wq and
+ * w_scale non-NULL (LORA_ERR_NULL), ldw >= d_in (LORA_ERR_SHAPE).  Codes
+ * 0x7F / 0xFF (NaN) propagate NaN.
+ */
+lora_status lora_base_gemm_fp8w(const void *X, int64_t ldx, const void *Wq, int64_t ldw,
+                                const float *w_scale, void *Y, int64_t ldy, int32_t n_rows,
+                                int32_t d_in, int32_t d_out, void *stream);
+
+/* lora_linear_fused with the FP8 base weight above; the pool must be bf16
+ * (LORA_ERR_DTYPE otherwise).  Rows of base-only and rank-0 segments equal
+ * lora_base_gemm_fp8w's output bit for bit. */
+lora_status lora_linear_fused_fp8w(const void *X, int64_t ldx, const void *Wq, int64_t ldw,
+                                   const float *w_scale, const float *H,
+                                   const lora_segments *seg, const lora_pool *pool, void *Y,
+                                   int64_t ldy, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,8 @@ EXPORTS = (
     "lora_pool_dora_prepare",
     "lora_base_gemm",
     "lora_linear_fused",
+    "lora_base_gemm_fp8w",
+    "lora_linear_fused_fp8w",
 )
 
 
@@ -120,6 +122,10 @@ def lib() -> ctypes.CDLL:
     L.lora_base_gemm.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
     L.lora_linear_fused.restype = i32
     L.lora_linear_fused.argtypes = [vp, i64, vp, i64, vp, SP, PP, vp, i64, vp]
+    L.lora_base_gemm_fp8w.restype = i32
+    L.lora_base_gemm_fp8w.argtypes = [vp, i64, vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    L.lora_linear_fused_fp8w.restype = i32
+    L.lora_linear_fused_fp8w.argtypes = [vp, i64, vp, i64, vp, vp, SP, PP, vp, i64, vp]
     if L.lora_abi_version() != ABI_VERSION:
         raise RuntimeError("liblora ABI version mismatch")
     _lib = L
@@ -379,3 +385,33 @@ def lora_linear_fused(X: torch.Tensor, W: torch.Tensor, H: torch.Tensor, seg: Se
         raise ValueError("H: contiguous float32 [n_rows, r_max]")
     _check(lib().lora_linear_fused(_ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(H), seg.c, pool.c,
                                    _ptr(Y), _ld(Y), _stream(stream)))
+
+
+def lora_base_gemm_fp8w(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, Y: torch.Tensor,
+                        stream=None) -> None:
+    """Y = X (w_scale * e4m3(Wq))^T with Wq uint8 E4M3 codes [d_out, d_in]
+    and w_scale float32 [d_out]; X, Y bf16."""
+    if X.dtype != torch.bfloat16 or Y.dtype != torch.bfloat16:
+        raise ValueError("X and Y must be bf16")
+    if Wq.dtype != torch.uint8 or w_scale.dtype != torch.float32 or not w_scale.is_contiguous():
+        raise ValueError("Wq uint8 E4M3 codes, w_scale contiguous float32")
+    n, d_in = X.shape
+    d_out = Wq.shape[0]
+    if Wq.shape[1] != d_in or tuple(Y.shape) != (n, d_out) or w_scale.numel() != d_out:
+        raise ValueError("shapes: X [n, d_in], Wq [d_out, d_in], w_scale [d_out], Y [n, d_out]")
+    _check(lib().lora_base_gemm_fp8w(_ptr(X), _ld(X), _ptr(Wq), _ld(Wq), _ptr(w_scale), _ptr(Y),
+                                     _ld(Y), n, d_in, d_out, _stream(stream)))
+
+
+def lora_linear_fused_fp8w(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+                           H: torch.Tensor, seg: Segments, pool: Pool, Y: torch.Tensor,
+                           stream=None) -> None:
+    """lora_linear_fused with the FP8 E4M3 base weight (Wq, w_scale)."""
+    if Wq.dtype != torch.uint8 or w_scale.dtype != torch.float32 or not w_scale.is_contiguous():
+        raise ValueError("Wq uint8 E4M3 codes, w_scale contiguous float32")
+    if tuple(Wq.shape) != (pool.d_out, pool.d_in) or w_scale.numel() != pool.d_out:
+        raise ValueError("Wq [d_out, d_in], w_scale [d_out]")
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max):
+        raise ValueError("H: float32 [n_rows, r_max]")
+    _check(lib().lora_linear_fused_fp8w(_ptr(X), _ld(X), _ptr(Wq), _ld(Wq), _ptr(w_scale), _ptr(H),
+                                        seg.c, pool.c, _ptr(Y), _ld(Y), _stream(stream)))

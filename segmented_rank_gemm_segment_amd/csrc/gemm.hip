@@ -47,6 +47,7 @@ struct GemmArgs {
   const float *seg_scale;
   int r_max, policy;
   const float *dora;   // optional DoRA column factors ([slot][N]) or null
+  const float *wscale; // FP8 weight: one scale per output row (W then holds E4M3 codes)
 };
 
 // Tile configurations <BM, BN, waves along M, waves along N, K per group
@@ -68,26 +69,32 @@ struct GemmArgs {
 // KG wave groups split each K step: group g takes the g-th BK-wide slice of
 // it with its own WM x WN waves and its own slice of the stage, and the
 // groups' partial sums are added through LDS at the end (KG = 1: one group).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
+// EB: bytes per element of the B operand (W): 2 for bf16, 1 for FP8 codes.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int EB = 2>
 struct TileCfg {
   static constexpr int NWG = WM * WN;               // waves per group
   static constexpr int NW = NWG * KG;
   static constexpr int T = NW * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int CH = BK / 8;                 // 16-byte chunks per operand row
-  static constexpr int RB = BK * 2;                 // bytes per operand row in LDS
-  static constexpr int RPI = 1024 / RB;             // rows per 1 KB DMA instruction
-  static constexpr int AI = BM / RPI / NWG, BI = BN / RPI / NWG;  // DMA instructions per wave
+  static constexpr int CH = BK / 8;                 // 16-byte chunks per A row (bf16)
+  static constexpr int RB = BK * 2;                 // bytes per A row in LDS
+  static constexpr int RPI = 1024 / RB;             // A rows per 1 KB DMA instruction
+  static constexpr int RBB = BK * EB;               // bytes per B row in LDS
+  static constexpr int CHB = RBB / 16;              // 16-byte chunks per B row
+  static constexpr int RPIB = 1024 / RBB;           // B rows per 1 KB DMA instruction
+  static constexpr int EPCB = 16 / EB;              // B elements per 16-byte chunk
+  static constexpr int AI = BM / RPI / NWG, BI = BN / RPIB / NWG;  // DMA instructions per wave
   static constexpr int IPW = AI + BI;
-  static constexpr int GSTAGE = (BM + BN) * RB;     // bytes of one group's slice
+  static constexpr int GSTAGE = BM * RB + BN * RBB; // bytes of one group's slice
   static constexpr int STAGE = KG * GSTAGE;         // bytes of a stage
   static constexpr int KSTEP = KG * BK;             // K per stage
   static constexpr int LDS = STAGES * STAGE;
   static constexpr int RED = (KG - 1) * NWG * FM * FN * 16 * kWave * 4;  // partial sums
   static_assert(BK == 32 || BK == 64, "K per stage");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert(BM % (RPI * NWG) == 0 && BN % (RPI * NWG) == 0, "DMA split");
+  static_assert(BM % (RPI * NWG) == 0 && BN % (RPIB * NWG) == 0, "DMA split");
+  static_assert(EB == 2 || (EB == 1 && BK == 64), "FP8 B rows are 64 bytes");
   static_assert(STAGES >= 2 && STAGES - 2 <= 6 && (STAGES - 2) * IPW <= 63, "pipeline depth");
   static_assert(LDS <= 160 * 1024 && RED <= LDS, "LDS");
   // physical chunk of logical chunk c in row r.  The gfx950 LDS serves a
@@ -98,17 +105,41 @@ struct TileCfg {
   __device__ static __forceinline__ int swz(int c, int r) {
     return CH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
   }
+  // the same for B rows (64-byte rows: four per bank row, so the chunk is
+  // XORed with bits 2..3 of the row)
+  __device__ static __forceinline__ int swzb(int c, int r) {
+    return CHB == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+  }
 };
 
+// Eight E4M3 codes (bytes of lo, then hi; element e = byte e) to eight bf16
+// for the MFMA: every E4M3 value is exact in bf16, so this is exact.
+__device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  return as_bf16x8(u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y),
+                         pack_bf16x2(d.x, d.y)});
+}
+
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
-// chunks XOR-swizzled per row (TileCfg::swz).
+// chunks XOR-swizzled per row (TileCfg::swz, swzb).  WF8: W holds E4M3 codes
+// (one byte per element, 64-byte B rows in LDS), widened to bf16 as each
+// fragment is read; the per-row weight scale multiplies the fp32 base
+// accumulator before the LoRA term is added.
 // LORA: 0 = plain product; 1 = fused LoRA with B gathered from Bt; 2 = fused
 // LoRA with B read from its d_out-major copy.  DORA: rows of rank > 0 are
 // multiplied by their slot's column factors before the rounding.
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, bool DORA>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, bool DORA,
+          bool WF8>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
-  using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG>;
-  __shared__ __align__(16) unsigned char smem[C::LDS];
+  using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG, WF8 ? 1 : 2>;
+  // LDS: the stage ring, or the fused LoRA staging of large tiles if larger
+  constexpr int LSTG = (LORA != 0 && KG == 1) ? 3 * (BM > BN ? BM : BN) * 128 + 16 + 4 * BM : 0;
+  constexpr int SMEM = C::LDS > LSTG ? C::LDS : LSTG;
+  __shared__ __align__(16) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
@@ -148,15 +179,22 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
   if constexpr (ROWEPI && LORA != 0)
     e_seg = gload_b32(g.row_segment + min(m0 + e_row, M - 1));
+  // FP8 weight: the thread's 8 column scales, requested now as well
+  u32x4 e_ws0 = u32x4{0, 0, 0, 0}, e_ws1 = u32x4{0, 0, 0, 0};
+  if constexpr (ROWEPI && WF8) {
+    const float *ws = g.wscale + min(n0 + e_c8, N - 8);
+    e_ws0 = gload_b128(ws);
+    e_ws1 = gload_b128(ws + 4);
+  }
 
   // DMA sources: lane l of an instruction fills tile row base + l / CH at
   // physical chunk l % CH, i.e. logical chunk swz(l % CH, row) (a function
   // of the row, so of the instruction too).  Rows past M / N are clamped to
   // the last valid row (their results are never stored).
-  const int rr = l / C::CH;
+  const int rr = l / C::CH, rrb = l / C::CHB;
   int alc[C::AI], blc[C::BI];
   const bf16_t *asrc[C::AI];
-  const bf16_t *bsrc[C::BI];
+  const unsigned char *bsrc[C::BI];                 // B sources in bytes
 #pragma unroll
   for (int i = 0; i < C::AI; ++i) {
     const int row = (wid * C::AI + i) * C::RPI + rr;
@@ -165,10 +203,16 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   }
 #pragma unroll
   for (int i = 0; i < C::BI; ++i) {
-    const int row = (wid * C::BI + i) * C::RPI + rr;
-    blc[i] = C::swz(l % C::CH, row);
-    bsrc[i] = g.W + (int64_t)min(n0 + row, N - 1) * g.ldw + blc[i] * 8;
+    const int row = (wid * C::BI + i) * C::RPIB + rrb;
+    blc[i] = C::swzb(l % C::CHB, row);
+    bsrc[i] = reinterpret_cast<const unsigned char *>(g.W) +
+              ((int64_t)min(n0 + row, N - 1) * g.ldw + blc[i] * C::EPCB) * (WF8 ? 1 : 2);
   }
+  // byte offset of K position k0 in a B row's chunk, or back to the row's
+  // first chunk when the chunk lies past K (in bounds; zeroed before use)
+  auto boff = [&](int i, int k0) __attribute__((always_inline)) {
+    return (k0 + blc[i] * C::EPCB < K) ? k0 * (WF8 ? 1 : 2) : -blc[i] * 16;
+  };
   const uint32_t sbase = lds_offset(smem);
   const uint32_t a_dst =
       __builtin_amdgcn_readfirstlane(sbase + kgrp * C::GSTAGE + wid * C::AI * 1024);
@@ -183,9 +227,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       dma16(a_dst + stage * C::STAGE + i * 1024,
             asrc[i] + ((k0 + alc[i] * 8 < K) ? k0 : -alc[i] * 8));
 #pragma unroll
-    for (int i = 0; i < C::BI; ++i)
-      dma16(b_dst + stage * C::STAGE + i * 1024,
-            bsrc[i] + ((k0 + blc[i] * 8 < K) ? k0 : -blc[i] * 8));
+    for (int i = 0; i < C::BI; ++i) dma16(b_dst + stage * C::STAGE + i * 1024, bsrc[i] + boff(i, k0));
   };
   // instruction q of a stage's DMA (A rows first, then B rows)
   auto issue_one = [&](int q, int stage, int k0) __attribute__((always_inline)) {
@@ -193,8 +235,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       dma16(a_dst + stage * C::STAGE + q * 1024,
             asrc[q] + ((k0 + alc[q] * 8 < K) ? k0 : -alc[q] * 8));
     else
-      dma16(b_dst + stage * C::STAGE + (q - C::AI) * 1024,
-            bsrc[q - C::AI] + ((k0 + blc[q - C::AI] * 8 < K) ? k0 : -blc[q - C::AI] * 8));
+      dma16(b_dst + stage * C::STAGE + (q - C::AI) * 1024, bsrc[q - C::AI] + boff(q - C::AI, k0));
   };
   auto zero_tail = [&](int stage, int k0) {
     unsigned char *st = smem + stage * C::STAGE + kgrp * C::GSTAGE;
@@ -204,7 +245,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
         *reinterpret_cast<u32x4 *>(st + (wid * C::AI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < C::BI; ++i)
-      if (k0 + blc[i] * 8 >= K)
+      if (k0 + blc[i] * C::EPCB >= K)
         *reinterpret_cast<u32x4 *>(st + BM * C::RB + (wid * C::BI + i) * 1024 + l * 16) =
             u32x4{0, 0, 0, 0};
   };
@@ -225,10 +266,15 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     a_row_off[i] = kgrp * C::GSTAGE + (wm * C::TM + i * 32 + (l & 31)) * C::RB;
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
-    b_row_off[j] = kgrp * C::GSTAGE + BM * C::RB + (wn * C::TN + j * 32 + (l & 31)) * C::RB;
-  int chunk_off[BK / 16];
+    b_row_off[j] = kgrp * C::GSTAGE + BM * C::RB + (wn * C::TN + j * 32 + (l & 31)) * C::RBB;
+  int chunk_off[BK / 16], chunkb_off[BK / 16];
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = C::swz(kk * 2 + (l >> 5), l & 31) * 16;
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    chunk_off[kk] = C::swz(kk * 2 + (l >> 5), l & 31) * 16;
+    // bf16 B: as A; FP8 B: sub-step kk is chunk kk, half l / 32 (8 bytes)
+    chunkb_off[kk] = WF8 ? C::swzb(kk, l & 31) * 16 + (l >> 5) * 8
+                         : C::swzb(kk * 2 + (l >> 5), l & 31) * 16;
+  }
 
   const int KT = (K + C::KSTEP - 1) / C::KSTEP;
   const bool ktail = (K % C::KSTEP) != 0;
@@ -251,8 +297,14 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     for (int i = 0; i < C::FM; ++i)
       af[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off[i] + chunk_off[kk]));
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      bfr[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off[j] + chunk_off[kk]));
+    for (int j = 0; j < C::FN; ++j) {
+      if constexpr (WF8) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(st + b_row_off[j] + chunkb_off[kk]);
+        bfr[buf][j] = fp8x8_to_bf16x8(q.x, q.y);
+      } else {
+        bfr[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off[j] + chunkb_off[kk]));
+      }
+    }
   };
   auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -326,7 +378,11 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // (k ascending, read in chunks of 8 rank rows; rows at or past r are
     // read inside the slot and skipped), the DoRA factor when the pool has
     // one, and one rounding; the 8 results leave in one 16-byte store.
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
+    if constexpr (WF8)
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb), "+v"(e_ws0),
+                   "+v"(e_ws1)::"memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
     lgkm_barrier();
     float *red = reinterpret_cast<float *>(smem);
     constexpr int RS = BN + 4;
@@ -356,6 +412,13 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
     const int grow = m0 + e_row, gcol = n0 + e_c8;
     const bool live = grow < M && gcol < N;       // N % 8 == 0: all 8 columns or none
+    if constexpr (WF8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] *= __uint_as_float(e_ws0[e]);
+        o[4 + e] *= __uint_as_float(e_ws1[e]);
+      }
+    }
     if constexpr (LORA != 0) {
       if (live && e_r > 0) {
         const bf16_t *bt = g.Bt + (int64_t)e_slot * g.r_max * N + gcol;
@@ -430,6 +493,18 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           }
   }
 
+  if constexpr (WF8 && !ROWEPI) {
+    // FP8 weight: the per-row weight scale of each accumulator column
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const float sw = g.wscale[min(n0 + wn * C::TN + j * 32 + (l & 31), N - 1)];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] *= sw;
+    }
+  }
+
   if constexpr (LORA != 0 && !ROWEPI) {
     // LoRA increment, after the K loop, one distinct LoRA segment u of the
     // tile's rows at a time (ascending id).  The whole workgroup stages the
@@ -444,7 +519,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // add exact zeros, so base-only rows stay bit-identical to the plain
     // product.
     constexpr int RBL = 128;                          // bytes per staged row
-    static_assert(3 * (BM > BN ? BM : BN) * RBL + 16 + 4 * BM <= C::LDS, "LoRA staging");
+    static_assert(3 * (BM > BN ? BM : BN) * RBL + 16 + 4 * BM <= SMEM, "LoRA staging");
     static_assert(C::T >= BM, "one tile row per thread");
     unsigned char *s_ahi = smem;
     unsigned char *s_alo = smem + BM * RBL;
@@ -702,39 +777,46 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
-hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, bool WF8>
+hipError_t launch_bf16_w(const GemmArgs &g, bool lora, hipStream_t stream) {
   const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(((ntiles + 7) / 8) * 8);
   dim3 block(WM * WN * KG * kWave);
   const bool dora = lora && g.dora;
   if (lora && g.Bn && dora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, true>), grid, block,
-                       0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, true, WF8>), grid,
+                       block, 0, stream, g);
   else if (lora && g.Bn)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, false>), grid, block,
-                       0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 2, false, WF8>), grid,
+                       block, 0, stream, g);
   else if (lora && dora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true>), grid, block,
-                       0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true, WF8>), grid,
+                       block, 0, stream, g);
   else if (lora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false>), grid, block,
-                       0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false, WF8>), grid,
+                       block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 0, false>), grid, block,
-                       0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 0, false, WF8>), grid,
+                       block, 0, stream, g);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
+hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
+  if (g.wscale) return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, true>(g, lora, stream);
+  return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, false>(g, lora, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
                        int64_t ldy, int M, int K, int N, int dtype, const float *H,
-                       const SegView *seg, const PoolView *pool, hipStream_t stream) {
+                       const SegView *seg, const PoolView *pool, hipStream_t stream,
+                       const float *wscale) {
   const bool lora = seg != nullptr;
   if (dtype == 1) {
     GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
-               H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr};
+               H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, wscale};
     if (lora) {
       g.Bt = (const bf16_t *)pool->Bt;
       g.Bn = (const bf16_t *)pool->B;

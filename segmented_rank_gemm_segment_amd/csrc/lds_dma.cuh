@@ -63,6 +63,14 @@ __device__ __forceinline__ int gload_b32(const void *p) {
   return r;
 }
 
+// 16-byte global load issued where it is written; the caller waits for it
+// (s_waitcnt vmcnt) before the first use of the result.
+__device__ __forceinline__ u32x4 gload_b128(const void *p) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 __device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }
 
 // Row of element v (0..15) of a 32x32 MFMA accumulator held by lane l

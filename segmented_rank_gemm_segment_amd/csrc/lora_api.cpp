@@ -218,6 +218,61 @@ lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ld
                                       static_cast<hipStream_t>(stream)));
 }
 
+// FP8 weight: E4M3 codes [d_out][ldw] (16-byte aligned rows, d_in % 16 == 0)
+// and one float32 scale per output row.
+lora_status check_fp8_weight(const void *Wq, int64_t ldw, const float *w_scale, int32_t d_in,
+                             int32_t d_out) {
+  if (d_in % 16) return LORA_ERR_ALIGN;
+  if (!Wq || !w_scale) return LORA_ERR_NULL;
+  if (ldw < d_in) return LORA_ERR_SHAPE;
+  if (ldw % 16 || !aligned16(Wq) || !aligned16(w_scale)) return LORA_ERR_ALIGN;
+  (void)d_out;
+  return LORA_OK;
+}
+
+lora_status lora_base_gemm_fp8w(const void *X, int64_t ldx, const void *Wq, int64_t ldw,
+                                const float *w_scale, void *Y, int64_t ldy, int32_t n_rows,
+                                int32_t d_in, int32_t d_out, void *stream) {
+  if (n_rows < 0 || d_in <= 0 || d_out <= 0) return LORA_ERR_SHAPE;
+  if (d_in % 8 || d_out % 8) return LORA_ERR_ALIGN;
+  lora_status st = check_fp8_weight(Wq, ldw, w_scale, d_in, d_out);
+  if (st != LORA_OK) return st;
+  st = check_matrix(X, ldx, d_in, n_rows);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, d_out, n_rows);
+  if (st != LORA_OK) return st;
+  if (n_rows == 0) return LORA_OK;
+  return hip_status(lora::launch_gemm(X, ldx, Wq, ldw, Y, ldy, n_rows, d_in, d_out, LORA_BF16,
+                                      nullptr, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream), w_scale));
+}
+
+lora_status lora_linear_fused_fp8w(const void *X, int64_t ldx, const void *Wq, int64_t ldw,
+                                   const float *w_scale, const float *H,
+                                   const lora_segments *seg, const lora_pool *pool, void *Y,
+                                   int64_t ldy, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (pool->dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  st = check_fp8_weight(Wq, ldw, w_scale, pool->d_in, pool->d_out);
+  if (st != LORA_OK) return st;
+  const int32_t n = seg->n_rows;
+  st = check_matrix(X, ldx, pool->d_in, n);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, pool->d_out, n);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  if (!H) return LORA_ERR_NULL;
+  if (!aligned16(H)) return LORA_ERR_ALIGN;
+  const lora::SegView sv = seg_view(seg);
+  const lora::PoolView pv = pool_view(pool);
+  return hip_status(lora::launch_gemm(X, ldx, Wq, ldw, Y, ldy, n, pool->d_in, pool->d_out,
+                                      LORA_BF16, H, &sv, &pv,
+                                      static_cast<hipStream_t>(stream), w_scale));
+}
+
 lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t ldw,
                               const float *H, const lora_segments *seg, const lora_pool *pool,
                               void *Y, int64_t ldy, void *stream) {

@@ -69,9 +69,12 @@ hipError_t launch_dora_prepare(const PoolView &pool, const int32_t *slot_rank,
                                const float *slot_scale, int slot, const void *W, int64_t ldw,
                                const float *magnitude, hipStream_t stream);
 
-// Y = X W^T (+ fused LoRA when seg/pool/H are given).
+// Y = X W^T (+ fused LoRA when seg/pool/H are given).  With wscale, W holds
+// FP8 E4M3 codes (bf16 X and Y) and row j of the weight is wscale[j] times
+// its codes.
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
                        int64_t ldy, int M, int K, int N, int dtype, const float *H,
-                       const SegView *seg, const PoolView *pool, hipStream_t stream);
+                       const SegView *seg, const PoolView *pool, hipStream_t stream,
+                       const float *wscale = nullptr);
 
 }  // namespace lora

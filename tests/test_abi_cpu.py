@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
               "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
-              "lora_status_str",
+              "lora_base_gemm_fp8w", "lora_linear_fused_fp8w", "lora_status_str",
               "lora_abi_version"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
@@ -187,6 +187,30 @@ def test_build_shrink_validation(L):
     assert bs(P, X + 4, 64, ctypes.byref(pool()), ctypes.byref(segs()), H, None) == EALIGN
     assert bs(P, X, 64, ctypes.byref(pool()), ctypes.byref(segs()), None, None) == ENULL
     assert bs(P, X, 64, ctypes.byref(pool()), ctypes.byref(segs()), H + 8, None) == EALIGN
+
+
+def test_fp8_weight_validation(L):
+    """FP8-weight calls: bf16 only, d_in % 16, 16-byte aligned codes, rows
+    and scales; checked on the host before any launch."""
+    W, S, X, Y, H = P + 0xC000, P + 0xC800, P + 0xD000, P + 0xE000, P + 0xF000
+    g = L.lora_base_gemm_fp8w
+    assert g(X, 64, W, 64, S, Y, 32, -1, 64, 32, None) == ESHAPE
+    assert g(X, 48, W, 48, S, Y, 32, 10, 40, 32, None) == EALIGN        # d_in % 16
+    assert g(X, 64, None, 64, S, Y, 32, 10, 64, 32, None) == ENULL
+    assert g(X, 64, W, 64, None, Y, 32, 10, 64, 32, None) == ENULL
+    assert g(X, 64, W, 56, S, Y, 32, 10, 64, 32, None) == ESHAPE        # ldw < d_in
+    assert g(X, 64, W, 72, S, Y, 32, 10, 64, 32, None) == EALIGN        # ldw % 16
+    assert g(X, 64, W + 8, 64, S, Y, 32, 10, 64, 32, None) == EALIGN
+    assert g(X, 64, W, 64, S + 4, Y, 32, 10, 64, 32, None) == EALIGN
+    assert g(X, 64, W, 64, S, Y + 2, 32, 10, 64, 32, None) == EALIGN
+    assert g(X, 64, W, 64, S, Y, 32, 0, 64, 32, None) == OK             # empty batch
+    f = L.lora_linear_fused_fp8w
+    p, sg = ctypes.byref(pool()), ctypes.byref(segs())
+    assert f(X, 64, W, 64, S, H, sg, ctypes.byref(pool(dtype=0)), Y, 32, None) == EDTYPE
+    assert f(X, 64, None, 64, S, H, sg, p, Y, 32, None) == ENULL
+    assert f(X, 64, W, 64, S, None, sg, p, Y, 32, None) == ENULL
+    assert f(X, 64, W, 72, S, H, sg, p, Y, 32, None) == EALIGN
+    assert f(X, 64, W, 64, S, H, sg, ctypes.byref(pool(d_in=40)), Y, 32, None) == EALIGN
 
 
 def test_expand_and_fused_validation(L):
