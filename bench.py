@@ -17,6 +17,7 @@ Prints one JSON line (rank 0; one GPU):
   prefill    = the prefill workload's step (tokens/s, TFLOP/s, MFMA fraction)
   dora       = the same step with every slot a DoRA adapter (column factors
                in the epilogue), and the per-adapter factor preparation
+  fp8_weight = the same step with the base weight in FP8 E4M3 (per-row scale)
   cpu_baseline = the float64 CPU oracle on a bounded sample of the headline
                workload, on this host's cores
 
@@ -60,6 +61,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dora", action="store_true",
                    help="skip the DoRA variant (column factors in the epilogue)")
+    p.add_argument("--no-fp8w", action="store_true",
+                   help="skip the FP8-weight variant of the base product")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the base product through torch.matmul for comparison")
     p.add_argument("--eager", action="store_true",
@@ -95,6 +98,10 @@ def work_figures(w):
             "expand": sum_r_distinct * do * e + sum_r_rows * 4 + 2 * n_lora * do * e,
             "base": do * di * e + n * di * e + n * do * e,
             "fused": do * di * e + n * di * e + n * do * e + sum_r_distinct * do * e + sum_r_rows * 4,
+            # FP8 base weight: one byte per weight plus a float32 scale per row
+            "base_fp8w": do * di + do * 4 + n * di * e + n * do * e,
+            "fused_fp8w": do * di + do * 4 + n * di * e + n * do * e + sum_r_distinct * do * e
+                          + sum_r_rows * 4,
         },
         "flops": {
             "shrink": 2 * sum_r_rows * di,
@@ -102,6 +109,8 @@ def work_figures(w):
             "expand": 2 * sum_r_rows * do,
             "base": 2 * n * di * do,
             "fused": 2 * n * di * do + 2 * sum_r_rows * do,
+            "base_fp8w": 2 * n * di * do,
+            "fused_fp8w": 2 * n * di * do + 2 * sum_r_rows * do,
         },
     }
     return f
@@ -111,6 +120,7 @@ def work_figures(w):
 # device state
 # ---------------------------------------------------------------------------
 DORA_SEED = 9
+FP8_SEED = 11
 
 
 def dora_magnitudes(w, device):
@@ -122,7 +132,7 @@ def dora_magnitudes(w, device):
 
 
 class Layer:
-    def __init__(self, w, policy, device, dora=False):
+    def __init__(self, w, policy, device, dora=False, fp8w=False):
         import torch
         import segmented_rank_gemm_segment_amd as srg
         import workloads as wl
@@ -134,6 +144,11 @@ class Layer:
         if dora:
             for a, m in enumerate(self.mag):
                 self.pool.dora_prepare(a, self.W, m)
+        self.Wq = self.ws = None
+        if fp8w:
+            codes, scale = wl.make_fp8_weight(FP8_SEED, w.d_out, w.d_in)
+            self.Wq = torch.from_numpy(codes).to(device)
+            self.ws = torch.from_numpy(scale).to(device)
         self.seg = srg.Segments(w.n, w.n_slots, device)
         dt = self.X.dtype
         self.H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=device)
@@ -147,6 +162,8 @@ class Layer:
         import segmented_rank_gemm_segment_amd as srg
         c = copy.copy(self)
         c.X, c.W = self.X.clone(), self.W.clone()
+        if self.Wq is not None:
+            c.Wq, c.ws = self.Wq.clone(), self.ws.clone()
         p = self.pool
         c.row_slot = self.row_slot.clone()
         c.pool = srg.Pool(p.A.clone(), p.Bt.clone(), p.slot_rank.clone(), self.alpha,
@@ -188,6 +205,16 @@ def k_expand(L):
     srg.lora_expand(L.H, L.seg, L.pool, L.Y)
 
 
+def k_fused_fp8w(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_linear_fused_fp8w(L.X, L.Wq, L.ws, L.H, L.seg, L.pool, L.Y)
+
+
+def k_base_fp8w(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_base_gemm_fp8w(L.X, L.Wq, L.ws, L.Y)
+
+
 def k_vendor_base(L):
     """The same X W^T through torch.matmul (the vendor BLAS): timed for
     comparison only, never part of a step."""
@@ -220,10 +247,11 @@ class _Overlap:
         k_expand(L)
 
 
-STEP = {"fused": (k_build_shrink, k_fused), "separate": (k_build_shrink, k_base, k_expand)}
+STEP = {"fused": (k_build_shrink, k_fused), "separate": (k_build_shrink, k_base, k_expand),
+        "fused_fp8w": (k_build_shrink, k_fused_fp8w)}
 PATHS = ("fused", "separate", "overlap")
 KNAME = {k_build: "build", k_shrink: "shrink", k_build_shrink: "build_shrink", k_fused: "fused",
-         k_base: "base", k_expand: "expand"}
+         k_base: "base", k_expand: "expand", k_fused_fp8w: "fused_fp8w", k_base_fp8w: "base_fp8w"}
 
 
 def _graph(fn_seq, layers, count, start=0):
@@ -275,9 +303,9 @@ def time_calls(fn_seq, layers, iters, warmup, use_graph):
 
 
 def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
-            device="cuda:0", vendor=False, dora=False):
+            device="cuda:0", vendor=False, dora=False, fp8w=False, kernels=None):
     import torch
-    L0 = Layer(w, policy, device, dora=dora)
+    L0 = Layer(w, policy, device, dora=dora, fp8w=fp8w)
     copies = max(1, int(np.ceil(rotate_mb * 1e6 / L0.nbytes)))
     layers = [L0] + [L0.clone(device) for _ in range(copies - 1)]
     for L in layers:                      # metadata/H valid for per-kernel loops
@@ -290,8 +318,9 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
         step[p] = time_calls(seq, layers, steps, warmup, use_graph)
     kl = kernel_loops or steps
     per_kernel = {}
-    for fn in sorted(set(STEP["fused"] + STEP["separate"] + (k_build, k_shrink)),
-                     key=lambda f: KNAME[f]):
+    if kernels is None:
+        kernels = STEP["fused"] + STEP["separate"] + (k_build, k_shrink)
+    for fn in sorted(set(kernels), key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
     res = {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
     if dora:
@@ -455,6 +484,24 @@ def dora_entry(w, fig, m, paths, args):
     }
 
 
+def fp8w_entry(w, fig, m, args):
+    """The headline workload with the base weight in FP8 E4M3 (one float32
+    scale per output row): the step (build + shrink, fused GEMM) and the
+    GEMM kernels against the bf16 weight's."""
+    mq = measure(w, ["fused_fp8w"], args.policy, args.steps, args.warmup, args.rotate_mb,
+                 args.kernel_loops, not args.eager, fp8w=True, kernels=(k_fused_fp8w, k_base_fp8w))
+    kt = kernel_table(fig, mq["per_kernel_s"], w.dtype)
+    st = mq["step"]["fused_fp8w"][0]
+    return {
+        "what": "same workload, base weight as E4M3 codes with a float32 scale per output row "
+                "(LoRA bf16 on the unquantized activations; paths add in fp32 before one rounding)",
+        "value": round(w.n / st, 1), "unit": "tokens/s", "step_us": round(st * 1e6, 3),
+        "step_vs_bf16": round(st / m["step"]["fused"][0], 4) if "fused" in m["step"] else None,
+        "kernels": kt,
+        "roofline": roofline_for("fused_fp8w", fig, mq["per_kernel_s"]["fused_fp8w"], w.dtype),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -555,6 +602,19 @@ def main():
                 "fused_us": round(md3["per_kernel_s"]["fused"] * 1e6, 3),
                 "fused_vs_plain": round(md3["per_kernel_s"]["fused"] / plain, 4),
                 "step_us": round(md3["step"]["fused"][0] * 1e6, 3)}
+            del w3
+    if not args.no_fp8w and w.dtype == "bf16":
+        out["fp8_weight"] = fp8w_entry(w, fig, m, args)
+        if "prefill" in out:
+            w3 = wl.make_config(3)
+            f3 = work_figures(w3)
+            st3 = max(5, args.steps // 10)
+            mq3 = measure(w3, ["fused_fp8w"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
+                          not args.eager, fp8w=True, kernels=(k_fused_fp8w,))
+            out["prefill"]["fp8_weight"] = {
+                "tokens_s": round(w3.n / mq3["step"]["fused_fp8w"][0], 1),
+                "fused_gemm": roofline_for("fused_fp8w", f3, mq3["per_kernel_s"]["fused_fp8w"], "bf16"),
+                "fused_us": round(mq3["per_kernel_s"]["fused_fp8w"] * 1e6, 3)}
             del w3
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -59,6 +59,12 @@ struct GemmArgs {
 #ifndef LORA_GEMM_LARGE
 #define LORA_GEMM_LARGE 256, 256, 2, 4, 64, 2, 1
 #endif
+#ifndef LORA_GEMM_SMALL_F8
+#define LORA_GEMM_SMALL_F8 LORA_GEMM_SMALL
+#endif
+#ifndef LORA_GEMM_LARGE_F8
+#define LORA_GEMM_LARGE_F8 LORA_GEMM_LARGE
+#endif
 #ifndef LORA_GEMM_SGB
 #define LORA_GEMM_SGB 1
 #endif
@@ -113,15 +119,14 @@ struct TileCfg {
 };
 
 // Eight E4M3 codes (bytes of lo, then hi; element e = byte e) to eight bf16
-// for the MFMA: every E4M3 value is exact in bf16, so this is exact.
+// for the MFMA, two per v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3
+// value is exact in bf16, so this is exact.
 __device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  return as_bf16x8(u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y),
-                         pack_bf16x2(d.x, d.y)});
+  return as_bf16x8(u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))});
 }
 
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
@@ -250,13 +255,19 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
             u32x4{0, 0, 0, 0};
   };
 
-  f32x16 acc[C::FM][C::FN];
+  // With FP8 weights the K loop of small tiles is bound by its arithmetic
+  // (fragment widening and MFMA), and a wave with a single 32x32 fragment
+  // would chain every MFMA on one accumulator; it keeps two instead (even
+  // and odd sub-steps) so that consecutive MFMAs are independent, and adds
+  // them after the K loop.  (The bf16 K loop is bound by its loads.)
+  constexpr bool DUAL = WF8 && C::FM * C::FN == 1;
+  f32x16 acc[C::FM][C::FN], acc2[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = acc2[i][j][v] = 0.f;
 
   // per-lane fragment offsets inside a stage (fragment rows start at
   // multiples of 32, so the swizzle of row base + (l & 31) depends on l only)
@@ -306,12 +317,16 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       }
     }
   };
-  auto mfmas = [&](int buf) __attribute__((always_inline)) {
+  auto mfmas = [&](int buf, bool odd) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < C::FN; ++j) {
+        if (DUAL && odd)
+          acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc2[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+      }
   };
   // interleave: one MFMA, then one LDS read, while reads remain
   auto interleave = [&]() __attribute__((always_inline)) {
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
       load_frags((kk + 1) & 1, st, kk + 1);
-      mfmas(kk & 1);
+      mfmas(kk & 1, kk & 1);
       interleave();
     }
     if (kt + 1 < KT) {
@@ -363,10 +378,21 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       if (q < C::FM * C::FN) {
         const int i = q / C::FN, j = q % C::FN;
         constexpr int b = (KK - 1) & 1;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc[i][j], 0, 0, 0);
+        if (DUAL && b)
+          acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc2[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc[i][j], 0, 0, 0);
       }
     }
     load_frags(KK & 1, smem + ((kt + 1) % STAGES) * C::STAGE, 0);
+  }
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] += acc2[i][j][v];
   }
 
   if constexpr (ROWEPI) {
@@ -803,8 +829,11 @@ hipError_t launch_bf16_w(const GemmArgs &g, bool lora, hipStream_t stream) {
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
 hipError_t launch_bf16(const GemmArgs &g, bool lora, hipStream_t stream) {
-  if (g.wscale) return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, true>(g, lora, stream);
   return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, false>(g, lora, stream);
+}
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
+hipError_t launch_fp8w(const GemmArgs &g, bool lora, hipStream_t stream) {
+  return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, true>(g, lora, stream);
 }
 
 }  // namespace
@@ -827,6 +856,10 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
       g.seg_scale = seg->seg_scale;
       g.r_max = pool->r_max;
       g.policy = pool->policy;
+    }
+    if (wscale) {
+      if (M <= LORA_GEMM_SMALL_M) return launch_fp8w<LORA_GEMM_SMALL_F8>(g, lora, stream);
+      return launch_fp8w<LORA_GEMM_LARGE_F8>(g, lora, stream);
     }
     if (M <= LORA_GEMM_SMALL_M) return launch_bf16<LORA_GEMM_SMALL>(g, lora, stream);
     return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
