@@ -19,6 +19,7 @@ from .lora_oracle import (  # noqa: F401
     gather_bmm_forward,
     per_adapter_forward,
     merged_forward,
+    stacked_forward,
     decode_fp8_e4m3,
     lora_forward_fp8w,
     dora_column_scale,

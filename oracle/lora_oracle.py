@@ -253,6 +253,27 @@ def merged_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype):
 
 
 # ---------------------------------------------------------------------------
+# stacked projections (fused QKV, stacked gate/up)
+# ---------------------------------------------------------------------------
+def stacked_forward(X, Ws, As, Bs, row_slot, slot_rank, slot_alpha, r_max: int, dtype: str,
+                    rows: Optional[Iterable[int]] = None):
+    """Several target projections of one input (adapter-batching page,
+    section "Adapter 不是一块连续 Weight": every target module has its own A
+    and B, and a model with fused QKV or stacked gate/up runs them as one
+    weight whose output concatenates the projections' outputs).  Projection
+    p has base weight Ws[p] [d_out_p, d_in] and adapter pools As[p]
+    [n_slots, r_max, d_in], Bs[p] [n_slots, d_out_p, r_max]; a slot's rank
+    and scale are shared by its projections.  Returns (Y, dY, H) with Y and
+    dY [rows, sum d_out_p] in projection order and H [rows, P * r_max]
+    (projection p's ranks at columns [p r_max, (p + 1) r_max))."""
+    outs = [lora_forward(X, W, A, B, row_slot, slot_rank, slot_alpha, r_max, dtype, rows=rows)
+            for W, A, B in zip(Ws, As, Bs)]
+    return (np.concatenate([o[0] for o in outs], axis=1),
+            np.concatenate([o[1] for o in outs], axis=1),
+            np.concatenate([o[2] for o in outs], axis=1))
+
+
+# ---------------------------------------------------------------------------
 # quantized base weight (FP8 E4M3 codes, one scale per output row)
 # ---------------------------------------------------------------------------
 # The adapter-batching page (section "Quantized Base Model 与 LoRA 的 Dtype
