@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 
@@ -99,10 +99,26 @@ typedef enum {
  * g row is all ones is a plain LoRA adapter and gives plain LoRA's bits.
  * Base-only rows and rank-0 slots are never rescaled.  g rows are written by
  * lora_pool_dora_prepare (and set to ones by lora_pool_pack_slot).
+ *
+ * Stacked projections (adapter-batching page, section "Adapter 不是一块连续
+ * Weight": every target module has its own A and B; a model with fused QKV
+ * or stacked gate/up runs them as one weight).  With n_proj = P >= 2 the
+ * pool serves P projections of the same input at once: output columns
+ * [proj_cols[q], proj_cols[q + 1]) are projection q's, and with
+ * rs = r_max / P, rank rows [q rs, q rs + r) of a slot are projection q's A
+ * rows; Bt rows [q rs, (q + 1) rs) are zero outside projection q's columns
+ * (the d_out-major B likewise).  A slot's rank r (<= rs) and scale are
+ * shared by its projections; H is [n][r_max] with projection q's ranks at
+ * columns [q rs, q rs + r).  Every call then computes, for each projection,
+ * exactly what it computes for a single one.  Requirements: proj_cols[0] =
+ * 0, proj_cols[P] = d_out, strictly increasing multiples of 8
+ * (LORA_ERR_SHAPE), rs in {8, 16, 32, 64} (LORA_ERR_RANK), proj_cols non-NULL
+ * (LORA_ERR_NULL).  lora_pool_pack_slot does not pack stacked pools
+ * (LORA_ERR_SHAPE).
  */
 typedef struct {
   int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
-  int32_t r_max;             /* 8, 16, 32 or 64 */
+  int32_t r_max;             /* 8, 16, 32 or 64 (times n_proj for stacked pools) */
   int32_t d_in;
   int32_t d_out;
   int32_t dtype;             /* lora_dtype */
@@ -113,6 +129,8 @@ typedef struct {
   const float *slot_scale;   /* device, [n_slots] */
   const void *B;             /* device, optional (NULL): [n_slots][d_out][r_max] */
   const float *dora_scale;   /* device, optional (NULL): fp32 [n_slots][d_out] DoRA g */
+  int32_t n_proj;            /* 0 or 1: one projection; 2..8: stacked projections */
+  const int32_t *proj_cols;  /* HOST, [n_proj + 1] column offsets (stacked pools only) */
 } lora_pool;
 
 /*

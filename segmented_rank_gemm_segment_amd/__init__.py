@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -49,6 +49,8 @@ class LoraPoolC(ctypes.Structure):
         ("slot_scale", ctypes.c_void_p),
         ("B", ctypes.c_void_p),
         ("dora_scale", ctypes.c_void_p),
+        ("n_proj", ctypes.c_int32),
+        ("proj_cols", ctypes.c_void_p),      # host int32 [n_proj + 1]
     ]
 
 
@@ -191,6 +193,7 @@ class Pool:
         self.d_out = Bt.shape[2]
         self.dora_scale = (torch.ones((self.n_slots, self.d_out), dtype=torch.float32,
                                       device=A.device) if dora else None)
+        self.proj_cols = None             # stacked projections: host int32 column offsets
         self.dtype = A.dtype
         self.slot_rank = slot_rank.to(device=A.device, dtype=torch.int32).contiguous()
         rank_host = self.slot_rank.cpu().to(torch.float64)
@@ -265,13 +268,56 @@ class Pool:
         if m is not None and m is not magnitude:
             m.record_stream(st)           # a copy made here: alive until read
 
+    @classmethod
+    def stacked(cls, pools, rank_policy: str = "exact", natural_b: bool = True,
+                dora: bool = False) -> "Pool":
+        """One pool serving several projections of the same input (fused QKV,
+        stacked gate/up): the projections' pools must agree on slots, r_max,
+        d_in, dtype, slot ranks and scales.  Projection q's A rows go to rank
+        rows [q r_max, (q + 1) r_max) of each slot, its Bt rows to the same
+        rank rows and its own output columns, zeros elsewhere (a layout
+        only).  The output columns are the projections' in order."""
+        p0 = pools[0]
+        P = len(pools)
+        if not 2 <= P <= 8:
+            raise ValueError("2..8 projections")
+        for p in pools:
+            if (p.n_slots, p.r_max, p.d_in, p.dtype) != (p0.n_slots, p0.r_max, p0.d_in, p0.dtype):
+                raise ValueError("projections must share n_slots, r_max, d_in and dtype")
+            if not torch.equal(p.slot_rank, p0.slot_rank) or not torch.equal(p.slot_scale,
+                                                                             p0.slot_scale):
+                raise ValueError("projections must share slot ranks and scales")
+        cols = [0]
+        for p in pools:
+            cols.append(cols[-1] + p.d_out)
+        rs, d_out = p0.r_max, cols[-1]
+        dev = p0.A.device
+        A = torch.cat([p.A for p in pools], dim=1).contiguous()         # [slots, P rs, d_in]
+        Bt = torch.zeros((p0.n_slots, P * rs, d_out), dtype=p0.dtype, device=dev)
+        for q, p in enumerate(pools):
+            Bt[:, q * rs:(q + 1) * rs, cols[q]:cols[q + 1]] = p.Bt
+        obj = cls.__new__(cls)
+        obj.A, obj.Bt = A, Bt
+        obj.B = Bt.transpose(1, 2).contiguous() if natural_b else None
+        obj.n_slots, obj.r_max, obj.d_in, obj.d_out = p0.n_slots, P * rs, p0.d_in, d_out
+        obj.dtype = p0.dtype
+        obj.slot_rank, obj.slot_scale = p0.slot_rank, p0.slot_scale
+        obj.dora_scale = (torch.ones((obj.n_slots, d_out), dtype=torch.float32, device=dev)
+                          if dora else None)
+        obj.generation = [0] * obj.n_slots
+        obj.proj_cols = (ctypes.c_int32 * (P + 1))(*cols)
+        obj.set_policy(rank_policy)
+        return obj
+
     def set_policy(self, rank_policy: str):
         self.rank_policy = rank_policy
+        P = 0 if self.proj_cols is None else len(self.proj_cols) - 1
         self._c = LoraPoolC(self.n_slots, self.r_max, self.d_in, self.d_out, _dtype_code(self.dtype),
                             RANK_POLICIES[rank_policy], self.A.data_ptr(), self.Bt.data_ptr(),
                             self.slot_rank.data_ptr(), self.slot_scale.data_ptr(),
                             self.B.data_ptr() if self.B is not None else None,
-                            self.dora_scale.data_ptr() if self.dora_scale is not None else None)
+                            self.dora_scale.data_ptr() if self.dora_scale is not None else None,
+                            P, ctypes.cast(self.proj_cols, ctypes.c_void_p) if P else None)
         return self
 
     @property

@@ -287,8 +287,8 @@ constexpr int kBSChunks = kBSMaxRows / kBSThreads;
 template <typename T>
 __global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, const T *X,
                                                                   int64_t ldx, const T *A,
-                                                                  int d_in, int policy, int nkb,
-                                                                  float *H) {
+                                                                  int d_in, int policy, int r_max,
+                                                                  int nkb, float *H) {
   extern __shared__ int lds[];
   if (blockIdx.x == 0) {
     build_segments_block(a, lds);
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, c
   const int kb = b % nkb;
   const int slot = (b / nkb) % a.n_slots;
   const int rb = b / (nkb * a.n_slots);
-  const int k0 = kb * kShRB;
+  const int k0 = kb * kShRB;              // rank row of the pool (a.r_max = rank bound)
+  const int kl0 = k0 % a.r_max;           // ... and inside its projection's block
   float (*s_part)[kShNP] = reinterpret_cast<float (*)[kShNP]>(lds);
   int *s_wc = lds + kShW * kShNP;
   int *s_rows = s_wc + kShW;                // [n]
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, c
   }
   if (r < 1 || r > a.r_max) return;         // rank-0 slot, or rows demoted by the build
   const int R = rank_bucket(r, policy, a.r_max);
-  if (k0 >= R) return;
+  if (kl0 >= R) return;
   // rows of the slot in ascending order
   int cnt = 0;
 #pragma unroll
@@ -336,8 +337,8 @@ __global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, c
   }
   const int p0 = rb * kRowBlk, p1 = min(cnt, p0 + kRowBlk);
   if (p0 >= p1) return;
-  shrink_rows<T>(X, ldx, A, slot, k0, min(kShRB, R - k0), r, a.r_max, d_in, s_rows, p0, p1, H,
-                 s_part);
+  shrink_rows<T>(X, ldx, A, slot, k0, kl0, min(kShRB, R - kl0), r, r_max, d_in, s_rows, p0, p1,
+                 H, s_part);
 }
 
 }  // namespace
@@ -355,11 +356,11 @@ hipError_t launch_build_shrink(const BuildArgs &a, const void *X, int64_t ldx,
   if (pool.dtype == 1)
     hipLaunchKernelGGL(build_shrink_kernel<bf16_t>, dim3((unsigned)blocks), dim3(kBSThreads), lds,
                        stream, a, (const bf16_t *)X, ldx, (const bf16_t *)pool.A, pool.d_in,
-                       pool.policy, nkb, H);
+                       pool.policy, pool.r_max, nkb, H);
   else
     hipLaunchKernelGGL(build_shrink_kernel<float>, dim3((unsigned)blocks), dim3(kBSThreads), lds,
                        stream, a, (const float *)X, ldx, (const float *)pool.A, pool.d_in,
-                       pool.policy, nkb, H);
+                       pool.policy, pool.r_max, nkb, H);
   return hipGetLastError();
 }
 

@@ -30,17 +30,21 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void dora_prepare_kernel(
     const T *__restrict__ W, int64_t ldw, const T *__restrict__ A, const T *__restrict__ Bt,
     const int32_t *__restrict__ slot_rank, const float *__restrict__ slot_scale, int slot,
-    int r_max, int d_in, int d_out, const float *__restrict__ magnitude, float *__restrict__ g) {
+    int r_max, int d_in, int d_out, const float *__restrict__ magnitude, float *__restrict__ g,
+    ProjView proj) {
   constexpr int V = Elem<T>::kVec;
   __shared__ float s_b[kRows][64];
   __shared__ float s_red[kThreads / kWave][kRows];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * kRows;
   int r = slot_rank[slot];
-  r = (r < 0 || r > r_max) ? 0 : r;
+  r = (r < 0 || r > proj.rs) ? 0 : r;
   const float sc = r > 0 ? slot_scale[slot] : 0.f;
-  const T *a_slot = A + (int64_t)slot * r_max * d_in;
-  const T *bt_slot = Bt + (int64_t)slot * r_max * d_out;
+  // the workgroup's output features belong to one projection (offsets are
+  // multiples of 8): its rank rows start at qoff
+  const int qoff = proj_of(proj, j0) * proj.rs;
+  const T *a_slot = A + ((int64_t)slot * r_max + qoff) * d_in;
+  const T *bt_slot = Bt + ((int64_t)slot * r_max + qoff) * d_out;
   // B_a[j0 + jj][k] for k < r (Bt row k is column k of B_a)
   for (int it = tid; it < kRows * 64; it += kThreads) {
     const int jj = it / 64, k = it - (it / 64) * 64;
@@ -108,12 +112,12 @@ hipError_t launch_dora_prepare(const PoolView &pool, const int32_t *slot_rank,
     hipLaunchKernelGGL(dora_prepare_kernel<bf16_t>, grid, dim3(kThreads), 0, stream,
                        (const bf16_t *)W, ldw, (const bf16_t *)pool.A, (const bf16_t *)pool.Bt,
                        slot_rank, slot_scale, slot, pool.r_max, pool.d_in, pool.d_out, magnitude,
-                       g);
+                       g, pool.proj);
   else
     hipLaunchKernelGGL(dora_prepare_kernel<float>, grid, dim3(kThreads), 0, stream,
                        (const float *)W, ldw, (const float *)pool.A, (const float *)pool.Bt,
                        slot_rank, slot_scale, slot, pool.r_max, pool.d_in, pool.d_out, magnitude,
-                       g);
+                       g, pool.proj);
   return hipGetLastError();
 }
 

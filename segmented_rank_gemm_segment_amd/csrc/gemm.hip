@@ -48,6 +48,7 @@ struct GemmArgs {
   int r_max, policy;
   const float *dora;   // optional DoRA column factors ([slot][N]) or null
   const float *wscale; // FP8 weight: one scale per output row (W then holds E4M3 codes)
+  ProjView proj;       // projections of the output columns (one unless stacked)
 };
 
 // Tile configurations <BM, BN, waves along M, waves along N, K per group
@@ -447,10 +448,13 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
     if constexpr (LORA != 0) {
       if (live && e_r > 0) {
-        const bf16_t *bt = g.Bt + (int64_t)e_slot * g.r_max * N + gcol;
-        const float *hp = g.H + (int64_t)grow * g.r_max;
+        // the 8 columns' projection: its rank rows start at qoff (offsets of
+        // projections are multiples of 8, so all 8 columns share it)
+        const int qoff = proj_of(g.proj, gcol) * g.proj.rs;
+        const bf16_t *bt = g.Bt + ((int64_t)e_slot * g.r_max + qoff) * N + gcol;
+        const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
         float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int kc = 0; kc < e_r; kc += 8) {      // kc + 8 <= r_max: in the slot
+        for (int kc = 0; kc < e_r; kc += 8) {      // kc + 8 <= rs: in the block
           const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
           const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
           const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
@@ -582,18 +586,26 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       const int slot = g.seg_slot[u];
       const int r = g.seg_rank[u];
       const float sc = g.seg_scale[u];
-      const int R = rank_bucket(r, g.policy, g.r_max);
+      const int rs = g.proj.rs;
+      const int R = rank_bucket(r, g.policy, rs);
       const int KS = (R + 15) / 16;
       const int NC = 2 * KS;                          // 16-byte chunks per staged row
+      // one pass per projection among the tile's columns (one unless the
+      // pool stacks projections and the tile straddles two): projection q's
+      // rank rows start at qoff, and columns outside it stage zeros
+      const int q_lo = proj_of(g.proj, n0), q_hi = proj_of(g.proj, min(n0 + BN, N) - 1);
+      for (int q = q_lo; q <= q_hi; ++q) {
+      const int qoff = q * rs;
+      const int c_lo = g.proj.col_off[q], c_hi = g.proj.col_off[q + 1];
       // A: (row, chunk) items
       for (int it = tid; it < BM * NC; it += C::T) {
         const int row = it / NC, c = it - (it / NC) * NC;
         const int grow = m0 + row;
         float h[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         const bool in_u = grow < M && g.row_segment[grow] == u;
-        // chunks past r_max (k >= R >= r, only when r_max = 8) stay zero
-        if (in_u && c * 8 < g.r_max) {
-          const float *hp = g.H + (int64_t)grow * g.r_max + c * 8;
+        // chunks past rs (k >= R >= r, only when rs = 8) stay zero
+        if (in_u && c * 8 < rs) {
+          const float *hp = g.H + (int64_t)grow * g.r_max + qoff + c * 8;
           const float4 h0 = *reinterpret_cast<const float4 *>(hp);
           const float4 h1 = *reinterpret_cast<const float4 *>(hp + 4);
           h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
@@ -618,14 +630,15 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
         for (int it = tid; it < BN * NC; it += C::T) {
           const int col = it / NC, c = it - (it / NC) * NC;
           const int colc = min(n0 + col, N - 1);     // columns past N: never stored
-          // a chunk past r_max (only when r_max = 8) is read from the
-          // column's first chunk and masked below
-          u32x4 v = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max +
-                                                      min(c * 8, g.r_max - 8));
+          const bool in_q = colc >= c_lo && colc < c_hi;
+          // a chunk past rs (only when rs = 8) is read from the block's
+          // first chunk and masked below
+          u32x4 v = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max + qoff +
+                                                      min(c * 8, rs - 8));
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const int k = c * 8 + e2 * 2;
-            v[e2] &= (k < r ? 0x0000ffffu : 0u) | (k + 1 < r ? 0xffff0000u : 0u);
+            v[e2] &= in_q ? ((k < r ? 0x0000ffffu : 0u) | (k + 1 < r ? 0xffff0000u : 0u)) : 0u;
           }
           *reinterpret_cast<u32x4 *>(s_b + col * RBL + sw(c, col)) = v;
         }
@@ -638,7 +651,8 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           const int k = it / CC, cc = it - (it / CC) * CC;
           const int col0 = n0 + cc * 8;
           u32x4 v = u32x4{0, 0, 0, 0};
-          if (k < r) v = *reinterpret_cast<const u32x4 *>(bt + (int64_t)k * N + min(col0, N - 8));
+          if (k < r && col0 >= c_lo && col0 < c_hi)
+            v = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(qoff + k) * N + min(col0, N - 8));
           const int c = k >> 3, kin = k & 7;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -676,8 +690,9 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           }
         }
       }
-      // the staging area is rewritten for the next segment
+      // the staging area is rewritten for the next projection or segment
       lgkm_barrier();
+      }
     }
   }
 
@@ -736,6 +751,7 @@ struct GemmF32Args {
   const float *seg_scale;
   int r_max;
   const float *dora;
+  ProjView proj;
 };
 
 template <bool LORA>
@@ -788,8 +804,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
         for (int j = 0; j < 4; ++j) {
           const int col = n0 + tx * 4 + j;
           if (col >= g.N) continue;
+          const int qoff = proj_of(g.proj, col) * g.proj.rs;
           float d = 0.f;
-          for (int k = 0; k < r; ++k) d = fmaf(hrow[k], bt[(int64_t)k * g.N + col], d);
+          for (int k = 0; k < r; ++k)
+            d = fmaf(hrow[qoff + k], bt[(int64_t)(qoff + k) * g.N + col], d);
           acc[i][j] += sc * d;
           if (g.dora) acc[i][j] *= g.dora[(int64_t)g.seg_slot[s] * g.N + col];
         }
@@ -846,7 +864,11 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
   if (dtype == 1) {
     GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
                H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, wscale};
+    g.proj.n_proj = 1;
+    g.proj.rs = 64;
+    for (int q = 0; q <= kMaxProj; ++q) g.proj.col_off[q] = q ? N : 0;
     if (lora) {
+      g.proj = pool->proj;
       g.Bt = (const bf16_t *)pool->Bt;
       g.Bn = (const bf16_t *)pool->B;
       g.dora = pool->dora;
@@ -866,7 +888,11 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
   }
   GemmF32Args g{(const float *)X, ldx, (const float *)W, ldw, (float *)Y, ldy, M, K, N,
                 H, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+  g.proj.n_proj = 1;
+  g.proj.rs = 64;
+  for (int q = 0; q <= kMaxProj; ++q) g.proj.col_off[q] = q ? N : 0;
   if (lora) {
+    g.proj = pool->proj;
     g.Bt = (const float *)pool->Bt;
     g.dora = pool->dora;
     g.row_segment = seg->row_segment;

@@ -15,11 +15,31 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_dtype(int32_t d) { return d == LORA_F32 || d == LORA_BF16; }
 
+bool valid_rank_width(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+
+// Per-projection rank stride of a pool (r_max for a single projection).
+int32_t pool_rs(const lora_pool *pool) {
+  return pool->n_proj >= 2 ? pool->r_max / pool->n_proj : pool->r_max;
+}
+
+lora_status check_proj(const lora_pool *pool) {
+  if (pool->n_proj < 0 || pool->n_proj > lora::kMaxProj) return LORA_ERR_SHAPE;
+  if (pool->n_proj <= 1) return valid_rank_width(pool->r_max) ? LORA_OK : LORA_ERR_RANK;
+  if (pool->r_max % pool->n_proj || !valid_rank_width(pool->r_max / pool->n_proj))
+    return LORA_ERR_RANK;
+  if (!pool->proj_cols) return LORA_ERR_NULL;
+  if (pool->proj_cols[0] != 0 || pool->proj_cols[pool->n_proj] != pool->d_out) return LORA_ERR_SHAPE;
+  for (int q = 0; q < pool->n_proj; ++q)
+    if (pool->proj_cols[q + 1] <= pool->proj_cols[q] || pool->proj_cols[q + 1] % 8)
+      return LORA_ERR_SHAPE;
+  return LORA_OK;
+}
+
 lora_status check_pool(const lora_pool *pool) {
   if (!pool) return LORA_ERR_NULL;
   if (!valid_dtype(pool->dtype)) return LORA_ERR_DTYPE;
-  if (pool->r_max != 8 && pool->r_max != 16 && pool->r_max != 32 && pool->r_max != 64)
-    return LORA_ERR_RANK;
+  lora_status st = check_proj(pool);
+  if (st != LORA_OK) return st;
   if (pool->rank_policy < LORA_RANK_EXACT || pool->rank_policy > LORA_RANK_PADDED)
     return LORA_ERR_POLICY;
   if (pool->n_slots < 1 || pool->n_slots > LORA_MAX_SLOTS) return LORA_ERR_SHAPE;
@@ -63,8 +83,15 @@ lora::SegView seg_view(const lora_segments *s) {
 }
 
 lora::PoolView pool_view(const lora_pool *p) {
-  return lora::PoolView{p->n_slots, p->r_max, p->d_in, p->d_out, p->dtype, p->rank_policy,
-                        p->A,       p->Bt,      p->B,      p->dora_scale};
+  lora::PoolView v{p->n_slots, p->r_max, p->d_in, p->d_out, p->dtype, p->rank_policy,
+                   p->A,       p->Bt,      p->B,      p->dora_scale, {}};
+  v.proj.n_proj = p->n_proj >= 2 ? p->n_proj : 1;
+  v.proj.rs = pool_rs(p);
+  for (int q = 0; q <= lora::kMaxProj; ++q)
+    v.proj.col_off[q] = q <= v.proj.n_proj ? (v.proj.n_proj == 1 ? (q ? p->d_out : 0)
+                                                                   : p->proj_cols[q])
+                                           : p->d_out;
+  return v;
 }
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
@@ -98,7 +125,7 @@ lora_status lora_build_segments(const int32_t *row_slot, const lora_pool *pool,
   if (st != LORA_OK) return st;
   if (seg->n_rows > 0 && !row_slot) return LORA_ERR_NULL;
   return hip_status(lora::launch_build_segments(
-      row_slot, seg->n_rows, pool->n_slots, pool->r_max, pool->slot_rank, pool->slot_scale,
+      row_slot, seg->n_rows, pool->n_slots, pool_rs(pool), pool->slot_rank, pool->slot_scale,
       seg->token_indices, seg->row_segment, seg->segment_offsets, seg->segment_slots,
       seg->segment_ranks, seg->segment_scales, seg->num_segments, seg->status,
       static_cast<hipStream_t>(stream)));
@@ -120,7 +147,7 @@ lora_status lora_build_shrink(const int32_t *row_slot, const void *X, int64_t ld
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const lora::BuildArgs a{row_slot,           seg->n_rows,         pool->n_slots,
-                          pool->r_max,        pool->slot_rank,     pool->slot_scale,
+                          pool_rs(pool),      pool->slot_rank,     pool->slot_scale,
                           seg->token_indices, seg->row_segment,    seg->segment_offsets,
                           seg->segment_slots, seg->segment_ranks,  seg->segment_scales,
                           seg->num_segments,  seg->status};
@@ -168,6 +195,7 @@ lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t ran
                                 void *stream) {
   lora_status st = check_pool(pool);
   if (st != LORA_OK) return st;
+  if (pool->n_proj >= 2) return LORA_ERR_SHAPE;   // stacked pools are laid out by the caller
   if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SHAPE;
   if (rank < 0 || rank > pool->r_max) return LORA_ERR_SHAPE;
   if (rank > 0) {

@@ -18,13 +18,32 @@ struct SegView {
   const int32_t *num_segments;
 };
 
+constexpr int kMaxProj = 8;
+
+// Stacked projections: output columns [col_off[q], col_off[q + 1]) belong
+// to projection q, whose rank rows are [q * rs, q * rs + rank) of a slot
+// (rs = r_max / n_proj).  One projection: n_proj = 1, rs = r_max.
+struct ProjView {
+  int n_proj, rs;
+  int col_off[kMaxProj + 1];
+};
+
 struct PoolView {
   int n_slots, r_max, d_in, d_out, dtype, policy;
   const void *A;
   const void *Bt;
   const void *B;   // optional d_out-major copy of B ([n_slots][d_out][r_max]) or null
   const float *dora;   // optional DoRA column factors ([n_slots][d_out]) or null
+  ProjView proj;
 };
+
+// Projection of output column col (col < col_off[n_proj]).
+__host__ __device__ inline int proj_of(const ProjView &pv, int col) {
+  int q = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i) q += (i < pv.n_proj && col >= pv.col_off[i]) ? 1 : 0;
+  return q;
+}
 
 struct BuildArgs {
   const int32_t *row_slot;

@@ -44,10 +44,11 @@ template <typename T>
 __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
-    const int32_t *num_segments, int r_max, int d_in, int policy, int seg_cap,
+    const int32_t *num_segments, int r_max, int rs, int d_in, int policy, int seg_cap,
     int cap_items, int long_min, float *__restrict__ H) {
   __shared__ float s_part[kShW][kShNP];
-  const int k0 = blockIdx.x * kShRB;
+  const int k0 = blockIdx.x * kShRB;       // rank row of the pool
+  const int kl0 = k0 % rs;                 // ... and inside its projection's block
   // items are ordered block-major (item = b * seg_cap + s): the first row
   // block of every segment comes first, so launch-order work is real work
   // and later (mostly empty) blocks cost one metadata read each
@@ -57,14 +58,14 @@ __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
     // s < capacity keeps the metadata read in bounds before S is known
     const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, nullptr);
     if (s >= m.S) continue;
-    const int R = rank_bucket(m.r, policy, r_max);
-    if (k0 >= R) continue;
+    const int R = rank_bucket(m.r, policy, rs);
+    if (kl0 >= R) continue;
     if (m.o1 - m.o0 >= long_min) continue;   // long segment: tiled MFMA kernel
     const int p0 = m.o0 + b * kRowBlk;
     const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
-    shrink_rows<T>(X, ldx, A, m.slot, k0, min(kShRB, R - k0), m.r, r_max, d_in, token_indices,
-                   p0, p1, H, s_part);
+    shrink_rows<T>(X, ldx, A, m.slot, k0, kl0, min(kShRB, R - kl0), m.r, r_max, d_in,
+                   token_indices, p0, p1, H, s_part);
   }
 }
 
@@ -84,8 +85,8 @@ constexpr int kSM = 64, kSN = 64, kSStages = 6;
 __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
     const bf16_t *__restrict__ X, int64_t ldx, const bf16_t *__restrict__ A,
     const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
-    const int32_t *seg_rank, const int32_t *num_segments, int r_max, int d_in, int policy,
-    int tiles_per_seg, int cap_items, float *__restrict__ H) {
+    const int32_t *seg_rank, const int32_t *num_segments, int r_max, int rs, int d_in, int policy,
+    int tiles_per_seg, int rank_tiles, int cap_items, float *__restrict__ H) {
   constexpr int NW = 4;
   constexpr int AI = kSM / 8 / NW, BI = kSN / 8 / NW, IPW = AI + BI;
   constexpr int STAGE = (kSM + kSN) * 128;
@@ -116,13 +117,16 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
   const int S = *num_segments;
 
   for (int item = blockIdx.x; item < cap_items; item += gridDim.x) {
-    const int s = item / tiles_per_seg;
-    const int t = item - s * tiles_per_seg;
+    // item = (segment, row tile, rank tile of 64 pool rank rows)
+    const int s = item / (tiles_per_seg * rank_tiles);
+    const int rem = item - s * (tiles_per_seg * rank_tiles);
+    const int t = rem / rank_tiles;
+    const int rt = rem - t * rank_tiles;
     const int r = seg_rank[s];
     const int o0 = seg_off[s], o1 = seg_off[s + 1];
     const int slot = seg_slot[s];
     if (s >= S) break;
-    const int R = rank_bucket(r, policy, r_max);
+    const int R = rank_bucket(r, policy, rs);
     if (R == 0 || o1 - o0 < kLongRows) continue;
     const int p0 = o0 + t * kSM;
     if (p0 >= o1) continue;
@@ -137,7 +141,12 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-      const int k = min((wid * BI + i) * 8 + r8, R - 1);
+      // pool rank row kg, kl rows into its projection's block; rows past the
+      // processed width R re-read the block's last processed row (in the
+      // slot) and are not stored
+      const int kg = rt * kSN + (wid * BI + i) * 8 + r8;
+      const int kl = kg % rs;
+      const int k = min(kl < R ? kg : kg - kl + R - 1, r_max - 1);
       bsrc[i] = A + ((int64_t)slot * r_max + k) * d_in + blc[i] * 8;
     }
     auto issue = [&](int stage, int k0) {
@@ -177,11 +186,12 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
       }
     }
-    const int k = wn * 32 + (l & 31);
+    const int k = rt * kSN + wn * 32 + (l & 31);
+    const bool kok = k < r_max && k % rs < r;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int p = p0 + wm * 32 + acc_row(v, l);
-      if (p < p1 && k < r) H[(int64_t)token_indices[p] * r_max + k] = acc[v];
+      if (p < p1 && kok) H[(int64_t)token_indices[p] * r_max + k] = acc[v];
     }
     lgkm_barrier();  // the next item's loads reuse the stages
   }
@@ -204,7 +214,7 @@ template <typename T, int R, bool DORA>
 __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T *bt,
                                             const float *gp, int d_out, bool active, int r,
                                             float sc, int p0, int p1,
-                                            const int32_t *token_indices, int r_max, T *Y,
+                                            const int32_t *token_indices, int r_max, int rs, T *Y,
                                             int64_t ldy, int col, int lane) {
   constexpr int V = Elem<T>::kVec;
   constexpr int NB = (R + 15) / 16;   // rank blocks of 4 per lane (at most)
@@ -226,7 +236,7 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
       // would; rows past the block are clamped into the slot.  Values are
       // masked where they are used (rank rows >= r) and inactive columns
       // are never stored.
-      braw[jb][e] = ldg16(bt + (int64_t)min(k0 + e, r_max - 1) * d_out);
+      braw[jb][e] = ldg16(bt + (int64_t)min(k0 + e, rs - 1) * d_out);
     }
   }
   // DoRA column factors of the lane's V columns (same for every row)
@@ -265,7 +275,7 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
         // block start k0 < R <= r_max and r_max % 8 == 0: the float4 is in
         // the row; blocks past R read the row's last float4 and are zeroed
         // (masked where used, by the same rank test as the adapter rows)
-        const int k0 = min(4 * (kq + 4 * jb), r_max - 4);
+        const int k0 = min(4 * (kq + 4 * jb), rs - 4);
         hv[q][jb] = *reinterpret_cast<const float4 *>(H + (int64_t)rows[q] * r_max + k0);
       }
     __builtin_amdgcn_sched_barrier(0);   // Y and H loads issued before any use
@@ -344,12 +354,16 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     const float *__restrict__ H, const T *__restrict__ Bt, const float *__restrict__ dora,
     const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
     const int32_t *seg_rank, const float *seg_scale, const int32_t *num_segments, int r_max,
-    int d_out, int policy, int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy) {
+    int d_out, int policy, int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy,
+    ProjView proj) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int col = ((blockIdx.x * kExpWaves + wave) * 16 + (lane & 15)) * V;
   const bool active = col < d_out;
+  // the lane's columns belong to one projection (its offsets are multiples
+  // of 8): its rank rows start at q * rs in the slot and in H
+  const int qoff = proj_of(proj, active ? col : 0) * proj.rs;
   // block-major items (item = b * seg_cap + s), as in the shrink
   for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
     const int b = item / seg_cap;
@@ -359,25 +373,27 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     if (s >= m.S) continue;
     const int r = m.r, slot = m.slot;
     const float sc = m.sc;
-    const int R = rank_bucket(r, policy, r_max);
+    const int R = rank_bucket(r, policy, proj.rs);
     if (R == 0) continue;
     const int p0 = m.o0 + b * kRowBlk;
     const int p1 = min(m.o1, p0 + kRowBlk);
     if (p0 >= p1) continue;
-    const T *bt = Bt + (int64_t)slot * r_max * d_out + (active ? col : 0);
+    const T *bt = Bt + ((int64_t)slot * r_max + qoff) * d_out + (active ? col : 0);
     const float *gp = DORA ? dora + (int64_t)slot * d_out + (active ? col : 0) : nullptr;
+    const float *Hq = H + qoff;   // the projection's ranks in each H row
+    const int rs = proj.rs;
     if (R == 8) {
-      expand_item<T, 8, DORA>(H, bt, gp, d_out, active, r, sc, p0, p1, token_indices, r_max, Y,
-                              ldy, col, lane);
+      expand_item<T, 8, DORA>(Hq, bt, gp, d_out, active, r, sc, p0, p1, token_indices, r_max, rs,
+                              Y, ldy, col, lane);
     } else if (RMAX >= 16 && R == 16) {
-      expand_item<T, (RMAX >= 16 ? 16 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
-                                                  token_indices, r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 16 ? 16 : 8), DORA>(Hq, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, rs, Y, ldy, col, lane);
     } else if (RMAX >= 32 && R == 32) {
-      expand_item<T, (RMAX >= 32 ? 32 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
-                                                  token_indices, r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 32 ? 32 : 8), DORA>(Hq, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, rs, Y, ldy, col, lane);
     } else if (RMAX >= 64) {
-      expand_item<T, (RMAX >= 64 ? 64 : 8), DORA>(H, bt, gp, d_out, active, r, sc, p0, p1,
-                                                  token_indices, r_max, Y, ldy, col, lane);
+      expand_item<T, (RMAX >= 64 ? 64 : 8), DORA>(Hq, bt, gp, d_out, active, r, sc, p0, p1,
+                                                  token_indices, r_max, rs, Y, ldy, col, lane);
     }
   }
 }
@@ -422,23 +438,26 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
     hipLaunchKernelGGL((shrink_kernel<bf16_t>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min, H);
+                       pool.proj.rs, pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min,
+                       H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
                        seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min, H);
+                       pool.proj.rs, pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min,
+                       H);
   }
   if (use_mfma) {
     const int tps = (n + kSM - 1) / kSM;
-    // one workgroup per (segment, tile) item up to 2048, so a workgroup
-    // walks at most a few (mostly empty) items
-    const int items = S_bound * tps;
+    const int nrt = (pool.r_max + kSN - 1) / kSN;   // rank tiles of 64 pool rank rows
+    // one workgroup per (segment, row tile, rank tile) item up to 2048, so a
+    // workgroup walks at most a few (mostly empty) items
+    const int items = S_bound * tps * nrt;
     const int g = items < 2048 ? items : 2048;
     hipLaunchKernelGGL(shrink_mfma_kernel, dim3(g), dim3(4 * kWave), 0, stream, (const bf16_t *)X,
                        ldx, (const bf16_t *)pool.A, seg.token_indices, seg.seg_off, seg.seg_slot,
-                       seg.seg_rank, seg.num_segments, pool.r_max, pool.d_in, pool.policy, tps,
-                       S_bound * tps, H);
+                       seg.seg_rank, seg.num_segments, pool.r_max, pool.proj.rs, pool.d_in,
+                       pool.policy, tps, nrt, S_bound * tps * nrt, H);
   }
   return hipGetLastError();
 }
@@ -454,18 +473,18 @@ void launch_expand_t(const float *H, const SegView &seg, const PoolView &pool, v
     hipLaunchKernelGGL((expand_kernel<T, RMAX, true>), grid, dim3(kExpWaves * kWave), 0, stream,
                        H, (const T *)pool.Bt, pool.dora, seg.token_indices, seg.seg_off,
                        seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
-                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
+                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy, pool.proj);
   else
     hipLaunchKernelGGL((expand_kernel<T, RMAX, false>), grid, dim3(kExpWaves * kWave), 0, stream,
                        H, (const T *)pool.Bt, nullptr, seg.token_indices, seg.seg_off,
                        seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
-                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy);
+                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy, pool.proj);
 }
 
 template <typename T>
 void launch_expand_r(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
                      int bps, int S_bound, int real_bound, hipStream_t stream) {
-  switch (pool.r_max) {
+  switch (pool.proj.rs) {
     case 8: launch_expand_t<T, 8>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
     case 16: launch_expand_t<T, 16>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
     case 32: launch_expand_t<T, 32>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;

@@ -54,12 +54,15 @@ __device__ __forceinline__ void butterfly_reduce(float (&v)[N], int lane) {
 
 // Rows rows[p0 .. p1) (original row indices; global or LDS memory) against
 // rank rows k0 .. k0 + nk of `slot` (nk <= kShRB rows inside the processed
-// width, so inside the slot); H entries with k >= r are not written.  Called
-// by every thread of a kShW-wave workgroup (it passes barriers).
+// width, so inside the slot); k0 is kl0 rows into its projection's rank
+// block, and H entries of rank rows at or past the rank r in that block are
+// not written.  Called by every thread of a kShW-wave workgroup (it passes
+// barriers).
 template <typename T>
 __device__ __forceinline__ void shrink_rows(const T *__restrict__ X, int64_t ldx,
-                                            const T *__restrict__ A, int slot, int k0, int nk,
-                                            int r, int r_max, int d_in, const int32_t *rows,
+                                            const T *__restrict__ A, int slot, int k0, int kl0,
+                                            int nk, int r, int r_max, int d_in,
+                                            const int32_t *rows,
                                             int p0, int p1, float *__restrict__ H,
                                             float (*s_part)[kShNP]) {
   constexpr int V = Elem<T>::kVec;
@@ -127,7 +130,7 @@ __device__ __forceinline__ void shrink_rows(const T *__restrict__ X, int64_t ldx
 #pragma unroll
       for (int w = 1; w < kShW; ++w) t += s_part[w][threadIdx.x];
       const int row = __shfl(tv, q);
-      if (q < nq && k0 + kk < r) H[(int64_t)row * r_max + k0 + kk] = t;
+      if (q < nq && kl0 + kk < r) H[(int64_t)row * r_max + k0 + kk] = t;
     }
     __syncthreads();   // s_part is rewritten by the next group
   }

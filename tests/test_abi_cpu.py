@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 3
+    assert L.lora_abi_version() == srg.ABI_VERSION == 4
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
@@ -211,6 +211,43 @@ def test_fp8_weight_validation(L):
     assert f(X, 64, W, 64, S, None, sg, p, Y, 32, None) == ENULL
     assert f(X, 64, W, 72, S, H, sg, p, Y, 32, None) == EALIGN
     assert f(X, 64, W, 64, S, H, sg, ctypes.byref(pool(d_in=40)), Y, 32, None) == EALIGN
+
+
+def _cols(*v):
+    arr = (ctypes.c_int32 * len(v))(*v)
+    _cols.keep.append(arr)               # the pool struct points at it (host memory)
+    return ctypes.cast(arr, ctypes.c_void_p).value
+
+
+_cols.keep = []
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_proj=3, r_max=48, d_out=48), None),              # valid: rs 16, columns below
+    (dict(n_proj=2, r_max=48, d_out=48), ERANK),             # rs = 24
+    (dict(n_proj=3, r_max=48, d_out=48, proj_cols=0), ENULL),
+    (dict(n_proj=9, r_max=72, d_out=48), ESHAPE),
+    (dict(n_proj=-1), ESHAPE),
+])
+def test_stacked_pool_validation(L, kw, code):
+    d = dict(kw)
+    if "proj_cols" not in d:
+        d["proj_cols"] = _cols(0, 16, 24, 48)
+    p = pool(**d)
+    # an empty batch: a valid pool returns OK without launching anything
+    empty = segs(n_rows=0, max_segments=0, token_indices=0, row_segment=0)
+    assert shrink(L, p, empty, X=0, H=0) == (OK if code is None else code)
+
+
+@pytest.mark.parametrize("cols", [(0, 16, 20, 48), (0, 24, 16, 48), (0, 16, 24, 40), (8, 16, 24, 48)])
+def test_stacked_pool_column_offsets(L, cols):
+    p = pool(n_proj=3, r_max=48, d_out=48, proj_cols=_cols(*cols))
+    assert shrink(L, p, segs()) == ESHAPE
+
+
+def test_stacked_pool_is_not_packed(L):
+    p = ctypes.byref(pool(n_proj=3, r_max=48, d_out=48, proj_cols=_cols(0, 16, 24, 48)))
+    assert L.lora_pool_pack_slot(p, 0, 8, 2.0, P + 0xC000, 64, P + 0xD000, 8, None) == ESHAPE
 
 
 def test_expand_and_fused_validation(L):
