@@ -18,6 +18,8 @@ Prints one JSON line (rank 0; one GPU):
   dora       = the same step with every slot a DoRA adapter (column factors
                in the epilogue), and the per-adapter factor preparation
   fp8_weight = the same step with the base weight in FP8 E4M3 (per-row scale)
+  layer_70b  = the 70B-shaped layer's seven projections per step, one call
+               pair each or with q|k|v and gate|up stacked
   cpu_baseline = the float64 CPU oracle on a bounded sample of the headline
                workload, on this host's cores
 
@@ -63,6 +65,8 @@ def parse():
                    help="skip the DoRA variant (column factors in the epilogue)")
     p.add_argument("--no-fp8w", action="store_true",
                    help="skip the FP8-weight variant of the base product")
+    p.add_argument("--no-layer", action="store_true",
+                   help="skip the 70B-shaped layer (seven projections, separate vs stacked)")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the base product through torch.matmul for comparison")
     p.add_argument("--eager", action="store_true",
@@ -502,6 +506,69 @@ def fp8w_entry(w, fig, m, args):
     }
 
 
+def layer_entry(args, device="cuda:0"):
+    """The 70B-shaped layer (q, k, v, o, gate, up, down; 2304 rows: a 2048-row
+    prefill chunk and 256 decode rows; 64 slots of rank 16 or 64).  q, k, v
+    share one input, gate and up another.  One step computes all seven
+    projections with one metadata build: either seven shrink + fused GEMM
+    pairs, or four with q|k|v and gate|up stacked (one shrink and one GEMM
+    over the concatenated weight each)."""
+    import torch
+    import segmented_rank_gemm_segment_amd as srg
+    import workloads as wl
+    names = [p[0] for p in wl.CFG5_PROJECTIONS]
+    ws = {nm: wl.cfg5_projection(nm) for nm in names}
+    for a, b in (("k_proj", "q_proj"), ("v_proj", "q_proj"), ("up_proj", "gate_proj")):
+        ws[a].X = ws[b].X
+    w0 = ws["q_proj"]
+    n = w0.n
+    row_slot = torch.from_numpy(np.ascontiguousarray(w0.row_slot, dtype=np.int32)).to(device)
+    dev = {}
+    for nm, w in ws.items():
+        d = wl.device_tensors(w, device)
+        dev[nm] = {"X": d["X"], "W": d["W"],
+                   "pool": srg.Pool(d["A"], d["Bt"], d["slot_rank"], w.slot_alpha)}
+    seg = srg.Segments(n, w0.n_slots, device)
+
+    def unit(X, W, pool):
+        H = torch.empty((n, pool.r_max), dtype=torch.float32, device=device)
+        Y = torch.empty((n, pool.d_out), dtype=torch.bfloat16, device=device)
+        return {"X": X, "W": W, "pool": pool, "H": H, "Y": Y}
+
+    sep = [unit(dev[nm]["X"], dev[nm]["W"], dev[nm]["pool"]) for nm in names]
+    groups = (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",))
+    stk = []
+    for g in groups:
+        if len(g) == 1:
+            stk.append(sep[names.index(g[0])])
+        else:
+            W = torch.cat([dev[nm]["W"] for nm in g], dim=0).contiguous()
+            stk.append(unit(dev[g[0]]["X"], W, srg.Pool.stacked([dev[nm]["pool"] for nm in g])))
+
+    def step(units):
+        def fn(_):
+            srg.lora_build_segments(row_slot, units[0]["pool"], seg)
+            for u in units:
+                srg.lora_shrink(u["X"], seg, u["pool"], u["H"])
+                srg.lora_linear_fused(u["X"], u["W"], u["H"], seg, u["pool"], u["Y"])
+        return fn
+
+    st = max(3, args.steps // 20)
+    t_sep, _ = time_calls((step(sep),), [None], st, 2, not args.eager)
+    t_stk, _ = time_calls((step(stk),), [None], st, 2, not args.eager)
+    flops = sum(2 * n * w.d_in * w.d_out for w in ws.values())
+    out = {"workload": "70B-shaped layer: q/k/v/o/gate/up/down, 2304 rows (2048 prefill + 256 "
+                       "decode), 64 slots r in {16, 64}",
+           "separate": {"tokens_s": round(n / t_sep, 1), "ms": round(t_sep * 1e3, 4),
+                        "TFLOP_s": round(flops / t_sep / 1e12, 1), "calls": 1 + 2 * len(sep)},
+           "stacked": {"tokens_s": round(n / t_stk, 1), "ms": round(t_stk * 1e3, 4),
+                       "TFLOP_s": round(flops / t_stk / 1e12, 1), "calls": 1 + 2 * len(stk)},
+           "stacked_speedup": round(t_sep / t_stk, 4)}
+    del dev, sep, stk
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -616,6 +683,8 @@ def main():
                 "fused_gemm": roofline_for("fused_fp8w", f3, mq3["per_kernel_s"]["fused_fp8w"], "bf16"),
                 "fused_us": round(mq3["per_kernel_s"]["fused_fp8w"] * 1e6, 3)}
             del w3
+    if not args.no_layer and args.config == 2:
+        out["layer_70b"] = layer_entry(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
