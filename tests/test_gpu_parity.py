@@ -118,6 +118,9 @@ CASES = [
     # long segments (tiled shrink) with a ragged K tail, large-tile GEMM K tail
     (109, 700, 200, 136, 7, 64, 0.1, "bf16", True),
     (110, 2100, 328, 264, 5, 32, 0.2, "bf16", True),
+    # 128 x 128 tiles (few 256 x 256 tiles) and 256 x 256 tiles with a K tail
+    (111, 1024, 256, 1024, 12, 64, 0.1, "bf16", False),
+    (112, 1100, 200, 8200, 7, 64, 0.1, "bf16", True),
 ]
 
 
