@@ -78,6 +78,12 @@ struct GemmArgs {
 #ifndef LORA_GEMM_LARGE_F8
 #define LORA_GEMM_LARGE_F8 LORA_GEMM_LARGE
 #endif
+// Large and mid tiles with more LoRA runs than this (consecutive rows of one
+// segment; decode rows make one each) finish row by row on the VALU instead
+// of one staged MFMA increment per segment.
+#ifndef LORA_GEMM_STAGED_RUNS
+#define LORA_GEMM_STAGED_RUNS 4
+#endif
 #ifndef LORA_GEMM_SGB
 #define LORA_GEMM_SGB 1
 #endif
@@ -142,6 +148,56 @@ __device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi)
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))});
 }
 
+// LoRA term of one output row over 8 consecutive columns, added to o in fp32:
+// o[e] += sc sum_{k < r} H[grow][qoff + k] Bt_slot[qoff + k][gcol + e], k
+// ascending, read in chunks of 8 rank rows (rows at or past r inside the
+// chunk are read inside the projection's block and skipped); then, with
+// DoRA, the slot's column factors.  qoff is the rank offset of the columns'
+// projection (offsets of projections are multiples of 8, so all 8 columns
+// share it).  Shared by both row epilogues, so both give the same bits.
+template <bool DORA>
+__device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol, int slot, int r,
+                                          float sc, float (&o)[8]) {
+  const int N = g.N;
+  const int qoff = proj_of(g.proj, gcol) * g.proj.rs;
+  const bf16_t *bt = g.Bt + ((int64_t)slot * g.r_max + qoff) * N + gcol;
+  const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
+  float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < r; kc += 8) {      // kc + 8 <= rs: in the block
+    const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
+    const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
+    const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    u32x4 b[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) b[q] = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(kc + q) * N);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool use = kc + q < r;
+      float bv[8];
+      Elem<bf16_t>::unpack(make_uint4(b[q][0], b[q][1], b[q][2], b[q][3]), bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = use ? fmaf(h[q], bv[e], d[e]) : d[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = fmaf(sc, d[e], o[e]);
+  if constexpr (DORA) {
+    const float *gp = g.dora + (int64_t)slot * N + gcol;
+    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
+    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+    o[0] *= g0[0]; o[1] *= g0[1]; o[2] *= g0[2]; o[3] *= g0[3];
+    o[4] *= g1[0]; o[5] *= g1[1]; o[6] *= g1[2]; o[7] *= g1[3];
+  }
+}
+
+// Rows per chunk of the many-run epilogue: all of the tile's rows, halved
+// (down to 32) until a chunk of fp32 rows fits in `limit` bytes.
+constexpr int epi_chunk_rows(int bm, int row_bytes, int limit) {
+  int cr = bm;
+  while (cr > 32 && cr * row_bytes > limit) cr /= 2;
+  return cr;
+}
+
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz, swzb).  WF8: W holds E4M3 codes
 // (one byte per element, 64-byte B rows in LDS), widened to bf16 as each
@@ -154,8 +210,15 @@ template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, 
           bool WF8>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG, WF8 ? 1 : 2>;
-  // LDS: the stage ring, or the fused LoRA staging of large tiles if larger
-  constexpr int LSTG = (LORA != 0 && KG == 1) ? 3 * (BM > BN ? BM : BN) * 128 + 16 + 4 * BM : 0;
+  // LDS: the stage ring, or the fused LoRA epilogue of large tiles if larger:
+  // the staged segment operands (EPI_STG bytes) or EPI_CR fp32 rows of the
+  // tile (row stride BN + 4), then per-row rank, slot and scale and a word
+  constexpr int EPI_STG = 3 * (BM > BN ? BM : BN) * 128 + 16 + 4 * BM;
+  constexpr int EPI_RS = BN + 4;
+  constexpr int EPI_CR = epi_chunk_rows(BM, EPI_RS * 4, C::LDS - 12 * BM - 16);
+  constexpr int EPI_META =
+      ((EPI_CR * EPI_RS * 4 > EPI_STG ? EPI_CR * EPI_RS * 4 : EPI_STG) + 15) / 16 * 16;
+  constexpr int LSTG = (LORA != 0 && KG == 1) ? EPI_META + 12 * BM + 16 : 0;
   constexpr int SMEM = C::LDS > LSTG ? C::LDS : LSTG;
   __shared__ __align__(16) unsigned char smem[SMEM];
 
@@ -459,40 +522,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       }
     }
     if constexpr (LORA != 0) {
-      if (live && e_r > 0) {
-        // the 8 columns' projection: its rank rows start at qoff (offsets of
-        // projections are multiples of 8, so all 8 columns share it)
-        const int qoff = proj_of(g.proj, gcol) * g.proj.rs;
-        const bf16_t *bt = g.Bt + ((int64_t)e_slot * g.r_max + qoff) * N + gcol;
-        const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
-        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int kc = 0; kc < e_r; kc += 8) {      // kc + 8 <= rs: in the block
-          const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
-          const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
-          const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-          u32x4 b[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) b[q] = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(kc + q) * N);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const bool use = kc + q < e_r;
-            float bv[8];
-            Elem<bf16_t>::unpack(make_uint4(b[q][0], b[q][1], b[q][2], b[q][3]), bv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) d[e] = use ? fmaf(h[q], bv[e], d[e]) : d[e];
-          }
-        }
-        const float sc = __int_as_float(e_scb);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(sc, d[e], o[e]);
-        if constexpr (DORA) {
-          const float *gp = g.dora + (int64_t)e_slot * N + gcol;
-          const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
-          const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
-          o[0] *= g0[0]; o[1] *= g0[1]; o[2] *= g0[2]; o[3] *= g0[3];
-          o[4] *= g1[0]; o[5] *= g1[1]; o[6] *= g1[2]; o[7] *= g1[3];
-        }
-      }
+      if (live && e_r > 0) lora_row8<DORA>(g, grow, gcol, e_slot, e_r, __int_as_float(e_scb), o);
     }
     if (live) stg16(g.Y + (int64_t)grow * g.ldy + gcol, Elem<bf16_t>::pack(o));
     return;
@@ -576,8 +606,79 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       const int sg = g.row_segment[m0 + tid];
       if (g.seg_rank[sg] > 0) my_seg = sg;
     }
+    int *s_rr = reinterpret_cast<int *>(smem + EPI_META);   // per row: rank (0: no term)
+    int *s_rslot = s_rr + BM;                               //          slot
+    float *s_rsc = reinterpret_cast<float *>(s_rslot + BM); //          scale
+    int *s_runs = reinterpret_cast<int *>(s_rsc + BM);
     // previous readers of LDS (the K loop, the partial sums) are done
     lgkm_barrier();
+    // Runs of LoRA rows: a row of a LoRA segment that differs from the
+    // previous row's starts one.  A tile of few long runs (prefill requests)
+    // takes the staged MFMA increment below, one segment at a time; a tile of
+    // many short runs (decode rows, each of its own adapter) would repeat
+    // that for each of them, and instead finishes row by row on the VALU.
+    if (tid == 0) *s_runs = 0;
+    if (tid < BM) s_rr[tid] = my_seg;
+    lgkm_barrier();
+    {
+      const bool start = tid < BM && my_seg >= 0 && (tid == 0 || s_rr[tid - 1] != my_seg);
+      const uint64_t bal = __ballot(start);
+      if (l == 0 && bal != 0) atomicAdd(s_runs, (int)__popcll(bal));
+    }
+    lgkm_barrier();
+    if (__builtin_amdgcn_readfirstlane(*s_runs) > LORA_GEMM_STAGED_RUNS) {
+      // Row epilogue of a large tile, EPI_CR rows at a time: the waves that
+      // hold the chunk's rows put their accumulators in LDS row-major, then
+      // each thread takes (row, 8 columns) items: lora_row8 with the row's
+      // own adapter, the rounding and one 16-byte store.
+      if (tid < BM) {
+        int r = 0, slot = 0;
+        float sc = 0.f;
+        if (my_seg >= 0) {
+          r = g.seg_rank[my_seg];
+          slot = g.seg_slot[my_seg];
+          sc = g.seg_scale[my_seg];
+        }
+        s_rr[tid] = r;
+        s_rslot[tid] = slot;
+        s_rsc[tid] = sc;
+      }
+      float *red = reinterpret_cast<float *>(smem);
+      for (int c0 = 0; c0 < BM; c0 += EPI_CR) {
+        // the previous chunk's readers are done (first chunk: the metadata
+        // writes are visible)
+        lgkm_barrier();
+        if (kgrp == 0) {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) {
+            const int fr = wm * C::TM + i * 32;             // wave-uniform
+            if (fr >= c0 && fr < c0 + EPI_CR) {
+#pragma unroll
+              for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                  red[(fr - c0 + acc_row(v, l)) * EPI_RS + wn * C::TN + j * 32 + (l & 31)] =
+                      acc[i][j][v];
+            }
+          }
+        }
+        lgkm_barrier();
+        for (int it = tid; it < EPI_CR * (BN / 8); it += C::T) {
+          const int row = it / (BN / 8), c8 = (it % (BN / 8)) * 8;
+          const int grow = m0 + c0 + row, gcol = n0 + c8;
+          if (grow >= M || gcol >= N) continue;       // N % 8 == 0: all 8 columns or none
+          float o[8];
+          const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8);
+          const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8 + 4);
+          o[0] = p0[0]; o[1] = p0[1]; o[2] = p0[2]; o[3] = p0[3];
+          o[4] = p1[0]; o[5] = p1[1]; o[6] = p1[2]; o[7] = p1[3];
+          const int r = s_rr[c0 + row];
+          if (r > 0) lora_row8<DORA>(g, grow, gcol, s_rslot[c0 + row], r, s_rsc[c0 + row], o);
+          stg16(g.Y + (int64_t)grow * g.ldy + gcol, Elem<bf16_t>::pack(o));
+        }
+      }
+      return;
+    }
     if constexpr (DORA) {
       if (tid < BM) s_rowslot[tid] = my_seg >= 0 ? g.seg_slot[my_seg] : -1;
     }
