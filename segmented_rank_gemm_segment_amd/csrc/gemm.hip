@@ -198,6 +198,71 @@ constexpr int epi_chunk_rows(int bm, int row_bytes, int limit) {
   return cr;
 }
 
+// lora_row8 for two (row, 8 columns) items at once, so that the loads of
+// both are in flight together: chunk kc of an item whose rank ends earlier
+// re-reads its last chunk (in the block) and adds nothing.  Each item's sum
+// is formed in the same order as lora_row8's, so the bits are the same.
+template <bool DORA>
+__device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&grow)[2],
+                                               const int (&gcol)[2], const int (&slot)[2],
+                                               const int (&r)[2], const float (&sc)[2],
+                                               float (&o)[2][8]) {
+  const int N = g.N;
+  const bf16_t *bt[2];
+  const float *hp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int qoff = proj_of(g.proj, gcol[u]) * g.proj.rs;
+    bt[u] = g.Bt + ((int64_t)slot[u] * g.r_max + qoff) * N + gcol[u];
+    hp[u] = g.H + (int64_t)grow[u] * g.r_max + qoff;
+  }
+  float d[2][8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[u][e] = 0.f;
+  const int rmax = max(r[0], r[1]);
+  for (int kc = 0; kc < rmax; kc += 8) {
+    f32x4 h0[2], h1[2];
+    u32x4 b[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = min(kc, max(r[u], 8) - 8);   // in the block
+      h0[u] = *reinterpret_cast<const f32x4 *>(hp[u] + kk);
+      h1[u] = *reinterpret_cast<const f32x4 *>(hp[u] + kk + 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        b[u][q] = *reinterpret_cast<const u32x4 *>(bt[u] + (int64_t)(kk + q) * N);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float h[8] = {h0[u][0], h0[u][1], h0[u][2], h0[u][3],
+                          h1[u][0], h1[u][1], h1[u][2], h1[u][3]};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool use = kc + q < r[u];
+        float bv[8];
+        Elem<bf16_t>::unpack(make_uint4(b[u][q][0], b[u][q][1], b[u][q][2], b[u][q][3]), bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[u][e] = use ? fmaf(h[q], bv[e], d[u][e]) : d[u][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (r[u] <= 0) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[u][e] = fmaf(sc[u], d[u][e], o[u][e]);
+    if constexpr (DORA) {
+      const float *gp = g.dora + (int64_t)slot[u] * N + gcol[u];
+      const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
+      const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+      o[u][0] *= g0[0]; o[u][1] *= g0[1]; o[u][2] *= g0[2]; o[u][3] *= g0[3];
+      o[u][4] *= g1[0]; o[u][5] *= g1[1]; o[u][6] *= g1[2]; o[u][7] *= g1[3];
+    }
+  }
+}
+
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz, swzb).  WF8: W holds E4M3 codes
 // (one byte per element, 64-byte B rows in LDS), widened to bf16 as each
@@ -663,7 +728,37 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           }
         }
         lgkm_barrier();
-        for (int it = tid; it < EPI_CR * (BN / 8); it += C::T) {
+        constexpr int ITEMS = EPI_CR * (BN / 8);
+        if constexpr (EPI_CR == BM) {
+          // one chunk (the accumulators are dead now): two items at a time
+          for (int it0 = tid; it0 < ITEMS; it0 += 2 * C::T) {
+            int grow[2], gcol[2], slot[2], r[2];
+            float sc[2], o[2][8];
+            bool live[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int it = it0 + u * C::T;
+              const int row = min(it, ITEMS - 1) / (BN / 8), c8 = (it % (BN / 8)) * 8;
+              live[u] = it < ITEMS && m0 + row < M && n0 + c8 < N;
+              // dead items read row and columns in bounds and add nothing
+              grow[u] = min(m0 + row, M - 1);
+              gcol[u] = min(n0 + c8, N - 8);
+              const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8);
+              const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8 + 4);
+              o[u][0] = p0[0]; o[u][1] = p0[1]; o[u][2] = p0[2]; o[u][3] = p0[3];
+              o[u][4] = p1[0]; o[u][5] = p1[1]; o[u][6] = p1[2]; o[u][7] = p1[3];
+              r[u] = live[u] ? s_rr[row] : 0;
+              slot[u] = s_rslot[row];
+              sc[u] = s_rsc[row];
+            }
+            lora_row8_pair<DORA>(g, grow, gcol, slot, r, sc, o);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              if (live[u]) stg16(g.Y + (int64_t)grow[u] * g.ldy + gcol[u], Elem<bf16_t>::pack(o[u]));
+          }
+          continue;
+        }
+        for (int it = tid; it < ITEMS; it += C::T) {
           const int row = it / (BN / 8), c8 = (it % (BN / 8)) * 8;
           const int grow = m0 + c0 + row, gcol = n0 + c8;
           if (grow >= M || gcol >= N) continue;       // N % 8 == 0: all 8 columns or none

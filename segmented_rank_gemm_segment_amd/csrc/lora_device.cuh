@@ -152,6 +152,75 @@ __device__ __forceinline__ SegMeta load_seg_meta(int s, const int32_t *num_segme
   return m;
 }
 
+// Work items of the segmented kernels: the positions of the segment order
+// (token_indices) in blocks of at most rb, cut at segment boundaries.  Item
+// y < nb is the block of positions [y rb, y rb + rb) inside the segment that
+// holds position y rb, unless that segment starts there; item nb + s is the
+// first block of segment s, from its start to the next multiple of rb (or
+// its end).  Every position lies in exactly one item, so a batch needs at
+// most nb + S items whatever the segment lengths, and no item has more than
+// rb rows.  ok is false for an item without rows (a block where a segment
+// starts, or s >= S).  Items y >= nb need y - nb < cap (the segment arrays'
+// capacity); metadata from the build keeps every segment id below it.
+struct SegItem {
+  bool ok;
+  int r, slot, o0, o1, p0, p1;
+  float sc;
+};
+__device__ __forceinline__ SegItem seg_item(int y, int nb, int rb, int cap,
+                                            const int32_t *token_indices,
+                                            const int32_t *row_segment,
+                                            const int32_t *num_segments, const int32_t *seg_rank,
+                                            const int32_t *seg_off, const int32_t *seg_slot,
+                                            const float *seg_scale) {
+  int s, p0 = y * rb;
+  if (y < nb) {
+    s = row_segment[token_indices[p0]];
+    s = min(max(s, 0), cap - 1);
+  } else {
+    s = y - nb;
+  }
+  const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, seg_scale);
+  SegItem it;
+  it.r = m.r;
+  it.slot = m.slot;
+  it.sc = m.sc;
+  it.o0 = m.o0;
+  it.o1 = m.o1;
+  if (y < nb) {
+    it.p0 = p0;
+    it.p1 = min(p0 + rb, m.o1);
+    it.ok = s < m.S && m.o0 != p0 && p0 < it.p1;
+  } else {
+    it.p0 = m.o0;
+    it.p1 = min(m.o1, (m.o0 / rb + 1) * rb);
+    it.ok = s < m.S && it.p0 < it.p1;
+  }
+  return it;
+}
+
+// Segment-major items for when only short segments are wanted: item
+// y = b cap + s is block b of segment s, [o0 + b rb, o0 + b rb + rb) inside
+// the segment.  With y < bps cap, segments of up to bps rb rows are covered.
+__device__ __forceinline__ SegItem seg_item_major(int y, int rb, int cap,
+                                                  const int32_t *num_segments,
+                                                  const int32_t *seg_rank, const int32_t *seg_off,
+                                                  const int32_t *seg_slot, const float *seg_scale) {
+  const int b = y / cap;
+  const int s = y - b * cap;
+  const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, seg_scale);
+  SegItem it;
+  it.r = m.r;
+  it.slot = m.slot;
+  it.sc = m.sc;
+  it.o0 = m.o0;
+  it.o1 = m.o1;
+  it.p0 = m.o0 + b * rb;
+  it.p1 = min(m.o1, it.p0 + rb);
+  it.ok = s < m.S && it.p0 < it.p1;
+  return it;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);

@@ -11,8 +11,11 @@
 // by g_a[j] before the rounding: Y[i][j] = g_a[j] (Y[i][j] + s_a ...).
 //
 // Both are bandwidth-bound segmented GEMV / skinny products.  Work items are
-// (segment, block of up to kRowBlk rows of that segment); a fixed grid walks
-// them with a stride, so no host synchronisation sizes the launch.  Adapter
+// blocks of at most rb rows of one segment, cut from the segment order at
+// multiples of rb and at segment starts (seg_item), so a batch has at most
+// n / rb + S of them however long its segments are; a grid of one workgroup
+// row per item (striding past a cap) walks them, so no host synchronisation
+// sizes the launch.  Adapter
 // rows are read once per work item with 16-byte coalesced loads along d, and
 // every load of a work item is issued before its arithmetic, so a work item
 // costs about one memory round trip.  Each token row lives in exactly one
@@ -43,29 +46,29 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 template <typename T>
 __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
-    const int32_t *seg_off, const int32_t *seg_slot, const int32_t *seg_rank,
-    const int32_t *num_segments, int r_max, int rs, int d_in, int policy, int seg_cap,
-    int cap_items, int long_min, float *__restrict__ H) {
+    const int32_t *row_segment, const int32_t *seg_off, const int32_t *seg_slot,
+    const int32_t *seg_rank, const int32_t *num_segments, int r_max, int rs, int d_in, int policy,
+    int rb, int nb, int seg_cap, int long_min, float *__restrict__ H) {
   __shared__ float s_part[kShW][kShNP];
   const int k0 = blockIdx.x * kShRB;       // rank row of the pool
   const int kl0 = k0 % rs;                 // ... and inside its projection's block
-  // items are ordered block-major (item = b * seg_cap + s): the first row
-  // block of every segment comes first, so launch-order work is real work
-  // and later (mostly empty) blocks cost one metadata read each
-  for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
-    const int b = item / seg_cap;
-    const int s = item - b * seg_cap;
-    // s < capacity keeps the metadata read in bounds before S is known
-    const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, nullptr);
-    if (s >= m.S) continue;
-    const int R = rank_bucket(m.r, policy, rs);
+  // position blocks first, then the segments' first blocks (seg_item); when
+  // the MFMA kernel takes the long segments, only the blocks of the short
+  // ones, segment-major (seg_item_major)
+  const bool major = long_min != INT_MAX;
+  const int n_items = major ? nb * seg_cap : nb + seg_cap;
+  for (int item = blockIdx.y; item < n_items; item += gridDim.y) {
+    const SegItem it =
+        major ? seg_item_major(item, rb, seg_cap, num_segments, seg_rank, seg_off, seg_slot,
+                               nullptr)
+              : seg_item(item, nb, rb, seg_cap, token_indices, row_segment, num_segments,
+                         seg_rank, seg_off, seg_slot, nullptr);
+    if (!it.ok) continue;
+    const int R = rank_bucket(it.r, policy, rs);
     if (kl0 >= R) continue;
-    if (m.o1 - m.o0 >= long_min) continue;   // long segment: tiled MFMA kernel
-    const int p0 = m.o0 + b * kRowBlk;
-    const int p1 = min(m.o1, p0 + kRowBlk);
-    if (p0 >= p1) continue;
-    shrink_rows<T>(X, ldx, A, m.slot, k0, kl0, min(kShRB, R - kl0), m.r, r_max, d_in,
-                   token_indices, p0, p1, H, s_part);
+    if (it.o1 - it.o0 >= long_min) continue;   // long segment: tiled MFMA kernel
+    shrink_rows<T>(X, ldx, A, it.slot, k0, kl0, min(kShRB, R - kl0), it.r, r_max, d_in,
+                   token_indices, it.p0, it.p1, H, s_part);
   }
 }
 
@@ -352,10 +355,10 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
 template <typename T, int RMAX, bool DORA>
 __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     const float *__restrict__ H, const T *__restrict__ Bt, const float *__restrict__ dora,
-    const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
-    const int32_t *seg_rank, const float *seg_scale, const int32_t *num_segments, int r_max,
-    int d_out, int policy, int seg_cap, int cap_items, T *__restrict__ Y, int64_t ldy,
-    ProjView proj) {
+    const int32_t *token_indices, const int32_t *row_segment, const int32_t *seg_off,
+    const int32_t *seg_slot, const int32_t *seg_rank, const float *seg_scale,
+    const int32_t *num_segments, int r_max, int d_out, int policy, int rb, int nb, int seg_cap,
+    T *__restrict__ Y, int64_t ldy, ProjView proj) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -364,20 +367,16 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
   // the lane's columns belong to one projection (its offsets are multiples
   // of 8): its rank rows start at q * rs in the slot and in H
   const int qoff = proj_of(proj, active ? col : 0) * proj.rs;
-  // block-major items (item = b * seg_cap + s), as in the shrink
-  for (int item = blockIdx.y; item < cap_items; item += gridDim.y) {
-    const int b = item / seg_cap;
-    const int s = item - b * seg_cap;
-    // s < capacity keeps the metadata read in bounds before S is known
-    const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, seg_scale);
-    if (s >= m.S) continue;
-    const int r = m.r, slot = m.slot;
-    const float sc = m.sc;
+  // position blocks first, then the segments' first blocks (seg_item)
+  for (int item = blockIdx.y; item < nb + seg_cap; item += gridDim.y) {
+    const SegItem it = seg_item(item, nb, rb, seg_cap, token_indices, row_segment, num_segments,
+                                seg_rank, seg_off, seg_slot, seg_scale);
+    if (!it.ok) continue;
+    const int r = it.r, slot = it.slot;
+    const float sc = it.sc;
     const int R = rank_bucket(r, policy, proj.rs);
     if (R == 0) continue;
-    const int p0 = m.o0 + b * kRowBlk;
-    const int p1 = min(m.o1, p0 + kRowBlk);
-    if (p0 >= p1) continue;
+    const int p0 = it.p0, p1 = it.p1;
     const T *bt = Bt + ((int64_t)slot * r_max + qoff) * d_out + (active ? col : 0);
     const float *gp = DORA ? dora + (int64_t)slot * d_out + (active ? col : 0) : nullptr;
     const float *Hq = H + qoff;   // the projection's ranks in each H row
@@ -413,39 +412,44 @@ inline int grid_items(int items, int x) {
 
 }  // namespace
 
+// Rows per work item: short blocks spread the rows of a long segment over
+// many workgroups (a Zipf-skewed decode batch has segments of a hundred rows
+// next to single rows); large batches take longer blocks, which read each
+// adapter row fewer times.
+inline int row_block(int n) { return n >= kLargeBatch ? kRowBlk : kRowBlkSmall; }
+
 hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const PoolView &pool,
                          float *H, hipStream_t stream) {
   const int n = seg.n_rows;
-  const int bps = (n + kRowBlk - 1) / kRowBlk;
+  const int rb = row_block(n);
+  const int nb = (n + rb - 1) / rb;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
-  // Real items: every segment has >= 1 row, so sum_s ceil(n_s / kRowBlk) <= S + n / kRowBlk.
-  const int real_bound = S_bound + n / kRowBlk;
   // long segments (>= kLongRows rows) go to the tiled MFMA kernel in large
   // (prefill-sized) batches; decode-sized batches keep every segment on the
   // GEMV kernel and launch nothing more
   const bool use_mfma = pool.dtype == 1 && n >= kMfmaShrinkMinBatch;
   const int long_min = use_mfma ? kLongRows : INT_MAX;
-  // one workgroup row per item up to the cap (empty items exit after one
-  // metadata read, in parallel rather than one after another).  When long
-  // segments go to the MFMA kernel, the GEMV kernel only sees segments
-  // shorter than kLongRows, whose rows fit in the first few row blocks.
-  (void)real_bound;
-  const int gemv_bps = use_mfma ? min(bps, (kLongRows + kRowBlk - 1) / kRowBlk) : bps;
+  // one workgroup row per item up to the cap (an item without rows exits
+  // after its metadata read).  With the MFMA kernel on the long segments, the
+  // GEMV kernel walks the first blocks of every segment (nb of them below
+  // kLongRows rows) instead of the position blocks.
+  const int nb_g = use_mfma ? (kLongRows + rb - 1) / rb : nb;
+  const int items = use_mfma ? nb_g * S_bound : nb + S_bound;
   const int gx = (pool.r_max + kShRB - 1) / kShRB;
-  dim3 grid(gx, grid_items(S_bound * gemv_bps, gx));
+  dim3 grid(gx, grid_items(items, gx));
   dim3 block(kShW * kWave);
   if (pool.dtype == 1) {
     hipLaunchKernelGGL((shrink_kernel<bf16_t>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
-                       seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.proj.rs, pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min,
-                       H);
+                       seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
+                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
+                       long_min, H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
-                       seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments, pool.r_max,
-                       pool.proj.rs, pool.d_in, pool.policy, S_bound, S_bound * gemv_bps, long_min,
-                       H);
+                       seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
+                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
+                       long_min, H);
   }
   if (use_mfma) {
     const int tps = (n + kSM - 1) / kSM;
@@ -464,44 +468,45 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
 
 template <typename T, int RMAX>
 void launch_expand_t(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
-                     int bps, int S_bound, int real_bound, hipStream_t stream) {
+                     int rb, int nb, int S_bound, hipStream_t stream) {
   const int cols_per_block = kExpWaves * 16 * Elem<T>::kVec;
-  (void)real_bound;
   const int gx = (pool.d_out + cols_per_block - 1) / cols_per_block;
-  dim3 grid(gx, grid_items(S_bound * bps, gx));
+  dim3 grid(gx, grid_items(nb + S_bound, gx));
   if (pool.dora)
     hipLaunchKernelGGL((expand_kernel<T, RMAX, true>), grid, dim3(kExpWaves * kWave), 0, stream,
-                       H, (const T *)pool.Bt, pool.dora, seg.token_indices, seg.seg_off,
-                       seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
-                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy, pool.proj);
+                       H, (const T *)pool.Bt, pool.dora, seg.token_indices, seg.row_segment,
+                       seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
+                       pool.r_max, pool.d_out, pool.policy, rb, nb, S_bound, (T *)Y, ldy,
+                       pool.proj);
   else
     hipLaunchKernelGGL((expand_kernel<T, RMAX, false>), grid, dim3(kExpWaves * kWave), 0, stream,
-                       H, (const T *)pool.Bt, nullptr, seg.token_indices, seg.seg_off,
-                       seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments, pool.r_max,
-                       pool.d_out, pool.policy, S_bound, S_bound * bps, (T *)Y, ldy, pool.proj);
+                       H, (const T *)pool.Bt, nullptr, seg.token_indices, seg.row_segment,
+                       seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
+                       pool.r_max, pool.d_out, pool.policy, rb, nb, S_bound, (T *)Y, ldy,
+                       pool.proj);
 }
 
 template <typename T>
 void launch_expand_r(const float *H, const SegView &seg, const PoolView &pool, void *Y, int64_t ldy,
-                     int bps, int S_bound, int real_bound, hipStream_t stream) {
+                     int rb, int nb, int S_bound, hipStream_t stream) {
   switch (pool.proj.rs) {
-    case 8: launch_expand_t<T, 8>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
-    case 16: launch_expand_t<T, 16>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
-    case 32: launch_expand_t<T, 32>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
-    default: launch_expand_t<T, 64>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream); break;
+    case 8: launch_expand_t<T, 8>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream); break;
+    case 16: launch_expand_t<T, 16>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream); break;
+    case 32: launch_expand_t<T, 32>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream); break;
+    default: launch_expand_t<T, 64>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream); break;
   }
 }
 
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream) {
   const int n = seg.n_rows;
-  const int bps = (n + kRowBlk - 1) / kRowBlk;
+  const int rb = row_block(n);
+  const int nb = (n + rb - 1) / rb;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
-  const int real_bound = S_bound + n / kRowBlk;
   if (pool.dtype == 1)
-    launch_expand_r<bf16_t>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream);
+    launch_expand_r<bf16_t>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream);
   else
-    launch_expand_r<float>(H, seg, pool, Y, ldy, bps, S_bound, real_bound, stream);
+    launch_expand_r<float>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream);
   return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@
 
 namespace lora {
 
-constexpr int kRowBlk = 64;    // rows of one segment per work item
+constexpr int kRowBlk = 64;    // rows of one segment per work item (large batches)
+constexpr int kRowBlkSmall = 16;  // ... in batches below kLargeBatch rows
+constexpr int kLargeBatch = 2048;
 constexpr int kShW = 4;        // waves per workgroup
 constexpr int kShRQ = 4;       // token rows per group
 constexpr int kShRB = 8;       // rank rows per workgroup
