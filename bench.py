@@ -65,6 +65,8 @@ def parse():
                    help="skip the DoRA variant (column factors in the epilogue)")
     p.add_argument("--no-fp8w", action="store_true",
                    help="skip the FP8-weight variant of the base product")
+    p.add_argument("--no-skewed", action="store_true",
+                   help="skip the skewed large-pool decode entry (configuration 4, three rank policies)")
     p.add_argument("--no-layer", action="store_true",
                    help="skip the 70B-shaped layer (seven projections, separate vs stacked)")
     p.add_argument("--no-vendor", action="store_true",
@@ -569,6 +571,30 @@ def layer_entry(args, device="cuda:0"):
     return out
 
 
+def skewed_entry(args):
+    """Configuration 4 (1024 decode rows, 1000 resident slots of mixed rank,
+    Zipf adapter ids) under each rank policy: per-rank buckets (exact), the
+    two buckets {8,16} / {32,64}, and every slot padded to rank 64.  Step on
+    each path (the fastest one named) and the shrink / fused GEMM per policy."""
+    import workloads as wl
+    w4 = wl.make_config(4)
+    f4 = work_figures(w4)
+    st = max(10, args.steps // 4)
+    out = {"workload": WORKLOAD_NAMES[4], "rows": w4.n,
+           "distinct_adapters": f4["distinct_adapters"], "policies": {}}
+    for pol in ("exact", "two_buckets", "padded"):
+        m4 = measure(w4, ["fused", "separate"], pol, st, max(3, args.warmup // 4), args.rotate_mb,
+                     st, not args.eager, kernels=(k_build_shrink, k_shrink, k_fused, k_expand))
+        best = min(m4["step"], key=lambda p: m4["step"][p][0])
+        out["policies"][pol] = {
+            "path": best, "tokens_s": round(w4.n / m4["step"][best][0], 1),
+            "step_us_by_path": {p: round(v[0] * 1e6, 3) for p, v in m4["step"].items()},
+            "us": {k: round(v * 1e6, 3) for k, v in m4["per_kernel_s"].items()}}
+    ex, pad = out["policies"]["exact"], out["policies"]["padded"]
+    out["padded_over_exact_step"] = round(ex["tokens_s"] / pad["tokens_s"], 4)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -683,6 +709,8 @@ def main():
                 "fused_gemm": roofline_for("fused_fp8w", f3, mq3["per_kernel_s"]["fused_fp8w"], "bf16"),
                 "fused_us": round(mq3["per_kernel_s"]["fused_fp8w"] * 1e6, 3)}
             del w3
+    if not args.no_skewed and args.config == 2:
+        out["skewed_decode"] = skewed_entry(args)
     if not args.no_layer and args.config == 2:
         out["layer_70b"] = layer_entry(args)
     if not args.no_cpu_baseline:

@@ -190,14 +190,6 @@ __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol,
   }
 }
 
-// Rows per chunk of the many-run epilogue: all of the tile's rows, halved
-// (down to 32) until a chunk of fp32 rows fits in `limit` bytes.
-constexpr int epi_chunk_rows(int bm, int row_bytes, int limit) {
-  int cr = bm;
-  while (cr > 32 && cr * row_bytes > limit) cr /= 2;
-  return cr;
-}
-
 // lora_row8 for two (row, 8 columns) items at once, so that the loads of
 // both are in flight together: chunk kc of an item whose rank ends earlier
 // re-reads its last chunk (in the block) and adds nothing.  Each item's sum
@@ -263,6 +255,83 @@ __device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&gr
   }
 }
 
+// Tile order of the MFMA kernels.  Workgroup b runs on XCD b % 8 (the
+// dispatcher deals consecutive ids round robin over the eight XCDs).  With
+// at least 8 N-tiles, XCD x owns N-tiles [x tiles_n / 8, (x + 1) tiles_n / 8)
+// of every M-tile and walks them in groups of 8 M-tiles sweeping its
+// N-tiles; with fewer, XCD x takes the x-th eighth of that grouped order
+// over all tiles.  An M-tile `heavy` (>= 0) comes before the groups, all of
+// its tiles of the XCD first (the others keep their order).  Returns false
+// for a workgroup past its XCD's tiles.  tile_grid is the launch size that
+// covers every tile.
+constexpr int kTileGroup = 8;
+constexpr int kHeavyMaxTilesM = 32;
+constexpr int kCUs = 256;   // compute units of an MI355X
+__host__ __device__ inline int tile_grid(int tiles_m, int tiles_n) {
+  return tiles_n >= 8 ? 8 * ((tiles_n + 7) / 8) * tiles_m : (tiles_m * tiles_n + 7) / 8 * 8;
+}
+__device__ __forceinline__ bool tile_order(int b, int tiles_m, int tiles_n, int heavy, int &m_idx,
+                                           int &n_idx) {
+  const int x = b & 7, j = b >> 3;
+  int n_lo, nx, t;
+  if (tiles_n >= 8) {
+    n_lo = x * tiles_n / 8;
+    nx = (x + 1) * tiles_n / 8 - n_lo;
+    if (j >= nx * tiles_m) return false;
+    t = j;
+  } else {
+    n_lo = 0;
+    nx = tiles_n;
+    t = x * ((tiles_m * tiles_n + 7) / 8) + j;
+    if (t >= tiles_m * tiles_n) return false;
+  }
+  int tm = tiles_m;
+  if (heavy >= 0) {
+    if (t < nx) {
+      m_idx = heavy;
+      n_idx = n_lo + t;
+      return true;
+    }
+    t -= nx;
+    tm = tiles_m - 1;
+  }
+  const int grp = t / (kTileGroup * nx);
+  const int first_m = grp * kTileGroup;
+  const int gcnt = min(kTileGroup, tm - first_m);
+  const int tin = t - grp * kTileGroup * nx;
+  m_idx = first_m + tin % gcnt;
+  if (heavy >= 0 && m_idx >= heavy) ++m_idx;
+  n_idx = n_lo + tin / gcnt;
+  return true;
+}
+
+// Which end M-tile of the batch holds more runs of segment ids (a row
+// whose segment differs from the previous row's starts one): tiles_m - 1 if
+// the last, 0 if the first, -1 if neither.  The first wave counts them with
+// ballots and shares the answer through one LDS word (s), which is free
+// again on return.  Called by every thread, before the tile's first LDS
+// write; tiles_m >= 2.
+__device__ __forceinline__ int heavier_end_tile(const int32_t *row_segment, int M, int BM,
+                                                int tiles_m, int *s) {
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    const int last0 = (tiles_m - 1) * BM;
+    int c0 = 0, c1 = 0;
+    for (int r = l; r < BM; r += kWave) {
+      // the first M-tile is whole (tiles_m >= 2); a tile's first row starts no run
+      const bool a = r > 0 && row_segment[r] != row_segment[r - 1];
+      const bool b = last0 + r < M && r > 0 && row_segment[last0 + r] != row_segment[last0 + r - 1];
+      c0 += __popcll(__ballot(a));
+      c1 += __popcll(__ballot(b));
+    }
+    if (l == 0) s[0] = c1 > c0 ? tiles_m - 1 : (c0 > c1 ? 0 : -1);
+  }
+  __syncthreads();
+  const int h = s[0];
+  __syncthreads();   // every wave has read s before the ring is written
+  return h;
+}
+
 // LDS layout of a stage: A rows [BM][BK] then B rows [BN][BK], 16-byte
 // chunks XOR-swizzled per row (TileCfg::swz, swzb).  WF8: W holds E4M3 codes
 // (one byte per element, 64-byte B rows in LDS), widened to bf16 as each
@@ -276,13 +345,11 @@ template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, 
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG, WF8 ? 1 : 2>;
   // LDS: the stage ring, or the fused LoRA epilogue of large tiles if larger:
-  // the staged segment operands (EPI_STG bytes) or EPI_CR fp32 rows of the
-  // tile (row stride BN + 4), then per-row rank, slot and scale and a word
+  // the staged segment operands (EPI_STG bytes) or one 32-row fp32 slot per
+  // wave (row stride TN + 4), then per-row rank, slot and scale and a word
   constexpr int EPI_STG = 3 * (BM > BN ? BM : BN) * 128 + 16 + 4 * BM;
-  constexpr int EPI_RS = BN + 4;
-  constexpr int EPI_CR = epi_chunk_rows(BM, EPI_RS * 4, C::LDS - 12 * BM - 16);
-  constexpr int EPI_META =
-      ((EPI_CR * EPI_RS * 4 > EPI_STG ? EPI_CR * EPI_RS * 4 : EPI_STG) + 15) / 16 * 16;
+  constexpr int EPI_ROW = C::NW * 32 * (BN / WN + 4) * 4;
+  constexpr int EPI_META = ((EPI_ROW > EPI_STG ? EPI_ROW : EPI_STG) + 15) / 16 * 16;
   constexpr int LSTG = (LORA != 0 && KG == 1) ? EPI_META + 12 * BM + 16 : 0;
   constexpr int SMEM = C::LDS > LSTG ? C::LDS : LSTG;
   __shared__ __align__(16) unsigned char smem[SMEM];
@@ -295,22 +362,28 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   const int kg0 = kgrp * BK;                        // the group's offset in a K step
   const int M = g.M, N = g.N, K = g.K;
 
-  // XCD-aware tile order: consecutive workgroup ids go to different XCDs
-  // (round robin over 8), so give each XCD a contiguous range of the
-  // grouped tile order (groups of 8 M-tiles sweeping N), keeping operand
-  // tiles shared by neighbours inside one L2.
+  // XCD-aware tile order (tile_order): consecutive workgroup ids go to
+  // different XCDs (round robin over 8); each XCD takes a contiguous range
+  // of N-tiles for every M-tile, in groups of 8 M-tiles sweeping its
+  // N-tiles, so operand tiles shared by neighbours stay inside one L2 and
+  // every M-tile's work is spread over all eight XCDs.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int per_xcd = (ntiles + 7) / 8;
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= ntiles) return;
-  constexpr int GROUP = 8;
-  const int grp = t / (GROUP * tiles_n);
-  const int first_m = grp * GROUP;
-  const int gcnt = min(GROUP, tiles_m - first_m);
-  const int tin = t - grp * GROUP * tiles_n;
-  const int m0 = (first_m + tin % gcnt) * BM;
-  const int n0 = (tin / gcnt) * BN;
+  // Tiles of many LoRA runs take the row epilogue, which costs more than
+  // the staged one (decode rows beside a prefill request); so that they run
+  // first rather than in a last, partly filled wave, the end M-tile of the
+  // batch with more runs is taken first (longest first).  Only for grids of
+  // more than one wave (these tiles run one workgroup per CU) and at most
+  // kHeavyMaxTilesM M-tiles: the check costs a memory round trip per
+  // workgroup.
+  int heavy = -1;
+  if constexpr (LORA != 0 && KG == 1) {
+    if (tiles_m > 1 && tiles_m <= kHeavyMaxTilesM && tiles_m * tiles_n > kCUs)
+      heavy = heavier_end_tile(g.row_segment, M, BM, tiles_m, reinterpret_cast<int *>(smem));
+  }
+  int m_idx, n_idx;
+  if (!tile_order(blockIdx.x, tiles_m, tiles_n, heavy, m_idx, n_idx)) return;
+  const int m0 = m_idx * BM;
+  const int n0 = n_idx * BN;
 
   // Small tiles (two K groups) finish row by row: thread tid owns tile row
   // tid / (BN / 8) and 8 consecutive columns (see the end of the kernel).
@@ -692,10 +765,13 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
     lgkm_barrier();
     if (__builtin_amdgcn_readfirstlane(*s_runs) > LORA_GEMM_STAGED_RUNS) {
-      // Row epilogue of a large tile, EPI_CR rows at a time: the waves that
-      // hold the chunk's rows put their accumulators in LDS row-major, then
-      // each thread takes (row, 8 columns) items: lora_row8 with the row's
-      // own adapter, the rounding and one 16-byte store.
+      // Row epilogue of a large tile, wave by wave: each wave puts one
+      // 32-row fragment row of its accumulators (32 rows x TN columns) in its
+      // own LDS slot, and its lanes take the (row, 8 columns) items of it,
+      // TN / 8 lanes per row: lora_row8 (or lora_row8_pair, same bits) with
+      // the row's own adapter, the rounding and one 16-byte store.  A
+      // fragment's registers are free once it is in LDS; no workgroup
+      // barrier is needed.
       if (tid < BM) {
         int r = 0, slot = 0;
         float sc = 0.f;
@@ -708,68 +784,55 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
         s_rslot[tid] = slot;
         s_rsc[tid] = sc;
       }
-      float *red = reinterpret_cast<float *>(smem);
-      for (int c0 = 0; c0 < BM; c0 += EPI_CR) {
-        // the previous chunk's readers are done (first chunk: the metadata
-        // writes are visible)
-        lgkm_barrier();
-        if (kgrp == 0) {
+      lgkm_barrier();                                 // the row metadata is visible
+      constexpr int WRS = C::TN + 4;                  // row stride of a wave's slot
+      constexpr int LPR = C::TN / 8;                  // lanes per row
+      constexpr int WITEMS = 32 * LPR;                // items per fragment row
+      static_assert(WITEMS % (2 * kWave) == 0, "whole steps of one or two items per lane");
+      float *wbuf = reinterpret_cast<float *>(smem) + wid * 32 * WRS;
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i) {
-            const int fr = wm * C::TM + i * 32;             // wave-uniform
-            if (fr >= c0 && fr < c0 + EPI_CR) {
+      for (int i = 0; i < C::FM; ++i) {
+        // the previous fragment's reads have landed before the slot is rewritten
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-              for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                  red[(fr - c0 + acc_row(v, l)) * EPI_RS + wn * C::TN + j * 32 + (l & 31)] =
-                      acc[i][j][v];
-            }
+          for (int v = 0; v < 16; ++v) wbuf[acc_row(v, l) * WRS + j * 32 + (l & 31)] = acc[i][j][v];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the wave's lanes
+        // two items at a time on tiles of at most four fragments per wave; on
+        // 256x256 tiles the second item's registers would spill
+        const bool PAIR = C::FM * C::FN <= 4;
+        const int NU = PAIR ? 2 : 1;
+        for (int it0 = l; it0 < WITEMS; it0 += NU * kWave) {
+          int grow[2], gcol[2], slot[2], r[2];
+          float sc[2], o[2][8];
+          bool live[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (u >= NU) break;
+            const int it = it0 + u * kWave;
+            const int rf = it / LPR, c8 = (it % LPR) * 8;
+            const int row = wm * C::TM + i * 32 + rf;
+            live[u] = m0 + row < M && n0 + wn * C::TN + c8 < N;
+            // dead items read a row and columns in bounds and add nothing
+            grow[u] = min(m0 + row, M - 1);
+            gcol[u] = min(n0 + wn * C::TN + c8, N - 8);
+            const f32x4 p0 = *reinterpret_cast<const f32x4 *>(wbuf + rf * WRS + c8);
+            const f32x4 p1 = *reinterpret_cast<const f32x4 *>(wbuf + rf * WRS + c8 + 4);
+            o[u][0] = p0[0]; o[u][1] = p0[1]; o[u][2] = p0[2]; o[u][3] = p0[3];
+            o[u][4] = p1[0]; o[u][5] = p1[1]; o[u][6] = p1[2]; o[u][7] = p1[3];
+            r[u] = live[u] ? s_rr[row] : 0;
+            slot[u] = s_rslot[row];
+            sc[u] = s_rsc[row];
           }
-        }
-        lgkm_barrier();
-        constexpr int ITEMS = EPI_CR * (BN / 8);
-        if constexpr (EPI_CR == BM) {
-          // one chunk (the accumulators are dead now): two items at a time
-          for (int it0 = tid; it0 < ITEMS; it0 += 2 * C::T) {
-            int grow[2], gcol[2], slot[2], r[2];
-            float sc[2], o[2][8];
-            bool live[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int it = it0 + u * C::T;
-              const int row = min(it, ITEMS - 1) / (BN / 8), c8 = (it % (BN / 8)) * 8;
-              live[u] = it < ITEMS && m0 + row < M && n0 + c8 < N;
-              // dead items read row and columns in bounds and add nothing
-              grow[u] = min(m0 + row, M - 1);
-              gcol[u] = min(n0 + c8, N - 8);
-              const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8);
-              const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8 + 4);
-              o[u][0] = p0[0]; o[u][1] = p0[1]; o[u][2] = p0[2]; o[u][3] = p0[3];
-              o[u][4] = p1[0]; o[u][5] = p1[1]; o[u][6] = p1[2]; o[u][7] = p1[3];
-              r[u] = live[u] ? s_rr[row] : 0;
-              slot[u] = s_rslot[row];
-              sc[u] = s_rsc[row];
-            }
+          if (PAIR) {
             lora_row8_pair<DORA>(g, grow, gcol, slot, r, sc, o);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              if (live[u]) stg16(g.Y + (int64_t)grow[u] * g.ldy + gcol[u], Elem<bf16_t>::pack(o[u]));
+          } else {
+            if (r[0] > 0) lora_row8<DORA>(g, grow[0], gcol[0], slot[0], r[0], sc[0], o[0]);
           }
-          continue;
-        }
-        for (int it = tid; it < ITEMS; it += C::T) {
-          const int row = it / (BN / 8), c8 = (it % (BN / 8)) * 8;
-          const int grow = m0 + c0 + row, gcol = n0 + c8;
-          if (grow >= M || gcol >= N) continue;       // N % 8 == 0: all 8 columns or none
-          float o[8];
-          const f32x4 p0 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8);
-          const f32x4 p1 = *reinterpret_cast<const f32x4 *>(red + row * EPI_RS + c8 + 4);
-          o[0] = p0[0]; o[1] = p0[1]; o[2] = p0[2]; o[3] = p0[3];
-          o[4] = p1[0]; o[5] = p1[1]; o[6] = p1[2]; o[7] = p1[3];
-          const int r = s_rr[c0 + row];
-          if (r > 0) lora_row8<DORA>(g, grow, gcol, s_rslot[c0 + row], r, s_rsc[c0 + row], o);
-          stg16(g.Y + (int64_t)grow * g.ldy + gcol, Elem<bf16_t>::pack(o));
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (u < NU && live[u]) stg16(g.Y + (int64_t)grow[u] * g.ldy + gcol[u], Elem<bf16_t>::pack(o[u]));
         }
       }
       return;
@@ -1031,8 +1094,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, bool WF8>
 hipError_t launch_bf16_w(const GemmArgs &g, bool lora, hipStream_t stream) {
-  const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  dim3 grid(((ntiles + 7) / 8) * 8);
+  dim3 grid(tile_grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN));
   dim3 block(WM * WN * KG * kWave);
   const bool dora = lora && g.dora;
   if (lora && g.Bn && dora)

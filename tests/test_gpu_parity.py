@@ -137,6 +137,33 @@ def test_random_cases(case, policy):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_target", [600, 2300])
+def test_segment_lengths_around_row_blocks(n_target, dtype):
+    """Segments of 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129 rows
+    and longer, in shuffled order, so segments start on and off multiples of
+    the shrink / expand row block (16 rows below 2048 rows, 64 from there on)
+    and long segments span several blocks; batches on both sides of 2048."""
+    rng = np.random.default_rng(n_target)
+    lens = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 3, 2]
+    while sum(lens) < n_target:
+        lens.append(int(rng.integers(1, 90)))
+    rng.shuffle(lens)
+    n_slots = len(lens) + 2
+    slots = rng.permutation(n_slots)[:len(lens)]
+    slots[3] = -1                                   # one base-only run
+    row_slot = np.concatenate([np.full(L, s) for L, s in zip(lens, slots)]).astype(np.int32)
+    ranks = rng.choice([8, 16, 32, 64], size=n_slots).astype(np.int32)
+    ranks[slots[5]] = 0                             # one rank-0 run
+    w = wl.build_workload("lengths", dtype, np.random.SeedSequence(n_target), len(row_slot), 136,
+                          264, row_slot, ranks, 64, 1.0, 0.02, 0.02)
+    say("segment lengths", n_target, dtype, len(row_slot))
+    r = run_hip(w)
+    check_metadata(w, r)
+    say("errors", check_values(w, r))
+    base_rows_bitwise(w, r)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fingerprint_mapping_exact(dtype):
     """Fingerprint adapters: the increment of a row on slot a is exactly
     s_a (a + 1) x[a mod d_in] (exact in fp32 here), so the expand into zeros

@@ -5,8 +5,10 @@ tile switches from one staged MFMA increment per segment to the row
 epilogue when its rows hold more than a few LoRA runs (decode rows, each of
 its own adapter), so the cases here put many short runs, a run count on
 either side of that switch, and prefill runs mixed with decode rows into
-tiles of both sizes.  Same tolerances and bitwise properties as the plain
-layer; DoRA factors and an FP8 weight through the same epilogue."""
+tiles of both sizes, and decode rows at either end of a grid of several
+waves (where the end tile with more runs is scheduled first).  Same
+tolerances and bitwise properties as the plain layer; DoRA factors and an
+FP8 weight through the same epilogue."""
 import math
 
 import numpy as np
@@ -173,3 +175,22 @@ def test_fp8_weight_many_runs(n, d_out):
     base = [i for i in range(w.n) if keys[i] < 0]
     tb = torch.as_tensor(base, device=DEV)
     assert torch.equal(Yf[tb], Yb[tb])
+
+
+@pytest.mark.parametrize("where", ["first", "last", "both"])
+def test_decode_rows_at_either_end_of_a_multi_wave_grid(where):
+    """Decode rows (one random slot each) at the start, the end or both ends
+    of a 1300-row batch with a prefill request in between, on a grid of more
+    than one wave of 256 x 256 tiles, so the tile with more runs is ordered
+    first (or, with both ends alike, neither is)."""
+    rng = np.random.default_rng({"first": 711, "last": 712, "both": 713}[where])
+    dec = lambda k: rng.integers(-1, 40, k)
+    pre = np.full(1300 - 200 if where != "both" else 1300 - 400, 7)
+    parts = {"first": [dec(200), pre], "last": [pre, dec(200)], "both": [dec(200), pre, dec(200)]}
+    row_slot = np.concatenate(parts[where]).astype(np.int32)
+    ranks = rng.choice([8, 16, 32, 64], size=40)
+    w = _mapped(714, row_slot, 64, 12288, ranks)
+    r = run_hip(w)
+    check_metadata(w, r)
+    say("either end", where, check_values(w, r))
+    base_rows_bitwise(w, r)
