@@ -256,25 +256,32 @@ __device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&gr
 }
 
 // Tile order of the MFMA kernels.  Workgroup b runs on XCD b % 8 (the
-// dispatcher deals consecutive ids round robin over the eight XCDs).  With
-// at least 8 N-tiles, XCD x owns N-tiles [x tiles_n / 8, (x + 1) tiles_n / 8)
-// of every M-tile and walks them in groups of 8 M-tiles sweeping its
-// N-tiles; with fewer, XCD x takes the x-th eighth of that grouped order
-// over all tiles.  An M-tile `heavy` (>= 0) comes before the groups, all of
-// its tiles of the XCD first (the others keep their order).  Returns false
-// for a workgroup past its XCD's tiles.  tile_grid is the launch size that
-// covers every tile.
+// dispatcher deals consecutive ids round robin over the eight XCDs), and
+// each XCD walks its tiles in groups of 8 M-tiles sweeping N, so that
+// neighbours share operand tiles in one L2.  Batches of at most
+// kHeavyMaxTilesM M-tiles with at least 8 N-tiles: XCD x owns N-tiles
+// [x tiles_n / 8, (x + 1) tiles_n / 8) of every M-tile, so any M-tile's work
+// spreads over all eight XCDs, and an M-tile `heavy` (>= 0) comes before the
+// groups, all of its tiles of the XCD first.  Larger batches: XCD x takes
+// the x-th eighth of the grouped order over all tiles (each XCD then holds
+// a few M-tiles' X rows and streams W, half the L2 misses of the N split at
+// 67 M-tiles).  Returns false for a workgroup past its XCD's tiles.
+// tile_grid is the launch size that covers every tile.
 constexpr int kTileGroup = 8;
 constexpr int kHeavyMaxTilesM = 32;
 constexpr int kCUs = 256;   // compute units of an MI355X
+__host__ __device__ inline bool n_split(int tiles_m, int tiles_n) {
+  return tiles_n >= 8 && tiles_m <= kHeavyMaxTilesM;
+}
 __host__ __device__ inline int tile_grid(int tiles_m, int tiles_n) {
-  return tiles_n >= 8 ? 8 * ((tiles_n + 7) / 8) * tiles_m : (tiles_m * tiles_n + 7) / 8 * 8;
+  return n_split(tiles_m, tiles_n) ? 8 * ((tiles_n + 7) / 8) * tiles_m
+                                   : (tiles_m * tiles_n + 7) / 8 * 8;
 }
 __device__ __forceinline__ bool tile_order(int b, int tiles_m, int tiles_n, int heavy, int &m_idx,
                                            int &n_idx) {
   const int x = b & 7, j = b >> 3;
   int n_lo, nx, t;
-  if (tiles_n >= 8) {
+  if (n_split(tiles_m, tiles_n)) {
     n_lo = x * tiles_n / 8;
     nx = (x + 1) * tiles_n / 8 - n_lo;
     if (j >= nx * tiles_m) return false;
