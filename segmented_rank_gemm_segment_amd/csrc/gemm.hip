@@ -150,11 +150,13 @@ __device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi)
 
 // LoRA term of one output row over 8 consecutive columns, added to o in fp32:
 // o[e] += sc sum_{k < r} H[grow][qoff + k] Bt_slot[qoff + k][gcol + e], k
-// ascending, read in chunks of 8 rank rows (rows at or past r inside the
-// chunk are read inside the projection's block and skipped); then, with
-// DoRA, the slot's column factors.  qoff is the rank offset of the columns'
+// ascending, read in chunks of 8 rank rows; then, with DoRA, the slot's
+// column factors.  r need not be a multiple of 8: a chunk's rank rows at or
+// past r are read inside the projection's block (whose width rs is a
+// multiple of 8) and skipped.  qoff is the rank offset of the columns'
 // projection (offsets of projections are multiples of 8, so all 8 columns
 // share it).  Shared by both row epilogues, so both give the same bits.
+// (Loading two chunks per step measured no faster on 64x64 tiles.)
 template <bool DORA>
 __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol, int slot, int r,
                                           float sc, float (&o)[8]) {
@@ -163,7 +165,7 @@ __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol,
   const bf16_t *bt = g.Bt + ((int64_t)slot * g.r_max + qoff) * N + gcol;
   const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
   float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < r; kc += 8) {      // kc + 8 <= rs: in the block
+  for (int kc = 0; kc < r; kc += 8) {      // kc < r <= rs: the chunk is in the block
     const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
     const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
     const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
@@ -192,7 +194,7 @@ __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol,
 
 // lora_row8 for two (row, 8 columns) items at once, so that the loads of
 // both are in flight together: chunk kc of an item whose rank ends earlier
-// re-reads its last chunk (in the block) and adds nothing.  Each item's sum
+// re-reads its first chunk (in the block) and adds nothing.  Each item's sum
 // is formed in the same order as lora_row8's, so the bits are the same.
 template <bool DORA>
 __device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&grow)[2],
@@ -219,7 +221,9 @@ __device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&gr
     u32x4 b[2][8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int kk = min(kc, max(r[u], 8) - 8);   // in the block
+      // an item whose rank ends before kc re-reads its first chunk (in the
+      // block) and adds nothing
+      const int kk = kc < r[u] ? kc : 0;
       h0[u] = *reinterpret_cast<const f32x4 *>(hp[u] + kk);
       h1[u] = *reinterpret_cast<const f32x4 *>(hp[u] + kk + 4);
 #pragma unroll
