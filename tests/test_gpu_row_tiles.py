@@ -196,13 +196,16 @@ def test_decode_rows_at_either_end_of_a_multi_wave_grid(where):
     base_rows_bitwise(w, r)
 
 
+@pytest.mark.parametrize("runs", [False, True], ids=["rows", "requests"])
 @pytest.mark.parametrize("n,d_out", [(1024, 264), (600, 11008), (300, 264)])
-def test_ranks_not_multiples_of_eight(n, d_out):
-    """Ranks 1, 5, 12, 24, 33, 47, 64 (a pool of r_max 64): each row epilogue
-    reads whole chunks of 8 rank rows and must skip the rows at or past the
-    rank, also when another item's rank runs further (the two-item step)."""
+def test_ranks_not_multiples_of_eight(n, d_out, runs):
+    """Ranks 1, 5, 12, 24, 33, 47, 64 (a pool of r_max 64): each epilogue
+    reads whole chunks of rank rows and must skip the rows at or past the
+    rank, also when another item's rank runs further (the two-item step);
+    random rows take the row epilogues, contiguous requests the staged MFMA
+    term of the larger tiles."""
     ranks = [1, 5, 12, 24, 33, 47, 64, 12, 5]
-    w = wl.make_random(715, n, 136, d_out, len(ranks), 64, ranks=ranks, p_base=0.1)
+    w = wl.make_random(715, n, 136, d_out, len(ranks), 64, ranks=ranks, p_base=0.1, runs=runs)
     r = run_hip(w)
     check_metadata(w, r)
     say("odd ranks", n, d_out, check_values(w, r))
