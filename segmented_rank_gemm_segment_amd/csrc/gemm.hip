@@ -399,18 +399,20 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   const int n0 = n_idx * BN;
 
   // Small tiles (two K groups) finish row by row: thread tid owns tile row
-  // tid / (BN / 8) and 8 consecutive columns (see the end of the kernel).
-  // With the LoRA term, the row's segment id is loaded before the first
-  // DMA and its segment's rank, slot and scale right after the first stage
-  // has landed, so all three have long arrived by the epilogue.  The loads
-  // are issued by hand (the compiler would sink them to their uses) and
-  // waited for explicitly.
+  // tid / (BN / 8) and 8 consecutive columns (see the end of the kernel);
+  // in larger tiles thread tid < BM holds tile row tid's metadata for the
+  // LoRA term.  The row's segment id is loaded before the first DMA and its
+  // segment's rank, slot and scale right after the first stage has landed,
+  // so all have long arrived by the epilogue.  The loads are issued by hand
+  // (the compiler would sink them to their uses) and waited for explicitly.
   constexpr bool ROWEPI = KG > 1;
   static_assert(!ROWEPI || C::T * 8 == BM * BN, "row epilogue: 8 outputs per thread");
-  const int e_row = tid / (BN / 8), e_c8 = (tid % (BN / 8)) * 8;
+  static_assert(ROWEPI || C::T >= BM, "one tile row per thread");
+  const int e_row = ROWEPI ? tid / (BN / 8) : tid, e_c8 = (tid % (BN / 8)) * 8;
+  const bool e_own = ROWEPI || tid < BM;            // the thread holds row e_row's metadata
   int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
-  if constexpr (ROWEPI && LORA != 0)
-    e_seg = gload_b32(g.row_segment + min(m0 + e_row, M - 1));
+  if constexpr (LORA != 0)
+    if (e_own) e_seg = gload_b32(g.row_segment + min(m0 + e_row, M - 1));
   // FP8 weight: the thread's 8 column scales, requested now as well
   u32x4 e_ws0 = u32x4{0, 0, 0, 0}, e_ws1 = u32x4{0, 0, 0, 0};
   if constexpr (ROWEPI && WF8) {
@@ -566,12 +568,14 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   // stage 0 landed (the later stages may stay in flight)
   wait_ahead<C::IPW>(min(STAGES - 1, KT - 1));
-  if constexpr (ROWEPI && LORA != 0) {
+  if constexpr (LORA != 0) {
     // the segment id was loaded before stage 0, so it has landed too
     asm volatile("" : "+v"(e_seg));
-    e_r = gload_b32(g.seg_rank + e_seg);
-    e_slot = gload_b32(g.seg_slot + e_seg);
-    e_scb = gload_b32(g.seg_scale + e_seg);
+    if (e_own) {
+      e_r = gload_b32(g.seg_rank + e_seg);
+      e_slot = gload_b32(g.seg_slot + e_seg);
+      e_scb = gload_b32(g.seg_scale + e_seg);
+    }
   }
   if (ktail && KT == 1) zero_tail(0, kg0);
   lgkm_barrier();
@@ -751,13 +755,11 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // DoRA: slot of each tile row (-1 = not rescaled), read by the store
     int *s_rowslot = reinterpret_cast<int *>(smem + 2 * BM * RBL + BN * RBL + 16);
     auto sw = [](int c, int r) { return ((c ^ ((r >> 1) & 7)) * 16); };
-    // this thread's tile row (threads past BM take no row)
-    int my_seg = -1;
-    if (tid < BM && m0 + tid < M) {
-      const int sg = g.row_segment[m0 + tid];
-      if (g.seg_rank[sg] > 0) my_seg = sg;
-    }
-    int *s_rr = reinterpret_cast<int *>(smem + EPI_META);   // per row: rank (0: no term)
+    // this thread's tile row (threads past BM take no row): its segment if
+    // that has a LoRA term (all DMAs and the metadata loads are done)
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_seg), "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
+    const int my_seg = (tid < BM && m0 + tid < M && e_r > 0) ? e_seg : -1;
+    int *s_rr = reinterpret_cast<int *>(smem + EPI_META);   // per row: segment, later rank
     int *s_rslot = s_rr + BM;                               //          slot
     float *s_rsc = reinterpret_cast<float *>(s_rslot + BM); //          scale
     int *s_runs = reinterpret_cast<int *>(s_rsc + BM);
@@ -786,16 +788,9 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       // fragment's registers are free once it is in LDS; no workgroup
       // barrier is needed.
       if (tid < BM) {
-        int r = 0, slot = 0;
-        float sc = 0.f;
-        if (my_seg >= 0) {
-          r = g.seg_rank[my_seg];
-          slot = g.seg_slot[my_seg];
-          sc = g.seg_scale[my_seg];
-        }
-        s_rr[tid] = r;
-        s_rslot[tid] = slot;
-        s_rsc[tid] = sc;
+        s_rr[tid] = my_seg >= 0 ? e_r : 0;
+        s_rslot[tid] = my_seg >= 0 ? e_slot : 0;
+        s_rsc[tid] = my_seg >= 0 ? __int_as_float(e_scb) : 0.f;
       }
       lgkm_barrier();                                 // the row metadata is visible
       constexpr int WRS = C::TN + 4;                  // row stride of a wave's slot
@@ -867,9 +862,16 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       const int u = __builtin_amdgcn_readfirstlane(*s_next);
       if (u == INT_MAX) break;
       prev = u;
-      const int slot = g.seg_slot[u];
-      const int r = g.seg_rank[u];
-      const float sc = g.seg_scale[u];
+      // u's slot, rank and scale from the rows of u (all write the same)
+      if (my_seg == u) {
+        s_next[1] = e_slot;
+        s_next[2] = e_r;
+        s_next[3] = e_scb;
+      }
+      lgkm_barrier();
+      const int slot = __builtin_amdgcn_readfirstlane(s_next[1]);
+      const int r = __builtin_amdgcn_readfirstlane(s_next[2]);
+      const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_next[3]));
       const int rs = g.proj.rs;
       const int R = rank_bucket(r, g.policy, rs);
       const int KS = (R + 15) / 16;
@@ -881,20 +883,29 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       for (int q = q_lo; q <= q_hi; ++q) {
       const int qoff = q * rs;
       const int c_lo = g.proj.col_off[q], c_hi = g.proj.col_off[q + 1];
-      // A: (row, chunk) items
-      for (int it = tid; it < BM * NC; it += C::T) {
+      // A: (row, chunk) items, at most JA per thread, then B likewise: each
+      // operand's loads are all issued before its first LDS store (both at
+      // once would spill on 256x256 tiles).  Loads are unconditional (rows
+      // past M and chunks past rs read in bounds) and masked where used; a
+      // row is in u by the tile's row -> segment table.
+      constexpr int JA = (BM * 8 + C::T - 1) / C::T;
+      float4 ha[JA], hb[JA];
+#pragma unroll
+      for (int j = 0; j < JA; ++j) {
+        const int it = min(tid + j * C::T, BM * NC - 1);
         const int row = it / NC, c = it - (it / NC) * NC;
-        const int grow = m0 + row;
-        float h[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const bool in_u = grow < M && g.row_segment[grow] == u;
+        const float *hp = g.H + (int64_t)min(m0 + row, M - 1) * g.r_max + qoff + min(c * 8, rs - 8);
+        ha[j] = *reinterpret_cast<const float4 *>(hp);
+        hb[j] = *reinterpret_cast<const float4 *>(hp + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < JA; ++j) {
+        const int it = tid + j * C::T;
+        if (it >= BM * NC) break;
+        const int row = it / NC, c = it - (it / NC) * NC;
         // chunks past rs (k >= R >= r, only when rs = 8) stay zero
-        if (in_u && c * 8 < rs) {
-          const float *hp = g.H + (int64_t)grow * g.r_max + qoff + c * 8;
-          const float4 h0 = *reinterpret_cast<const float4 *>(hp);
-          const float4 h1 = *reinterpret_cast<const float4 *>(hp + 4);
-          h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
-          h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
-        }
+        const bool in_u = s_rr[row] == u && c * 8 < rs;
+        const float h[8] = {ha[j].x, ha[j].y, ha[j].z, ha[j].w, hb[j].x, hb[j].y, hb[j].z, hb[j].w};
         u32x4 phi, plo;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -909,16 +920,30 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
         *reinterpret_cast<u32x4 *>(s_alo + row * RBL + sw(c, row)) = plo;
       }
       // B: rank values of column col, k in chunk c, zero for k >= r
+      constexpr int JB = (BN * 8 + C::T - 1) / C::T;
+      u32x4 bv[JB];
       if constexpr (LORA == 2) {
         const bf16_t *bn = g.Bn + (int64_t)slot * N * g.r_max;
-        for (int it = tid; it < BN * NC; it += C::T) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const int it = min(tid + j * C::T, BN * NC - 1);
           const int col = it / NC, c = it - (it / NC) * NC;
           const int colc = min(n0 + col, N - 1);     // columns past N: never stored
-          const bool in_q = colc >= c_lo && colc < c_hi;
           // a chunk past rs (only when rs = 8) is read from the block's
           // first chunk and masked below
-          u32x4 v = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max + qoff +
-                                                      min(c * 8, rs - 8));
+          bv[j] = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max + qoff +
+                                                   min(c * 8, rs - 8));
+        }
+      }
+      if constexpr (LORA == 2) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const int it = tid + j * C::T;
+          if (it >= BN * NC) break;
+          const int col = it / NC, c = it - (it / NC) * NC;
+          const int colc = min(n0 + col, N - 1);
+          const bool in_q = colc >= c_lo && colc < c_hi;
+          u32x4 v = bv[j];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const int k = c * 8 + e2 * 2;
