@@ -467,6 +467,38 @@ def cpu_baseline(w, budget_s=12.0, single_core_s=6.0):
     return out
 
 
+def cpu_baseline_sampled(w, k=128, budget_s=6.0):
+    """The oracle on a large batch, timed on a seeded sample of k rows (the
+    rows are independent) and extrapolated linearly to the whole batch; the
+    metadata build is timed on the whole batch, once per pass."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rows = np.sort(np.random.default_rng(0).choice(w.n, size=min(k, w.n), replace=False))
+    runs, t_meta, t_rows, t0 = 0, 0.0, 0.0, time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)
+        b = time.perf_counter()
+        oracle.lora_forward(w.X, w.W, w.A, w.B, w.row_slot, w.slot_rank, w.slot_alpha, w.r_max,
+                            w.dtype, rows=rows)
+        c = time.perf_counter()
+        t_meta += b - a
+        t_rows += c - b
+        runs += 1
+        if c - t0 >= budget_s:
+            break
+    per_batch = (t_meta + t_rows * w.n / len(rows)) / runs
+    return {"value": round(w.n / per_batch, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{runs} passes of {len(rows)} seeded rows of the {w.n}-row batch in "
+                      f"{t_rows:.1f} s, extrapolated linearly; metadata on the whole batch "
+                      f"({t_meta:.1f} s)"}
+
+
 def dora_entry(w, fig, m, paths, args):
     """The headline workload with every slot a DoRA adapter: step and kernel
     times against the plain pool's, and the column-factor preparation."""
@@ -682,6 +714,8 @@ def main():
         }
         if vendor_entry(f3, m3):
             out["prefill"]["vendor_base_gemm"] = vendor_entry(f3, m3)
+        if not args.no_cpu_baseline:
+            out["prefill"]["cpu_baseline"] = cpu_baseline_sampled(w3)
         del w3
     if not args.no_dora:
         out["dora"] = dora_entry(w, fig, m, paths, args)
