@@ -846,7 +846,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       return;
     }
     if constexpr (DORA) {
-      if (tid < BM) s_rowslot[tid] = my_seg >= 0 ? g.seg_slot[my_seg] : -1;
+      if (tid < BM) s_rowslot[tid] = my_seg >= 0 ? e_slot : -1;
     }
     int prev = -1;
     while (true) {
