@@ -57,7 +57,12 @@ __global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
   // ones, segment-major (seg_item_major)
   const bool major = long_min != INT_MAX;
   const int n_items = major ? nb * seg_cap : nb + seg_cap;
+  // items are walked in ascending order; segment heads past the batch's
+  // segment count are empty, and so are all later ones
+  const int S = __builtin_amdgcn_readfirstlane(*num_segments);
   for (int item = blockIdx.y; item < n_items; item += gridDim.y) {
+    if (!major && item >= nb && item - nb >= S) break;
+    if (major && item % seg_cap >= S) continue;
     const SegItem it =
         major ? seg_item_major(item, rb, seg_cap, num_segments, seg_rank, seg_off, seg_slot,
                                nullptr)
@@ -367,8 +372,12 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
   // the lane's columns belong to one projection (its offsets are multiples
   // of 8): its rank rows start at q * rs in the slot and in H
   const int qoff = proj_of(proj, active ? col : 0) * proj.rs;
-  // position blocks first, then the segments' first blocks (seg_item)
+  // position blocks first, then the segments' first blocks (seg_item), in
+  // ascending order: heads past the batch's segment count are empty, and so
+  // are all later ones
+  const int S = __builtin_amdgcn_readfirstlane(*num_segments);
   for (int item = blockIdx.y; item < nb + seg_cap; item += gridDim.y) {
+    if (item >= nb && item - nb >= S) break;
     const SegItem it = seg_item(item, nb, rb, seg_cap, token_indices, row_segment, num_segments,
                                 seg_rank, seg_off, seg_slot, seg_scale);
     if (!it.ok) continue;
@@ -403,9 +412,14 @@ inline int seg_bound(int n_rows, int n_slots, int max_segments) {
 }
 
 // Workgroup rows for `items` work items when each row has `x` workgroups:
-// one row per item, but at most ~16k workgroups in all (the rest stride).
+// one row per item, but at most kMaxItemWGs workgroups in all; the rows then
+// walk the items with a stride.  Several rounds of workgroups at these
+// kernels' occupancy (2 or fewer per CU at 256 VGPRs), so a large bound on
+// the segment count (a 1000-slot pool) no longer launches thousands of
+// empty workgroups.
+constexpr int kMaxItemWGs = 2048;
 inline int grid_items(int items, int x) {
-  int cap = 16384 / (x > 0 ? x : 1);
+  int cap = kMaxItemWGs / (x > 0 ? x : 1);
   cap = cap > 1 ? cap : 1;
   return items < cap ? (items > 0 ? items : 1) : cap;
 }
