@@ -44,7 +44,7 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // lane l holds pair l % 32), then over the waves through LDS in wave order.
 // ----------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kShW * kWave) void shrink_kernel(
+__global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
     const T *__restrict__ X, int64_t ldx, const T *__restrict__ A, const int32_t *token_indices,
     const int32_t *row_segment, const int32_t *seg_off, const int32_t *seg_slot,
     const int32_t *seg_rank, const int32_t *num_segments, int r_max, int rs, int d_in, int policy,

@@ -104,22 +104,28 @@ __device__ __forceinline__ void shrink_rows(const T *__restrict__ X, int64_t ldx
           xv[u][q] = ldg16(X + (int64_t)__builtin_amdgcn_readlane(tv, q) * ldx + cc);
       }
       __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use
+      // each token row of the group unpacked once per chunk, each adapter
+      // row once; every (row, rank row) sum still runs over the chunks and
+      // their elements in order
 #pragma unroll
       for (int u = 0; u < kShCU; ++u) {
         const bool ok = cb + u * kShW * CH + lane * V < d_in;
+        float xf[kShRQ][V];
 #pragma unroll
         for (int q = 0; q < kShRQ; ++q) {
-          float xf[V];
-          Elem<T>::unpack(xv[u][q], xf);
+          Elem<T>::unpack(xv[u][q], xf[q]);
 #pragma unroll
-          for (int e = 0; e < V; ++e) xf[e] = (ok && q < nq) ? xf[e] : 0.f;
+          for (int e = 0; e < V; ++e) xf[q][e] = (ok && q < nq) ? xf[q][e] : 0.f;
+        }
 #pragma unroll
-          for (int kk = 0; kk < kShRB; ++kk) {
-            float af[V];
-            Elem<T>::unpack(av[u][kk], af);
+        for (int kk = 0; kk < kShRB; ++kk) {
+          float af[V];
+          Elem<T>::unpack(av[u][kk], af);
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc[q * kShRB + kk] = fmaf(af[e], xf[e], acc[q * kShRB + kk]);
-          }
+          for (int q = 0; q < kShRQ; ++q)
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+              acc[q * kShRB + kk] = fmaf(af[e], xf[q][e], acc[q * kShRB + kk]);
         }
       }
     }
