@@ -79,39 +79,45 @@ __global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
 
 // ----------------------------------------------------------------------------
 // shrink of long segments (prefill): a tiled MFMA product per segment,
-//   H[rows of s][0:64] = X[token_indices[rows]] A_slot[0:64]^T,
-// 64 rows x 64 rank columns per tile, K = d_in streamed through a 6-stage
-// LDS ring with direct global->LDS loads (the row gather is free: every
-// lane supplies its own source address).  Each X row is read once per
-// segment tile instead of once per rank row.  Rank rows past R are not
-// fetched (their loads re-read row R-1); columns k >= r are not stored.
+//   H[rows of s][0:SN] = X[token_indices[rows]] A_slot[0:SN]^T,
+// SM rows x SN rank columns per tile (one 32 x 32 MFMA block per wave),
+// K = d_in streamed through a 6-stage LDS ring with direct global->LDS
+// loads (the row gather is free: every lane supplies its own source
+// address).  Each X row is read once per segment tile instead of once per
+// rank row.  Work items are the position blocks of the segment order
+// (seg_item with rb = SM) of segments of at least kLongRows rows, times the
+// rank tiles (blockIdx.x).  Rank rows past R are not fetched (their loads
+// re-read row R-1); columns k >= r are not stored.
 // ----------------------------------------------------------------------------
 constexpr int kLongRows = 128;   // segments at least this long take the MFMA path
 constexpr int kMfmaShrinkMinBatch = 2048;
-constexpr int kSM = 64, kSN = 64, kSStages = 6;
+constexpr int kSStages = 6;
 
-__global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
+template <int SM, int SN>
+__global__ __launch_bounds__((SM / 32) * (SN / 32) * kWave) void shrink_mfma_kernel(
     const bf16_t *__restrict__ X, int64_t ldx, const bf16_t *__restrict__ A,
-    const int32_t *token_indices, const int32_t *seg_off, const int32_t *seg_slot,
-    const int32_t *seg_rank, const int32_t *num_segments, int r_max, int rs, int d_in, int policy,
-    int tiles_per_seg, int rank_tiles, int cap_items, float *__restrict__ H) {
-  constexpr int NW = 4;
-  constexpr int AI = kSM / 8 / NW, BI = kSN / 8 / NW, IPW = AI + BI;
-  constexpr int STAGE = (kSM + kSN) * 128;
+    const int32_t *token_indices, const int32_t *row_segment, const int32_t *seg_off,
+    const int32_t *seg_slot, const int32_t *seg_rank, const int32_t *num_segments, int r_max,
+    int rs, int d_in, int policy, int nb, int seg_cap, float *__restrict__ H) {
+  constexpr int NWN = SN / 32;                      // waves along the rank columns
+  constexpr int NW = (SM / 32) * NWN;
+  constexpr int AI = SM / 8 / NW, BI = SN / 8 / NW, IPW = AI + BI;
+  static_assert(AI >= 1 && BI >= 1 && SM % (8 * NW) == 0 && SN % (8 * NW) == 0, "DMA split");
+  constexpr int STAGE = (SM + SN) * 128;
   constexpr int BK = 64;
   __shared__ __align__(16) unsigned char smem[kSStages * STAGE];
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / NWN, wn = wid % NWN;
   // 128-byte LDS rows, chunk c of row r at c ^ ((r >> 1) & 7): 16
   // consecutive rows at one chunk hit 16 distinct bank groups
   const int r8 = l >> 3;
   const uint32_t sbase = lds_offset(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * AI * 1024);
-  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + kSM * 128 + wid * BI * 1024);
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + SM * 128 + wid * BI * 1024);
   const int a_row_off = (wm * 32 + (l & 31)) * 128;
-  const int b_row_off = kSM * 128 + (wn * 32 + (l & 31)) * 128;
+  const int b_row_off = SM * 128 + (wn * 32 + (l & 31)) * 128;
   int chunk_off[BK / 16];
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = (((kk * 2 + (l >> 5)) ^ ((l >> 1) & 7)) * 16);
@@ -122,23 +128,20 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
   for (int i = 0; i < BI; ++i) blc[i] = (l & 7) ^ ((((wid * BI + i) * 8 + r8) >> 1) & 7);
   const int KT = (d_in + BK - 1) / BK;
   const bool ktail = (d_in % BK) != 0;
-  const int S = *num_segments;
+  const int S = __builtin_amdgcn_readfirstlane(*num_segments);
+  const int rt = blockIdx.x;                        // rank tile of SN pool rank rows
 
-  for (int item = blockIdx.x; item < cap_items; item += gridDim.x) {
-    // item = (segment, row tile, rank tile of 64 pool rank rows)
-    const int s = item / (tiles_per_seg * rank_tiles);
-    const int rem = item - s * (tiles_per_seg * rank_tiles);
-    const int t = rem / rank_tiles;
-    const int rt = rem - t * rank_tiles;
-    const int r = seg_rank[s];
-    const int o0 = seg_off[s], o1 = seg_off[s + 1];
-    const int slot = seg_slot[s];
-    if (s >= S) break;
-    const int R = rank_bucket(r, policy, rs);
-    if (R == 0 || o1 - o0 < kLongRows) continue;
-    const int p0 = o0 + t * kSM;
-    if (p0 >= o1) continue;
-    const int p1 = min(o1, p0 + kSM);
+  // position blocks first, then the segments' first blocks (seg_item), in
+  // ascending order: heads past the batch's segment count end the walk
+  for (int item = blockIdx.y; item < nb + seg_cap; item += gridDim.y) {
+    if (item >= nb && item - nb >= S) break;
+    const SegItem it = seg_item(item, nb, SM, seg_cap, token_indices, row_segment, num_segments,
+                                seg_rank, seg_off, seg_slot, nullptr);
+    if (!it.ok || it.o1 - it.o0 < kLongRows) continue;
+    const int R = rank_bucket(it.r, policy, rs);
+    if (R == 0) continue;
+    const int p0 = it.p0, p1 = it.p1;
+    const int slot = it.slot, r = it.r;
 
     const bf16_t *asrc[AI];
     const bf16_t *bsrc[BI];
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
       // pool rank row kg, kl rows into its projection's block; rows past the
       // processed width R re-read the block's last processed row (in the
       // slot) and are not stored
-      const int kg = rt * kSN + (wid * BI + i) * 8 + r8;
+      const int kg = rt * SN + (wid * BI + i) * 8 + r8;
       const int kl = kg % rs;
       const int k = min(kl < R ? kg : kg - kl + R - 1, r_max - 1);
       bsrc[i] = A + ((int64_t)slot * r_max + k) * d_in + blc[i] * 8;
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < BI; ++i)
           if (kt * BK + blc[i] * 8 >= d_in)
-            *reinterpret_cast<u32x4 *>(st + kSM * 128 + (wid * BI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4 *>(st + SM * 128 + (wid * BI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
       }
       lgkm_barrier();
       if (kt + kSStages - 1 < KT) issue((kt + kSStages - 1) % kSStages, (kt + kSStages - 1) * BK);
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(4 * kWave) void shrink_mfma_kernel(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
       }
     }
-    const int k = rt * kSN + wn * 32 + (l & 31);
+    const int k = rt * SN + wn * 32 + (l & 31);
     const bool kok = k < r_max && k % rs < r;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -426,6 +429,20 @@ inline int grid_items(int items, int x) {
 
 }  // namespace
 
+template <int SM, int SN>
+void launch_shrink_mfma(const void *X, int64_t ldx, const SegView &seg, const PoolView &pool,
+                        float *H, hipStream_t stream) {
+  const int n = seg.n_rows;
+  const int nb = (n + SM - 1) / SM;
+  const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
+  const int nrt = (pool.r_max + SN - 1) / SN;        // rank tiles of SN pool rank rows
+  dim3 grid(nrt, grid_items(nb + S_bound, nrt));
+  hipLaunchKernelGGL((shrink_mfma_kernel<SM, SN>), grid, dim3((SM / 32) * (SN / 32) * kWave), 0,
+                     stream, (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
+                     seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
+                     pool.r_max, pool.proj.rs, pool.d_in, pool.policy, nb, S_bound, H);
+}
+
 // Rows per work item: short blocks spread the rows of a long segment over
 // many workgroups (a Zipf-skewed decode batch has segments of a hundred rows
 // next to single rows); large batches take longer blocks, which read each
@@ -465,18 +482,9 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
                        pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
                        long_min, H);
   }
-  if (use_mfma) {
-    const int tps = (n + kSM - 1) / kSM;
-    const int nrt = (pool.r_max + kSN - 1) / kSN;   // rank tiles of 64 pool rank rows
-    // one workgroup per (segment, row tile, rank tile) item up to 2048, so a
-    // workgroup walks at most a few (mostly empty) items
-    const int items = S_bound * tps * nrt;
-    const int g = items < 2048 ? items : 2048;
-    hipLaunchKernelGGL(shrink_mfma_kernel, dim3(g), dim3(4 * kWave), 0, stream, (const bf16_t *)X,
-                       ldx, (const bf16_t *)pool.A, seg.token_indices, seg.seg_off, seg.seg_slot,
-                       seg.seg_rank, seg.num_segments, pool.r_max, pool.proj.rs, pool.d_in,
-                       pool.policy, tps, nrt, S_bound * tps * nrt, H);
-  }
+  // (32 x 32 tiles, one wave each, measured slower at d_in 8192: 61 against
+  // about 50 us, too few bytes in flight per CU)
+  if (use_mfma) launch_shrink_mfma<64, 64>(X, ldx, seg, pool, H, stream);
   return hipGetLastError();
 }
 

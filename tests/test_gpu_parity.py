@@ -121,6 +121,8 @@ CASES = [
     # 128 x 128 tiles (few 256 x 256 tiles) and 256 x 256 tiles with a K tail
     (111, 1024, 256, 1024, 12, 64, 0.1, "bf16", False),
     (112, 1100, 200, 8200, 7, 64, 0.1, "bf16", True),
+    # long segments at a long, ragged d_in (MFMA shrink K tail)
+    (113, 2100, 8200, 136, 6, 64, 0.1, "bf16", True),
 ]
 
 
