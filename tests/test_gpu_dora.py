@@ -133,6 +133,7 @@ DCASES = [
     (315, 2100, 328, 264, 5, 32, 0.2, "bf16", True),
     (316, 70, 64, 64, 4, 64, 0.1, "f32", True),
     (317, 513, 200, 120, 17, 32, 0.1, "f32", False),
+    (318, 400, 136, 4104, 9, 32, 0.1, "bf16", True),     # two-stage small tiles
 ]
 
 

@@ -123,6 +123,10 @@ CASES = [
     (112, 1100, 200, 8200, 7, 64, 0.1, "bf16", True),
     # long segments at a long, ragged d_in (MFMA shrink K tail)
     (113, 2100, 8200, 136, 6, 64, 0.1, "bf16", True),
+    # small batches with more 64 x 64 tiles than CUs (two-stage small tiles),
+    # ragged N and K tails
+    (114, 333, 200, 4168, 40, 32, 0.1, "bf16", False),
+    (115, 500, 1032, 2056, 9, 64, 0.1, "bf16", True),
 ]
 
 
