@@ -576,7 +576,13 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   };
 
   // stage 0 landed (the later stages may stay in flight)
-  wait_ahead<C::IPW>(min(STAGES - 1, KT - 1));
+  // The first stage is waited for together with every prologue stage:
+  // DMAs issued back to back can land out of order (with a one-stage
+  // allowance a stage issued right after stage 0 counted as landed while
+  // part of stage 0 had not, on cold operands), so counts of later DMAs
+  // left in flight are only trusted in the loop, where each was issued at
+  // least one stage after the one waited for.
+  vm_wait<0>();
   if constexpr (LORA != 0) {
     // the segment id was loaded before stage 0, so it has landed too
     asm volatile("" : "+v"(e_seg));

@@ -142,6 +142,22 @@ def test_random_cases(case, policy):
     base_rows_bitwise(w, r)
 
 
+@pytest.mark.parametrize("shape", [(400, 136, 4104), (512, 256, 4096), (320, 200, 4168),
+                                   (256, 136, 4096)])
+def test_short_k_fresh_operands_repeated(shape):
+    """Small batches with one or two K stages on freshly copied operands,
+    three times each: the GEMM prologue must wait for every stage it
+    issued (a one-stage allowance let stage 0 be read before it had fully
+    landed on cold operands).  Both paths against the oracle each time."""
+    n, d_in, d_out = shape
+    w = wl.make_random(400 + n, n, d_in, d_out, 9, 32, p_base=0.1, dtype="bf16", runs=True)
+    for rep in range(3):
+        say("short K", shape, rep)
+        r = run_hip(w)
+        check_values(w, r)
+        base_rows_bitwise(w, r)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("n_target", [600, 2300])
 def test_segment_lengths_around_row_blocks(n_target, dtype):
