@@ -175,7 +175,13 @@ __global__ __launch_bounds__((SM / 32) * (SN / 32) * kWave) void shrink_mfma_ker
     for (int st = 0; st < kSStages - 1; ++st)
       if (st < KT) issue(st, st * BK);
     for (int kt = 0; kt < KT; ++kt) {
-      wait_ahead<IPW>(min(kSStages - 2, KT - 1 - kt));
+      // the first step waits for every prologue stage (DMAs issued back to
+      // back can land out of order); later steps leave the stages issued
+      // after the one they wait for in flight
+      if (kt == 0)
+        vm_wait<0>();
+      else
+        wait_ahead<IPW>(min(kSStages - 2, KT - 1 - kt));
       if (ktail && kt == KT - 1) {
         unsigned char *st = smem + (kt % kSStages) * STAGE;
 #pragma unroll
