@@ -1028,38 +1028,64 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   if (KG > 1 && kgrp > 0) return;
 
-  // store: bf16 round to nearest even, once.  DoRA: rows of rank > 0 are
-  // first multiplied by g[slot][col]; the tile's row -> slot table (-1 = not
-  // rescaled) was written before the segment loop, whose barriers order it
-  // before these reads.  Rows without a factor read slot 0's in bounds and
-  // multiply by 1.  One fragment row block at a time, so the factors of
-  // only one block are live.
+  // DoRA: rows of rank > 0 are multiplied by g[slot][col]; the tile's
+  // row -> slot table (-1 = not rescaled) was written before the segment
+  // loop, whose barriers order it before these reads.  Rows without a
+  // factor read slot 0's in bounds and multiply by 1.  One fragment row
+  // block at a time, so the factors of only one block are live.
+  if constexpr (DORA) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    int rs[16];
-    if constexpr (DORA) {
+    for (int i = 0; i < C::FM; ++i) {
+      int rs[16];
       const int *s_rowslot = reinterpret_cast<const int *>(smem + 2 * BM * 128 + BN * 128 + 16);
 #pragma unroll
       for (int v = 0; v < 16; ++v) rs[v] = s_rowslot[wm * C::TM + i * 32 + acc_row(v, l)];
-    }
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = n0 + wn * C::TN + j * 32 + (l & 31);
-      if constexpr (DORA) {
-        const int colc = min(col, N - 1);
+      for (int j = 0; j < C::FN; ++j) {
+        const int colc = min(n0 + wn * C::TN + j * 32 + (l & 31), N - 1);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float f = g.dora[(int64_t)max(rs[v], 0) * N + colc];
           acc[i][j][v] *= rs[v] >= 0 ? f : 1.f;
         }
       }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * C::TM + i * 32 + acc_row(v, l);
-        if (row < M && col < N) g.Y[(int64_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_rne(acc[i][j][v]);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (DORA) __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Store: bf16 round to nearest even, once.  A lane holds one column of
+  // each 32x32 fragment, so the rounded tile goes through LDS row-major
+  // (RCH rows per pass, rows padded by 8 elements) and leaves as 16-byte
+  // row segments: an eighth of the store instructions of storing the
+  // fragments' 2-byte elements directly (measured: those took about 5% of
+  // the prefill product).
+  constexpr int RSB = BN + 8;                         // bf16 elements per staged row
+  constexpr int RCH = (BM * RSB * 2 <= SMEM) ? BM : BM / 2;
+  static_assert(RCH * RSB * 2 <= SMEM && RCH % C::TM == 0, "store staging");
+  constexpr int CPR = BN / 8;                         // 16-byte segments per row
+  uint16_t *s16 = reinterpret_cast<uint16_t *>(smem);
+  lgkm_barrier();                                     // every LDS read above is done
+#pragma unroll
+  for (int p0 = 0; p0 < BM; p0 += RCH) {
+    if (wm * C::TM >= p0 && wm * C::TM < p0 + RCH) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s16[(wm * C::TM - p0 + i * 32 + acc_row(v, l)) * RSB + wn * C::TN + j * 32 + (l & 31)] =
+                f32_to_bf16_rne(acc[i][j][v]);
+    }
+    lgkm_barrier();
+#pragma unroll
+    for (int q = tid; q < RCH * CPR; q += C::T) {
+      const int r = q / CPR, c8 = (q % CPR) * 8;
+      const int row = m0 + p0 + r, col = n0 + c8;    // N % 8 == 0: all 8 columns or none
+      if (row < M && col < N)
+        stg16(g.Y + (int64_t)row * g.ldy + col, *reinterpret_cast<const uint4 *>(s16 + r * RSB + c8));
+    }
+    if (p0 + RCH < BM) lgkm_barrier();               // the next pass rewrites the rows
   }
 }
 
