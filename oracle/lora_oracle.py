@@ -22,7 +22,7 @@ The pool argument ``B`` is the [n_slots, d_out, r_max] array whose slot a is
 B_a as the pages write it; rows/columns at or beyond a slot's rank are pool
 padding and are never read.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * a row whose slot is outside [-1, n_slots) or whose slot rank is outside
   [0, r_max] is treated as base-only and counted in ``status``;
