@@ -94,6 +94,18 @@ lora::PoolView pool_view(const lora_pool *p) {
   return v;
 }
 
+// FP8 weight: E4M3 codes [d_out][ldw] (16-byte aligned rows, d_in % 16 == 0)
+// and one float32 scale per output row.
+lora_status check_fp8_weight(const void *Wq, int64_t ldw, const float *w_scale, int32_t d_in,
+                             int32_t d_out) {
+  if (d_in % 16) return LORA_ERR_ALIGN;
+  if (!Wq || !w_scale) return LORA_ERR_NULL;
+  if (ldw < d_in) return LORA_ERR_SHAPE;
+  if (ldw % 16 || !aligned16(Wq) || !aligned16(w_scale)) return LORA_ERR_ALIGN;
+  (void)d_out;
+  return LORA_OK;
+}
+
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
 
 }  // namespace
@@ -244,18 +256,6 @@ lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ld
   return hip_status(lora::launch_gemm(X, ldx, W, ldw, Y, ldy, n_rows, d_in, d_out, dtype,
                                       nullptr, nullptr, nullptr,
                                       static_cast<hipStream_t>(stream)));
-}
-
-// FP8 weight: E4M3 codes [d_out][ldw] (16-byte aligned rows, d_in % 16 == 0)
-// and one float32 scale per output row.
-lora_status check_fp8_weight(const void *Wq, int64_t ldw, const float *w_scale, int32_t d_in,
-                             int32_t d_out) {
-  if (d_in % 16) return LORA_ERR_ALIGN;
-  if (!Wq || !w_scale) return LORA_ERR_NULL;
-  if (ldw < d_in) return LORA_ERR_SHAPE;
-  if (ldw % 16 || !aligned16(Wq) || !aligned16(w_scale)) return LORA_ERR_ALIGN;
-  (void)d_out;
-  return LORA_OK;
 }
 
 lora_status lora_base_gemm_fp8w(const void *X, int64_t ldx, const void *Wq, int64_t ldw,

@@ -315,14 +315,21 @@ def make_integer_case(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_
 
 
 def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_max: int,
-                     ranks=None, p_base: float = 0.1, dtype: str = "bf16") -> Workload:
+                     ranks=None, p_base: float = 0.1, dtype: str = "bf16", runs: bool = False,
+                     row_slot=None) -> Workload:
     """Fingerprint adapters: slot a has A_a row 0 = unit vector at column
     (a mod d_in) and every other rank row zero, and B_a filled with the
     constant (a + 1) (exact in bf16 for a < 256).  The LoRA increment of a row
     on slot a is then s_a * (a + 1) * x[a mod d_in] in every output column, so
-    a row that picks up another slot's weights is off by a visible amount."""
+    a row that picks up another slot's weights is off by a visible amount.
+    ``runs`` draws request runs as make_random does; ``row_slot`` (int32 [n])
+    replaces the drawn mapping."""
     w = make_random(seed, n, d_in, d_out, n_slots, r_max, ranks=ranks, p_base=p_base,
-                    dtype=dtype, pad="nan")
+                    dtype=dtype, pad="nan", runs=runs)
+    if row_slot is not None:
+        w.row_slot = np.asarray(row_slot, dtype=np.int32).copy()
+        if len(w.row_slot) != n:
+            raise ValueError("row_slot must have n entries")
     if dtype == "f32":
         # keep x on the bf16 grid so that s_a (a + 1) x is exact in fp32 too
         w.X = bf16_bits_to_f32(bf16_bits_rne(w.X))
@@ -337,6 +344,32 @@ def make_fingerprint(seed: int, n: int, d_in: int, d_out: int, n_slots: int, r_m
         w.Bt[a, :r] = _encode(rowsB, dtype).astype(et)
     w.name = f"fingerprint_s{seed}"
     return w
+
+
+def tile_runs_mapping(seed: int, n: int, tile_rows: int, runs, n_slots: int,
+                      base_every: int = 3) -> np.ndarray:
+    """A row -> slot mapping whose consecutive blocks of ``tile_rows`` rows
+    hold runs[t % len(runs)] runs each (block t), every run on a slot other
+    than its neighbours', and in every ``base_every``-th block one run
+    base-only (-1).  The last block may be short.  Mapping only."""
+    rng = _rng(np.random.SeedSequence([seed, 0x7E]))
+    out = []
+    t = 0
+    while len(out) < n:
+        rows = min(tile_rows, n - len(out))
+        k = max(1, min(int(runs[t % len(runs)]), rows))
+        cuts = np.sort(rng.choice(np.arange(1, rows), size=k - 1, replace=False)) if k > 1 else []
+        lens = np.diff(np.concatenate([[0], cuts, [rows]])).astype(int)
+        slots = rng.choice(n_slots, size=k, replace=k > n_slots)
+        for j in range(1, k):
+            if slots[j] == slots[j - 1]:
+                slots[j] = (slots[j] + 1) % n_slots
+        if base_every and t % base_every == base_every - 1:
+            slots[k // 2] = -1
+        for L, sl in zip(lens, slots):
+            out.extend([int(sl)] * int(L))
+        t += 1
+    return np.array(out[:n], dtype=np.int32)
 
 
 def fp8_e4m3_bits_rne(x32) -> np.ndarray:
