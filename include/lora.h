@@ -14,7 +14,8 @@
  * ---------------------------------
  * - Every pointer argument is a DEVICE pointer unless stated otherwise; the
  *   structs themselves live in host memory.  The caller owns every buffer;
- *   the library allocates nothing and keeps no state between calls.
+ *   the library allocates nothing and keeps no state between calls, apart
+ *   from the static device scratch of lora_linear_fused_static.
  * - Calls are asynchronous on the given HIP stream (`hipStream_t` passed as
  *   `void*`, NULL = the default stream).  Argument errors are detected on
  *   the host and returned before anything is launched; no output is touched
@@ -40,9 +41,13 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 4
+#define LORA_ABI_VERSION 5
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
+/* Limits of the allocation-free call lora_linear_fused_static: token rows,
+ * and n_rows * r_max (the entries of its H). */
+#define LORA_STATIC_MAX_ROWS 32768
+#define LORA_STATIC_MAX_H (1 << 21)
 
 typedef enum {
   LORA_OK = 0,
@@ -53,7 +58,8 @@ typedef enum {
   LORA_ERR_DTYPE = -5,     /* unknown dtype */
   LORA_ERR_CAPACITY = -6,  /* segment arrays too small for the worst case */
   LORA_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
-  LORA_ERR_POLICY = -8     /* unknown rank policy */
+  LORA_ERR_POLICY = -8,    /* unknown rank policy */
+  LORA_ERR_SCRATCH = -9    /* batch larger than the allocation-free call's scratch */
 } lora_status;
 
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
@@ -324,6 +330,32 @@ lora_status lora_linear_fused_fp8w(const void *X, int64_t ldx, const void *Wq, i
                                    const float *w_scale, const float *H,
                                    const lora_segments *seg, const lora_pool *pool, void *Y,
                                    int64_t ldy, void *stream);
+
+/*
+ * The whole layer with no workspace arguments, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc):
+ *   Y = X W^T + s_a H[i][0:r] B_a^T,   H = the shrink of X,
+ * exactly what lora_build_shrink followed by lora_linear_fused computes (same
+ * kernels, same bits), with the segment metadata and H kept in a static
+ * device array of the library (about 8.4 MB per GPU, held until the process
+ * ends) instead of caller buffers.  row_slot: device int32 [n_rows] (-1 =
+ * base-only); X [n_rows][d_in] (ld ldx), W [d_out][d_in] (ld ldw), Y
+ * [n_rows][d_out] (ld ldy), all of the pool's dtype, as for
+ * lora_linear_fused.  Rows demoted for a bad slot or rank are base-only, as
+ * there (their count is kept in the scratch, not returned).
+ * Limits: n_rows <= LORA_STATIC_MAX_ROWS and n_rows * r_max <=
+ * LORA_STATIC_MAX_H, else LORA_ERR_SCRATCH before anything is launched.
+ * Nothing is allocated: no hipMalloc, no hipFree, no allocating library call.
+ * Every call on one GPU uses that GPU's one scratch array, so calls that
+ * overlap on a GPU (other streams, other threads) race; calls queued on one
+ * stream are ordered.  The first call on a device looks the array's address
+ * up (a HIP runtime call that does not allocate); later calls reuse it.
+ * Other errors as lora_linear_fused.  n_rows == 0 is a no-op.
+ */
+lora_status lora_linear_fused_static(const int32_t *row_slot, const void *X, int64_t ldx,
+                                     const void *W, int64_t ldw, const lora_pool *pool,
+                                     int32_t n_rows, void *Y, int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

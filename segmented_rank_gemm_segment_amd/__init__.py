@@ -30,7 +30,9 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 4
+ABI_VERSION = 5
+STATIC_MAX_ROWS = 32768
+STATIC_MAX_H = 1 << 21
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -90,6 +92,7 @@ EXPORTS = (
     "lora_linear_fused",
     "lora_base_gemm_fp8w",
     "lora_linear_fused_fp8w",
+    "lora_linear_fused_static",
 )
 
 
@@ -128,6 +131,8 @@ def lib() -> ctypes.CDLL:
     L.lora_base_gemm_fp8w.argtypes = [vp, i64, vp, i64, vp, vp, i64, i32, i32, i32, vp]
     L.lora_linear_fused_fp8w.restype = i32
     L.lora_linear_fused_fp8w.argtypes = [vp, i64, vp, i64, vp, vp, SP, PP, vp, i64, vp]
+    L.lora_linear_fused_static.restype = i32
+    L.lora_linear_fused_static.argtypes = [vp, vp, i64, vp, i64, PP, i32, vp, i64, vp]
     if L.lora_abi_version() != ABI_VERSION:
         raise RuntimeError("liblora ABI version mismatch")
     _lib = L
@@ -461,3 +466,21 @@ def lora_linear_fused_fp8w(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Ten
         raise ValueError("H: float32 [n_rows, r_max]")
     _check(lib().lora_linear_fused_fp8w(_ptr(X), _ld(X), _ptr(Wq), _ld(Wq), _ptr(w_scale), _ptr(H),
                                         seg.c, pool.c, _ptr(Y), _ld(Y), _stream(stream)))
+
+
+def lora_linear_fused_static(row_slot: torch.Tensor, X: torch.Tensor, W: torch.Tensor, pool: Pool,
+                             Y: torch.Tensor, stream=None) -> None:
+    """The whole layer, Y = X W^T + LoRA, with the segment metadata and H in
+    the library's static device scratch (no workspace, nothing allocated);
+    the same bits as lora_build_shrink followed by lora_linear_fused.  Calls
+    that overlap on one GPU race on that scratch."""
+    if row_slot.dtype != torch.int32 or (row_slot.numel() and not row_slot.is_contiguous()):
+        raise ValueError("row_slot: contiguous int32")
+    n = row_slot.numel()
+    if not (X.dtype == W.dtype == Y.dtype == pool.dtype):
+        raise ValueError("X, W, Y must share the pool dtype")
+    if X.shape[0] != n or tuple(W.shape) != (pool.d_out, pool.d_in) \
+            or tuple(Y.shape) != (n, pool.d_out):
+        raise ValueError("shapes: row_slot [n], X [n, d_in], W [d_out, d_in], Y [n, d_out]")
+    _check(lib().lora_linear_fused_static(_ptr(row_slot), _ptr(X), _ld(X), _ptr(W), _ld(W), pool.c,
+                                          n, _ptr(Y), _ld(Y), _stream(stream)))

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora.so")
 
 SOURCES = ["build_segments.hip", "shrink_expand.hip", "gemm.hip", "pack_slot.hip", "dora.hip",
-           "lora_api.cpp"]
+           "static_scratch.hip", "lora_api.cpp"]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-inline-asm",

@@ -125,6 +125,8 @@ const char *lora_status_str(int32_t status) {
     case LORA_ERR_CAPACITY: return "segment arrays smaller than min(n_rows, n_slots + 1)";
     case LORA_ERR_HIP: return "HIP runtime error at launch";
     case LORA_ERR_POLICY: return "unknown rank policy";
+    case LORA_ERR_SCRATCH:
+      return "batch exceeds the static scratch (LORA_STATIC_MAX_ROWS rows, LORA_STATIC_MAX_H H entries)";
     default: return "unknown status";
   }
 }
@@ -323,6 +325,46 @@ lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t
   return hip_status(lora::launch_gemm(X, ldx, W, ldw, Y, ldy, n, pool->d_in, pool->d_out,
                                       pool->dtype, H, &sv, &pv,
                                       static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_linear_fused_static(const int32_t *row_slot, const void *X, int64_t ldx,
+                                     const void *W, int64_t ldw, const lora_pool *pool,
+                                     int32_t n_rows, void *Y, int64_t ldy, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (n_rows < 0) return LORA_ERR_SHAPE;
+  if (n_rows > LORA_STATIC_MAX_ROWS || (int64_t)n_rows * pool->r_max > LORA_STATIC_MAX_H)
+    return LORA_ERR_SCRATCH;
+  if (n_rows > 0 && !row_slot) return LORA_ERR_NULL;
+  st = check_matrix(X, ldx, pool->d_in, n_rows);
+  if (st != LORA_OK) return st;
+  st = check_matrix(W, ldw, pool->d_in, pool->d_out);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, pool->d_out, n_rows);
+  if (st != LORA_OK) return st;
+  if (n_rows == 0) return LORA_OK;
+  // the scratch's device address on the current device (never the array's
+  // host-side name)
+  void *base = nullptr;
+  if (lora::static_scratch(&base) != hipSuccess) return LORA_ERR_HIP;
+  unsigned char *b = static_cast<unsigned char *>(base);
+  lora_segments seg;
+  seg.n_rows = n_rows;
+  seg.max_segments = seg_worst_case(n_rows, pool->n_slots);
+  seg.token_indices = reinterpret_cast<int32_t *>(b + lora::kScrTok);
+  seg.row_segment = reinterpret_cast<int32_t *>(b + lora::kScrRowSeg);
+  seg.segment_offsets = reinterpret_cast<int32_t *>(b + lora::kScrSegOff);
+  seg.segment_slots = reinterpret_cast<int32_t *>(b + lora::kScrSegSlot);
+  seg.segment_ranks = reinterpret_cast<int32_t *>(b + lora::kScrSegRank);
+  seg.segment_scales = reinterpret_cast<float *>(b + lora::kScrSegScale);
+  seg.num_segments = reinterpret_cast<int32_t *>(b + lora::kScrNumSeg);
+  seg.status = reinterpret_cast<int32_t *>(b + lora::kScrStatus);
+  float *H = reinterpret_cast<float *>(b + lora::kScrH);
+  // every entry the two calls read is written by them first: the metadata by
+  // the build, H[i][0:r] by the shrink for the rows whose term is added
+  st = lora_build_shrink(row_slot, X, ldx, pool, &seg, H, stream);
+  if (st != LORA_OK) return st;
+  return lora_linear_fused(X, ldx, W, ldw, H, &seg, pool, Y, ldy, stream);
 }
 
 }  // extern "C"

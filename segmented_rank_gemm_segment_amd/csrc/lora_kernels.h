@@ -2,7 +2,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/lora.h"
 
 namespace lora {
 
@@ -95,5 +98,24 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
                        int64_t ldy, int M, int K, int N, int dtype, const float *H,
                        const SegView *seg, const PoolView *pool, hipStream_t stream,
                        const float *wscale = nullptr);
+
+// Device scratch of the allocation-free call lora_linear_fused_static: byte
+// offsets of its parts, each 256-byte aligned.  H is float [n][r_max]; the
+// segment arrays hold up to LORA_MAX_SLOTS + 1 segments (min(n, n_slots + 1)).
+constexpr size_t kScrAlign = 256;
+constexpr size_t scr_up(size_t x) { return (x + kScrAlign - 1) / kScrAlign * kScrAlign; }
+constexpr size_t kScrH = 0;
+constexpr size_t kScrTok = scr_up(kScrH + 4ull * LORA_STATIC_MAX_H);
+constexpr size_t kScrRowSeg = scr_up(kScrTok + 4ull * LORA_STATIC_MAX_ROWS);
+constexpr size_t kScrSegOff = scr_up(kScrRowSeg + 4ull * LORA_STATIC_MAX_ROWS);
+constexpr size_t kScrSegSlot = scr_up(kScrSegOff + 4ull * (LORA_MAX_SLOTS + 2));
+constexpr size_t kScrSegRank = scr_up(kScrSegSlot + 4ull * (LORA_MAX_SLOTS + 1));
+constexpr size_t kScrSegScale = scr_up(kScrSegRank + 4ull * (LORA_MAX_SLOTS + 1));
+constexpr size_t kScrNumSeg = scr_up(kScrSegScale + 4ull * (LORA_MAX_SLOTS + 1));
+constexpr size_t kScrStatus = kScrNumSeg + kScrAlign;
+constexpr size_t kScratchBytes = kScrStatus + kScrAlign;
+
+// Device address of this device's scratch (looked up once per device).
+hipError_t static_scratch(void **out);
 
 }  // namespace lora

@@ -13,7 +13,8 @@ import segmented_rank_gemm_segment_amd as srg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lora.h")
 
-OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH = (0, -1, -2, -3, -4, -5,
+                                                                   -6, -7, -8, -9)
 
 
 @pytest.fixture(scope="session")
@@ -35,7 +36,7 @@ def test_header_declares_the_boundary():
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
               "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
               "lora_base_gemm_fp8w", "lora_linear_fused_fp8w", "lora_status_str",
-              "lora_abi_version"):
+              "lora_abi_version", "lora_linear_fused_static"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -50,8 +51,8 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 4
-    for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY):
+    assert L.lora_abi_version() == srg.ABI_VERSION == 5
+    for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
     assert L.lora_status_str(12345).decode() == "unknown status"
@@ -275,3 +276,23 @@ def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(srg, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         srg.lib()
+
+
+def test_static_call_validation(L):
+    """The allocation-free call rejects batches beyond its scratch, and bad
+    arguments, on the host (nothing is launched: these addresses are fake)."""
+    f = L.lora_linear_fused_static
+    p = pool()                                              # r_max 16
+    rs, X, W, Y = P + 0x4000, P + 0xC000, P + 0xD000, P + 0xE000
+    pp = ctypes.byref(p)
+    assert f(rs, X, 64, W, 64, None, 10, Y, 32, None) == ENULL
+    assert f(rs, X, 64, W, 64, pp, srg.STATIC_MAX_ROWS + 1, Y, 32, None) == ESCRATCH
+    big = ctypes.byref(pool(r_max=64))                      # 32768 rows x 64 > 2^21
+    assert f(rs, X, 64, W, 64, big, srg.STATIC_MAX_H // 64 + 1, Y, 32, None) == ESCRATCH
+    assert f(rs, X, 64, W, 64, pp, -1, Y, 32, None) == ESHAPE
+    assert f(None, X, 64, W, 64, pp, 10, Y, 32, None) == ENULL
+    assert f(rs, None, 64, W, 64, pp, 10, Y, 32, None) == ENULL
+    assert f(rs, X, 60, W, 64, pp, 10, Y, 32, None) == ESHAPE        # ldx < d_in
+    assert f(rs, X, 64, W, 64, pp, 10, Y + 8, 32, None) == EALIGN    # Y not 16-byte aligned
+    assert f(rs, X, 64, W, 64, pp, 0, Y, 32, None) == OK             # empty batch: no-op
+
