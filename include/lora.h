@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 5
+#define LORA_ABI_VERSION 6
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 /* Limits of the allocation-free call lora_linear_fused_static: token rows,
@@ -84,11 +84,13 @@ typedef enum {
  *   A [n_slots][r_max][d_in]   row k = row k of A_a      (A_a in R^{r x d_in})
  *   Bt[n_slots][r_max][d_out]  row k = column k of B_a   (B_a in R^{d_out x r})
  * Rows k >= slot_rank[a] are padding and are never multiplied in.
- * slot_scale[a] is s_a = alpha_a / r_a (0 for a rank-0 slot).
+ * slot_scale[a] is s_a = alpha_a / r_a (0 for a rank-0 slot), written by the
+ * library (lora_pool_pack_slot, lora_pool_set_scales), never by the caller.
  * Optionally the pool also carries B in its own d_out-major layout,
  *   B [n_slots][d_out][r_max]  row j = row j of B_a   (the layout of the
  *                              adapter's up-projection weight),
- * the same values as Bt.  lora_linear_fused then reads whole 16-byte runs of
+ * the same values as Bt (written by lora_pool_pack_slot, or from Bt by
+ * lora_pool_write_b).  lora_linear_fused then reads whole 16-byte runs of
  * rank values per output column; with B NULL it gathers them from Bt.
  *
  * DoRA (ybb.press multi-LoRA serving article, section 9.2: the adapted
@@ -119,8 +121,8 @@ typedef enum {
  * exactly what it computes for a single one.  Requirements: proj_cols[0] =
  * 0, proj_cols[P] = d_out, strictly increasing multiples of 8
  * (LORA_ERR_SHAPE), rs in {8, 16, 32, 64} (LORA_ERR_RANK), proj_cols non-NULL
- * (LORA_ERR_NULL).  lora_pool_pack_slot does not pack stacked pools
- * (LORA_ERR_SHAPE).
+ * (LORA_ERR_NULL).  lora_pool_pack_slot writes this layout from each
+ * projection's own A and B.
  */
 typedef struct {
   int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
@@ -231,33 +233,69 @@ lora_status lora_base_gemm(const void *X, int64_t ldx, const void *W, int64_t ld
                            void *Y, int64_t ldy, int32_t n_rows, int32_t d_in,
                            int32_t d_out, int32_t dtype, void *stream);
 
+/* Layout of the B sources of lora_pool_pack_slot. */
+typedef enum {
+  LORA_B_ROWS = 0,      /* B_q [d_out_q][ldb], ldb >= rank: the adapter weight's own layout */
+  LORA_B_RANK_ROWS = 1  /* B_q^T [rank][ldb], ldb >= d_out_q: the pool's Bt layout */
+} lora_b_layout;
+
 /*
  * Pack one adapter into slot `slot` of the pool (LoRA/QLoRA 多租户GPU推理服务化实战,
  * section 1.1 "Adapter的统一尺寸对齐": one preallocated buffer, each adapter packed
- * into the slot its offset names; adapter-batching page, "动态加载是一个安全边界":
- * rank and sizes bounded, a failed load leaves the old contents usable, the new
- * slot published only when its weights are complete).
- *   A_src [rank][d_in]   ld lda (a multiple of 8)  down-projection A_a, pool dtype
- *   B_src [d_out][rank]  ld ldb (>= rank)          up-projection B_a, pool dtype
- * both device memory.  Writes A rows [0, rank) and zeros up to r_max, Bt rows
- * [0, rank) = B_src transposed and zeros up to r_max, the d_out-major B of the
- * pool when it has one (zeros past rank), and then, by a second kernel on the
- * same stream, slot_rank[slot] = rank and slot_scale[slot] = scale (the caller
- * passes alpha / rank; 0 is stored for rank 0).  When the pool has a
- * dora_scale array, the slot's row of it is set to ones with the weights (the
- * new adapter starts as plain LoRA; lora_pool_dora_prepare makes it DoRA).
- * Work queued later on `stream` sees the whole new adapter.  rank = 0 empties the slot (its rows take the
- * base-only path); A_src and B_src may then be NULL.  The caller must not pack
- * a slot that queued or running work on other streams still reads (wait for
- * it first).  The pool's slot_rank and slot_scale arrays are written.
- * Errors (all before any write): NULL pool or sources, slot outside
- * [0, n_slots) or rank outside [0, r_max] (LORA_ERR_SHAPE), lda < d_in or
- * ldb < rank (LORA_ERR_SHAPE), lda not a multiple of 8 or A_src not 16-byte
+ * into the slot its offset names, and section 1.2: the alpha / r scaling is the
+ * kernel library's; adapter-batching page, "动态加载是一个安全边界": rank and sizes
+ * bounded, a failed load leaves the old contents usable, the new slot published
+ * only when its weights are complete; "Adapter 不是一块连续 Weight": each target
+ * projection has its own A and B).  HOST arrays of P = max(1, pool->n_proj)
+ * entries give projection q's sources, both device memory of the pool dtype:
+ *   A_src[q]  [rank][lda[q]]   down-projection A_q   (lda % 8 == 0, 16-byte aligned)
+ *   B_src[q]  up-projection B_q in b_layout: [d_out_q][ldb[q]] (LORA_B_ROWS)
+ *             or its transpose [rank][ldb[q]] (LORA_B_RANK_ROWS),
+ * with d_out_q the projection's column count (d_out for a single projection).
+ * Writes, per projection q with rs = r_max / P: A rank rows [q rs, q rs + rank)
+ * and zeros up to (q + 1) rs; Bt rank rows [q rs, q rs + rank) = B_q^T in the
+ * projection's columns and zeros elsewhere and past the rank; the pool's
+ * d_out-major B when it has one, likewise; ones in the slot's dora_scale row
+ * when the pool has that array (the new adapter starts as plain LoRA;
+ * lora_pool_dora_prepare makes it DoRA).  Then, by a later kernel on the same
+ * stream, slot_rank[slot] = rank and slot_scale[slot] = alpha / rank (the
+ * double quotient rounded once to float; 0 for rank 0).  Work queued later
+ * on `stream` sees the whole new adapter.  rank = 0 empties the slot (its
+ * rows take the base-only path); the source arrays may then be NULL.  The
+ * caller must not pack a slot that queued or running work on other streams
+ * still reads (wait for it first).  The pool's slot_rank and slot_scale
+ * arrays are written.  Errors (all before any write): NULL pool, or for
+ * rank > 0 a NULL array or source (LORA_ERR_NULL); slot outside
+ * [0, n_slots), rank outside [0, rs], lda[q] < d_in, ldb[q] below rank
+ * (LORA_B_ROWS) or d_out_q (LORA_B_RANK_ROWS), or an unknown b_layout
+ * (LORA_ERR_SHAPE); lda[q] not a multiple of 8 or A_src[q] not 16-byte
  * aligned (LORA_ERR_ALIGN).
  */
-lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, float scale,
-                                const void *A_src, int64_t lda, const void *B_src, int64_t ldb,
+lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, double alpha,
+                                const void *const *A_src, const int64_t *lda,
+                                const void *const *B_src, const int64_t *ldb, int32_t b_layout,
                                 void *stream);
+
+/*
+ * The scale of every slot from its alpha (the scaling s = alpha / r of the
+ * adapter-batching page, "LoRA 在一层 Linear 上增加了什么"; kept in the kernel
+ * library as LoRA/QLoRA 多租户GPU推理服务化实战 section 1.2 asks):
+ *   slot_scale[a] = alpha[a] / slot_rank[a]   (double quotient rounded once to
+ *                                              float; 0 where slot_rank[a] <= 0)
+ * slot_alpha: device double [n_slots], 8-byte aligned (LORA_ERR_ALIGN),
+ * non-NULL (LORA_ERR_NULL).  For a pool whose A, Bt and slot_rank the
+ * caller laid out directly; reads slot_rank as queued work on `stream`
+ * leaves it.  Writes slot_scale only.
+ */
+lora_status lora_pool_set_scales(const lora_pool *pool, const double *slot_alpha, void *stream);
+
+/*
+ * The pool's d_out-major copy of B from its Bt, for every slot:
+ * B[a][j][k] = Bt[a][k][j] (adapter-batching page, "Adapter 不是一块连续
+ * Weight": B_a in R^{d_out x r} is the adapter weight's own layout).  pool->B
+ * must be non-NULL (LORA_ERR_NULL).  Asynchronous on `stream`; writes B only.
+ */
+lora_status lora_pool_write_b(const lora_pool *pool, void *stream);
 
 /*
  * DoRA column factors of one slot (ybb.press multi-LoRA serving article,

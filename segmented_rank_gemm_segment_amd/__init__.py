@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 5
+ABI_VERSION = 6
 STATIC_MAX_ROWS = 32768
 STATIC_MAX_H = 1 << 21
 
@@ -87,6 +87,8 @@ EXPORTS = (
     "lora_build_shrink",
     "lora_expand",
     "lora_pool_pack_slot",
+    "lora_pool_set_scales",
+    "lora_pool_write_b",
     "lora_pool_dora_prepare",
     "lora_base_gemm",
     "lora_linear_fused",
@@ -120,7 +122,11 @@ def lib() -> ctypes.CDLL:
     L.lora_expand.restype = i32
     L.lora_expand.argtypes = [vp, SP, PP, vp, i64, vp]
     L.lora_pool_pack_slot.restype = i32
-    L.lora_pool_pack_slot.argtypes = [PP, i32, i32, ctypes.c_float, vp, i64, vp, i64, vp]
+    L.lora_pool_pack_slot.argtypes = [PP, i32, i32, ctypes.c_double, vp, vp, vp, vp, i32, vp]
+    L.lora_pool_set_scales.restype = i32
+    L.lora_pool_set_scales.argtypes = [PP, vp, vp]
+    L.lora_pool_write_b.restype = i32
+    L.lora_pool_write_b.argtypes = [PP, vp]
     L.lora_pool_dora_prepare.restype = i32
     L.lora_pool_dora_prepare.argtypes = [PP, i32, vp, i64, vp, vp]
     L.lora_base_gemm.restype = i32
@@ -177,78 +183,131 @@ class Pool:
 
     ``A``  [n_slots, r_max, d_in]  and  ``Bt`` [n_slots, r_max, d_out]
     (rank-major; row k of Bt[a] is column k of B_a), ``slot_rank`` int32
-    [n_slots] and per-slot alpha.  The per-slot scale alpha/r is stored as
-    float32 (0 for rank 0) when the pool is created, as adapter loading does.
+    [n_slots] and ``slot_scale`` float32 [n_slots], which the library writes
+    from the slots' alphas (lora_pool_set_scales, lora_pool_pack_slot).
     With ``natural_b`` (default) the pool also keeps B in its d_out-major
-    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM.  With
-    ``dora`` it keeps DoRA column factors ``dora_scale`` float32 [n_slots,
-    d_out], all ones (plain LoRA) until ``dora_prepare`` sets a slot's.
+    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM (written by
+    the library: lora_pool_write_b, lora_pool_pack_slot).  With ``dora`` it
+    keeps DoRA column factors ``dora_scale`` float32 [n_slots, d_out], all
+    ones (plain LoRA) until ``dora_prepare`` sets a slot's.  A pool of
+    stacked projections (``empty(..., proj_outs=...)``, ``stacked``) serves
+    several projections of one input; its ``proj_cols`` are the host column
+    offsets.  torch only allocates here: every value is written by liblora.
     """
 
     def __init__(self, A: torch.Tensor, Bt: torch.Tensor, slot_rank: torch.Tensor,
                  slot_alpha, rank_policy: str = "exact", natural_b: bool = True,
-                 dora: bool = False):
+                 dora: bool = False, proj_outs=None, stream=None):
         if A.dim() != 3 or Bt.dim() != 3 or A.shape[:2] != Bt.shape[:2]:
             raise ValueError("A [n_slots, r_max, d_in] and Bt [n_slots, r_max, d_out] expected")
         if A.dtype != Bt.dtype or not A.is_contiguous() or not Bt.is_contiguous():
             raise ValueError("A and Bt: same dtype, contiguous")
+        dev = A.device
         self.A, self.Bt = A, Bt
-        self.B = Bt.transpose(1, 2).contiguous() if natural_b else None
         self.n_slots, self.r_max, self.d_in = A.shape
         self.d_out = Bt.shape[2]
-        self.dora_scale = (torch.ones((self.n_slots, self.d_out), dtype=torch.float32,
-                                      device=A.device) if dora else None)
-        self.proj_cols = None             # stacked projections: host int32 column offsets
         self.dtype = A.dtype
-        self.slot_rank = slot_rank.to(device=A.device, dtype=torch.int32).contiguous()
-        rank_host = self.slot_rank.cpu().to(torch.float64)
+        self.B = (torch.empty((self.n_slots, self.d_out, self.r_max), dtype=A.dtype, device=dev)
+                  if natural_b else None)
+        self.dora_scale = (torch.ones((self.n_slots, self.d_out), dtype=torch.float32, device=dev)
+                           if dora else None)
+        self.proj_cols = None             # stacked projections: host int32 column offsets
+        if proj_outs is not None and len(proj_outs) >= 2:
+            cols = [0]
+            for c in proj_outs:
+                cols.append(cols[-1] + int(c))
+            if cols[-1] != self.d_out:
+                raise ValueError("projection widths must add up to d_out")
+            self.proj_cols = (ctypes.c_int32 * len(cols))(*cols)
+        self.slot_rank = slot_rank.to(device=dev, dtype=torch.int32).contiguous()
+        self.slot_scale = torch.empty(self.n_slots, dtype=torch.float32, device=dev)
         alpha = torch.as_tensor(slot_alpha, dtype=torch.float64).reshape(-1)
-        scale = torch.where(rank_host > 0, alpha / rank_host.clamp(min=1), torch.zeros_like(alpha))
-        self.slot_scale = scale.to(torch.float32).to(A.device).contiguous()
+        if alpha.numel() == 1:
+            alpha = alpha.expand(self.n_slots)
+        if alpha.numel() != self.n_slots:
+            raise ValueError("slot_alpha: one value or one per slot")
+        self.slot_alpha = alpha.clone()   # host copy of each slot's alpha (bookkeeping)
         self.generation = [0] * self.n_slots
         self.set_policy(rank_policy)
+        st = torch.cuda.current_stream(dev) if stream is None else stream
+        alpha_d = alpha.contiguous().to(dev)
+        with torch.cuda.stream(st):
+            _check(lib().lora_pool_set_scales(self.c, _ptr(alpha_d), _stream(st)))
+            if self.B is not None:
+                _check(lib().lora_pool_write_b(self.c, _stream(st)))
+        alpha_d.record_stream(st)         # alive until the queued kernel has read it
 
     @classmethod
     def empty(cls, n_slots: int, r_max: int, d_in: int, d_out: int, dtype=torch.bfloat16,
               device="cuda", rank_policy: str = "exact", natural_b: bool = True,
-              dora: bool = False) -> "Pool":
-        """A pool of empty slots (rank 0, zero weights), filled by ``pack``."""
-        A = torch.zeros((n_slots, r_max, d_in), dtype=dtype, device=device)
-        Bt = torch.zeros((n_slots, r_max, d_out), dtype=dtype, device=device)
+              dora: bool = False, proj_outs=None) -> "Pool":
+        """A pool of empty slots (rank 0, zero weights), filled by ``pack``.
+        ``proj_outs``: output widths of stacked projections (r_max is then
+        the per-projection rank bound, the pool's being len(proj_outs)
+        times it)."""
+        P = len(proj_outs) if proj_outs is not None and len(proj_outs) >= 2 else 1
+        if P > 1:
+            d_out = sum(int(c) for c in proj_outs)
+        A = torch.zeros((n_slots, P * r_max, d_in), dtype=dtype, device=device)
+        Bt = torch.zeros((n_slots, P * r_max, d_out), dtype=dtype, device=device)
         rank = torch.zeros(n_slots, dtype=torch.int32, device=device)
-        return cls(A, Bt, rank, 0.0, rank_policy, natural_b, dora)
+        return cls(A, Bt, rank, 0.0, rank_policy, natural_b, dora,
+                   proj_outs=proj_outs if P > 1 else None)
 
-    def pack(self, slot: int, A: torch.Tensor, B: torch.Tensor, alpha: float, stream=None) -> int:
-        """Load one adapter (A [r, d_in], B [d_out, r], the layouts of the
-        adapter's own weights) into ``slot`` with scale alpha / r, through
-        lora_pool_pack_slot on the device; host tensors are copied over
-        first (from pinned memory, asynchronously).  Returns the slot's new
-        generation.  r = 0 (A [0, d_in], B [d_out, 0]) empties the slot."""
-        r = int(A.shape[0])
-        if A.dim() != 2 or B.dim() != 2 or A.shape[1] != self.d_in or tuple(B.shape) != (self.d_out, r):
-            raise ValueError("A [r, d_in] and B [d_out, r] expected")
+    @property
+    def n_proj(self) -> int:
+        return 1 if self.proj_cols is None else len(self.proj_cols) - 1
+
+    def _on_device(self, t: torch.Tensor) -> torch.Tensor:
         dev = self.A.device
-        st = torch.cuda.current_stream(dev) if stream is None else stream
+        t = t.to(dtype=self.dtype)
+        if t.device != dev:
+            t = t.contiguous()
+            if t.device.type == "cpu":
+                t = t.pin_memory()
+            t = t.to(dev, non_blocking=True)
+        return t.contiguous()
 
-        def on_device(t):
-            t = t.to(dtype=self.dtype)
-            if t.device != dev:
-                t = t.contiguous()
-                if t.device.type == "cpu":
-                    t = t.pin_memory()
-                t = t.to(dev, non_blocking=True)
-            return t.contiguous()
-
-        Ad, Bd = on_device(A), on_device(B)
-        scale = float(torch.tensor(float(alpha) / r, dtype=torch.float32)) if r > 0 else 0.0
+    def pack(self, slot: int, A, B, alpha: float, stream=None, b_layout: str = "rows") -> int:
+        """Load one adapter into ``slot`` through lora_pool_pack_slot: A and B
+        are one tensor each (A [r, d_in], B [d_out, r], the layouts of the
+        adapter's own weights) or, for a stacked pool, lists with one per
+        projection; ``b_layout="rank_rows"`` takes B transposed ([r,
+        d_out_q]).  The library stores scale alpha / r.  Host tensors are
+        copied over first (from pinned memory, asynchronously).  Returns the
+        slot's new generation.  r = 0 (A [0, d_in]) empties the slot."""
+        As = list(A) if isinstance(A, (list, tuple)) else [A]
+        Bs = list(B) if isinstance(B, (list, tuple)) else [B]
+        P = self.n_proj
+        if len(As) != P or len(Bs) != P:
+            raise ValueError(f"{P} projection(s): one A and one B each")
+        r = int(As[0].shape[0])
+        cols = [self.d_out] if P == 1 else [self.proj_cols[q + 1] - self.proj_cols[q]
+                                             for q in range(P)]
+        rank_rows = b_layout == "rank_rows"
+        for q in range(P):
+            want_b = (r, cols[q]) if rank_rows else (cols[q], r)
+            if As[q].dim() != 2 or tuple(As[q].shape) != (r, self.d_in) \
+                    or tuple(Bs[q].shape) != want_b:
+                raise ValueError("A [r, d_in] and B [d_out_q, r] (or [r, d_out_q]) per projection")
+        st = torch.cuda.current_stream(self.A.device) if stream is None else stream
+        keep = []
+        if r > 0:
+            Ad = [self._on_device(t) for t in As]
+            Bd = [self._on_device(t) for t in Bs]
+            keep = Ad + Bd
+            a_ptrs = (ctypes.c_void_p * P)(*[t.data_ptr() for t in Ad])
+            b_ptrs = (ctypes.c_void_p * P)(*[t.data_ptr() for t in Bd])
+            ldas = (ctypes.c_int64 * P)(*[_ld(t) for t in Ad])
+            ldbs = (ctypes.c_int64 * P)(*[_ld(t) for t in Bd])
+        else:
+            a_ptrs = b_ptrs = ldas = ldbs = None
         with torch.cuda.stream(st):
-            _check(lib().lora_pool_pack_slot(self.c, int(slot), r, scale,
-                                             _ptr(Ad) if r else None, _ld(Ad) if r else 0,
-                                             _ptr(Bd) if r else None, _ld(Bd) if r else 0,
-                                             _stream(st)))
-        # the copies stay alive until the queued kernels have read them
-        Ad.record_stream(st)
-        Bd.record_stream(st)
+            _check(lib().lora_pool_pack_slot(self.c, int(slot), r, float(alpha), a_ptrs, ldas,
+                                             b_ptrs, ldbs, 1 if rank_rows else 0, _stream(st)))
+        for t in keep:                    # the copies stay alive until the kernels read them
+            t.record_stream(st)
+        self.slot_alpha[slot] = float(alpha)
         self.generation[slot] += 1
         return self.generation[slot]
 
@@ -275,13 +334,12 @@ class Pool:
 
     @classmethod
     def stacked(cls, pools, rank_policy: str = "exact", natural_b: bool = True,
-                dora: bool = False) -> "Pool":
+                dora: bool = False, slot_alpha=None) -> "Pool":
         """One pool serving several projections of the same input (fused QKV,
-        stacked gate/up): the projections' pools must agree on slots, r_max,
-        d_in, dtype, slot ranks and scales.  Projection q's A rows go to rank
-        rows [q r_max, (q + 1) r_max) of each slot, its Bt rows to the same
-        rank rows and its own output columns, zeros elsewhere (a layout
-        only).  The output columns are the projections' in order."""
+        stacked gate/up), packed slot by slot by lora_pool_pack_slot from the
+        projections' pools (which must agree on slots, r_max, d_in, dtype and
+        slot ranks; a slot's alpha is pools[0]'s unless ``slot_alpha`` is
+        given).  The output columns are the projections' in order."""
         p0 = pools[0]
         P = len(pools)
         if not 2 <= P <= 8:
@@ -289,29 +347,20 @@ class Pool:
         for p in pools:
             if (p.n_slots, p.r_max, p.d_in, p.dtype) != (p0.n_slots, p0.r_max, p0.d_in, p0.dtype):
                 raise ValueError("projections must share n_slots, r_max, d_in and dtype")
-            if not torch.equal(p.slot_rank, p0.slot_rank) or not torch.equal(p.slot_scale,
-                                                                             p0.slot_scale):
-                raise ValueError("projections must share slot ranks and scales")
-        cols = [0]
-        for p in pools:
-            cols.append(cols[-1] + p.d_out)
-        rs, d_out = p0.r_max, cols[-1]
-        dev = p0.A.device
-        A = torch.cat([p.A for p in pools], dim=1).contiguous()         # [slots, P rs, d_in]
-        Bt = torch.zeros((p0.n_slots, P * rs, d_out), dtype=p0.dtype, device=dev)
-        for q, p in enumerate(pools):
-            Bt[:, q * rs:(q + 1) * rs, cols[q]:cols[q + 1]] = p.Bt
-        obj = cls.__new__(cls)
-        obj.A, obj.Bt = A, Bt
-        obj.B = Bt.transpose(1, 2).contiguous() if natural_b else None
-        obj.n_slots, obj.r_max, obj.d_in, obj.d_out = p0.n_slots, P * rs, p0.d_in, d_out
-        obj.dtype = p0.dtype
-        obj.slot_rank, obj.slot_scale = p0.slot_rank, p0.slot_scale
-        obj.dora_scale = (torch.ones((obj.n_slots, d_out), dtype=torch.float32, device=dev)
-                          if dora else None)
-        obj.generation = [0] * obj.n_slots
-        obj.proj_cols = (ctypes.c_int32 * (P + 1))(*cols)
-        obj.set_policy(rank_policy)
+            if not torch.equal(p.slot_rank, p0.slot_rank):
+                raise ValueError("projections must share slot ranks")
+        alpha = p0.slot_alpha if slot_alpha is None else \
+            torch.as_tensor(slot_alpha, dtype=torch.float64).reshape(-1).expand(p0.n_slots)
+        obj = cls.empty(p0.n_slots, p0.r_max, p0.d_in, 0, dtype=p0.dtype, device=p0.A.device,
+                        rank_policy=rank_policy, natural_b=natural_b, dora=dora,
+                        proj_outs=[p.d_out for p in pools])
+        ranks = p0.slot_rank.cpu().tolist()
+        for a, r in enumerate(ranks):
+            if 0 < r <= p0.r_max:
+                obj.pack(a, [p.A[a, :r] for p in pools], [p.Bt[a, :r] for p in pools],
+                         float(alpha[a]), b_layout="rank_rows")
+            elif r != 0:
+                raise ValueError(f"slot {a}: rank {r} outside [0, r_max]")
         return obj
 
     def set_policy(self, rank_policy: str):

@@ -204,28 +204,47 @@ lora_status lora_expand(const float *H, const lora_segments *seg, const lora_poo
                                         static_cast<hipStream_t>(stream)));
 }
 
-lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, float scale,
-                                const void *A_src, int64_t lda, const void *B_src, int64_t ldb,
+lora_status lora_pool_pack_slot(const lora_pool *pool, int32_t slot, int32_t rank, double alpha,
+                                const void *const *A_src, const int64_t *lda,
+                                const void *const *B_src, const int64_t *ldb, int32_t b_layout,
                                 void *stream) {
   lora_status st = check_pool(pool);
   if (st != LORA_OK) return st;
-  if (pool->n_proj >= 2) return LORA_ERR_SHAPE;   // stacked pools are laid out by the caller
   if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SHAPE;
-  if (rank < 0 || rank > pool->r_max) return LORA_ERR_SHAPE;
+  if (rank < 0 || rank > pool_rs(pool)) return LORA_ERR_SHAPE;
+  if (b_layout != LORA_B_ROWS && b_layout != LORA_B_RANK_ROWS) return LORA_ERR_SHAPE;
+  const int P = pool->n_proj >= 2 ? pool->n_proj : 1;
   if (rank > 0) {
-    if (!A_src || !B_src) return LORA_ERR_NULL;
-    if (lda < pool->d_in || ldb < rank) return LORA_ERR_SHAPE;
-    if (lda % 8 || !aligned16(A_src)) return LORA_ERR_ALIGN;
-  } else {
-    // nothing is read; the pool's own arrays stand in for the sources
-    A_src = pool->A;
-    lda = pool->d_in;
-    B_src = pool->Bt;
-    ldb = 1;
+    if (!A_src || !lda || !B_src || !ldb) return LORA_ERR_NULL;
+    for (int q = 0; q < P; ++q) {
+      const int64_t cols = P > 1 ? pool->proj_cols[q + 1] - pool->proj_cols[q] : pool->d_out;
+      if (!A_src[q] || !B_src[q]) return LORA_ERR_NULL;
+      if (lda[q] < pool->d_in) return LORA_ERR_SHAPE;
+      if (lda[q] % 8 || !aligned16(A_src[q])) return LORA_ERR_ALIGN;
+      if (ldb[q] < (b_layout == LORA_B_ROWS ? (int64_t)rank : cols)) return LORA_ERR_SHAPE;
+    }
   }
   return hip_status(lora::launch_pack_slot(
-      pool_view(pool), const_cast<int32_t *>(pool->slot_rank), const_cast<float *>(pool->slot_scale),
-      slot, rank, scale, A_src, lda, B_src, ldb, static_cast<hipStream_t>(stream)));
+      pool_view(pool), const_cast<int32_t *>(pool->slot_rank),
+      const_cast<float *>(pool->slot_scale), slot, rank, alpha, A_src, lda, B_src, ldb,
+      b_layout == LORA_B_RANK_ROWS, static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_pool_set_scales(const lora_pool *pool, const double *slot_alpha, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (!slot_alpha) return LORA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(slot_alpha) & 7u) return LORA_ERR_ALIGN;
+  return hip_status(lora::launch_set_scales(pool->slot_rank, slot_alpha,
+                                            const_cast<float *>(pool->slot_scale), pool->n_slots,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_pool_write_b(const lora_pool *pool, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (!pool->B) return LORA_ERR_NULL;
+  return hip_status(lora::launch_write_b(pool_view(pool), static_cast<hipStream_t>(stream)));
 }
 
 lora_status lora_pool_dora_prepare(const lora_pool *pool, int32_t slot, const void *W,

@@ -81,10 +81,20 @@ hipError_t launch_build_shrink(const BuildArgs &a, const void *X, int64_t ldx,
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream);
 
-// Adapter weights into a slot, then the slot's rank and scale.
+// Adapter weights into a slot (one source per projection), then the slot's
+// rank and scale alpha / rank.  b_rank_rows: B sources are [rank][ldb]
+// (B^T) instead of [d_out_q][ldb].
 hipError_t launch_pack_slot(const PoolView &pool, int32_t *slot_rank, float *slot_scale, int slot,
-                            int rank, float scale, const void *A_src, int64_t lda,
-                            const void *B_src, int64_t ldb, hipStream_t stream);
+                            int rank, double alpha, const void *const *A_src, const int64_t *lda,
+                            const void *const *B_src, const int64_t *ldb, int b_rank_rows,
+                            hipStream_t stream);
+
+// slot_scale[a] = alpha[a] / slot_rank[a] (0 for rank <= 0), on the device.
+hipError_t launch_set_scales(const int32_t *slot_rank, const double *alpha, float *slot_scale,
+                             int n_slots, hipStream_t stream);
+
+// The pool's d_out-major B from its Bt, every slot.
+hipError_t launch_write_b(const PoolView &pool, hipStream_t stream);
 
 // DoRA column factors of one slot from its current contents and W.
 hipError_t launch_dora_prepare(const PoolView &pool, const int32_t *slot_rank,

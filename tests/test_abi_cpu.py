@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     for n in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_linear_fused",
               "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
               "lora_base_gemm_fp8w", "lora_linear_fused_fp8w", "lora_status_str",
-              "lora_abi_version", "lora_linear_fused_static"):
+              "lora_abi_version", "lora_linear_fused_static", "lora_pool_set_scales",
+              "lora_pool_write_b"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 5
+    assert L.lora_abi_version() == srg.ABI_VERSION == 6
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
@@ -139,23 +140,44 @@ def test_empty_batch_is_a_noop_without_launch(L):
     assert L.lora_base_gemm(0, 64, P, 64, 0, 32, 0, 64, 32, 1, None) == OK
 
 
+def _arr(kind, *vals):
+    return (kind * len(vals))(*vals)
+
+
 def test_pack_slot_validation(L):
     """Every bad argument is rejected on the host (nothing is launched)."""
     p = ctypes.byref(pool())                        # 4 slots, r_max 16, d_in 64, d_out 32
-    A, B = P + 0xC000, P + 0xD000
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    A, B = _arr(vp, P + 0xC000), _arr(vp, P + 0xD000)
+    la, lb = _arr(i64, 64), _arr(i64, 8)
     pack = L.lora_pool_pack_slot
-    assert pack(None, 0, 8, 2.0, A, 64, B, 8, None) == ENULL
-    assert pack(p, -1, 8, 2.0, A, 64, B, 8, None) == ESHAPE
-    assert pack(p, 4, 8, 2.0, A, 64, B, 8, None) == ESHAPE
-    assert pack(p, 0, 17, 1.0, A, 64, B, 17, None) == ESHAPE
-    assert pack(p, 0, -1, 1.0, A, 64, B, 8, None) == ESHAPE
-    assert pack(p, 0, 8, 2.0, None, 64, B, 8, None) == ENULL
-    assert pack(p, 0, 8, 2.0, A, 64, None, 8, None) == ENULL
-    assert pack(p, 0, 8, 2.0, A, 56, B, 8, None) == ESHAPE       # lda < d_in
-    assert pack(p, 0, 8, 2.0, A, 68, B, 8, None) == EALIGN       # lda % 8
-    assert pack(p, 0, 8, 2.0, A + 4, 64, B, 8, None) == EALIGN   # A not 16-byte aligned
-    assert pack(p, 0, 8, 2.0, A, 64, B, 7, None) == ESHAPE       # ldb < rank
-    assert pack(ctypes.byref(pool(A=0)), 0, 8, 2.0, A, 64, B, 8, None) == ENULL
+    assert pack(None, 0, 8, 16.0, A, la, B, lb, 0, None) == ENULL
+    assert pack(p, -1, 8, 16.0, A, la, B, lb, 0, None) == ESHAPE
+    assert pack(p, 4, 8, 16.0, A, la, B, lb, 0, None) == ESHAPE
+    assert pack(p, 0, 17, 16.0, A, la, B, _arr(i64, 17), 0, None) == ESHAPE
+    assert pack(p, 0, -1, 16.0, A, la, B, lb, 0, None) == ESHAPE
+    assert pack(p, 0, 8, 16.0, A, la, B, lb, 2, None) == ESHAPE        # unknown B layout
+    assert pack(p, 0, 8, 16.0, None, la, B, lb, 0, None) == ENULL
+    assert pack(p, 0, 8, 16.0, A, None, B, lb, 0, None) == ENULL
+    assert pack(p, 0, 8, 16.0, _arr(vp, 0), la, B, lb, 0, None) == ENULL
+    assert pack(p, 0, 8, 16.0, A, la, None, lb, 0, None) == ENULL
+    assert pack(p, 0, 8, 16.0, A, la, _arr(vp, 0), lb, 0, None) == ENULL
+    assert pack(p, 0, 8, 16.0, A, _arr(i64, 56), B, lb, 0, None) == ESHAPE   # lda < d_in
+    assert pack(p, 0, 8, 16.0, A, _arr(i64, 68), B, lb, 0, None) == EALIGN   # lda % 8
+    assert pack(p, 0, 8, 16.0, _arr(vp, P + 0xC004), la, B, lb, 0, None) == EALIGN
+    assert pack(p, 0, 8, 16.0, A, la, B, _arr(i64, 7), 0, None) == ESHAPE    # ldb < rank
+    assert pack(p, 0, 8, 16.0, A, la, B, _arr(i64, 31), 1, None) == ESHAPE   # ldb < d_out (B^T)
+    assert pack(ctypes.byref(pool(A=0)), 0, 8, 16.0, A, la, B, lb, 0, None) == ENULL
+
+
+def test_set_scales_and_write_b_validation(L):
+    p = ctypes.byref(pool())
+    assert L.lora_pool_set_scales(None, P, None) == ENULL
+    assert L.lora_pool_set_scales(p, None, None) == ENULL
+    assert L.lora_pool_set_scales(p, P + 4, None) == EALIGN              # double array
+    assert L.lora_pool_set_scales(ctypes.byref(pool(dtype=7)), P, None) == EDTYPE
+    assert L.lora_pool_write_b(p, None) == ENULL                         # pool without B
+    assert L.lora_pool_write_b(ctypes.byref(pool(B=P + 0x4008)), None) == EALIGN
 
 
 def test_dora_prepare_validation(L):
@@ -246,9 +268,23 @@ def test_stacked_pool_column_offsets(L, cols):
     assert shrink(L, p, segs()) == ESHAPE
 
 
-def test_stacked_pool_is_not_packed(L):
+def test_stacked_pool_pack_validation(L):
+    """A stacked pool takes one A and one B source per projection, each B
+    checked against its own projection's width; ranks are bounded by the
+    per-projection rank stride."""
     p = ctypes.byref(pool(n_proj=3, r_max=48, d_out=48, proj_cols=_cols(0, 16, 24, 48)))
-    assert L.lora_pool_pack_slot(p, 0, 8, 2.0, P + 0xC000, 64, P + 0xD000, 8, None) == ESHAPE
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    A = _arr(vp, P + 0xC000, P + 0xC400, P + 0xC800)
+    B = _arr(vp, P + 0xD000, P + 0xD400, P + 0xD800)
+    la = _arr(i64, 64, 64, 64)
+    pack = L.lora_pool_pack_slot
+    assert pack(p, 0, 17, 16.0, A, la, B, _arr(i64, 17, 17, 17), 0, None) == ESHAPE  # rs 16
+    assert pack(p, 0, 8, 16.0, _arr(vp, P + 0xC000, 0, P + 0xC800), la, B,
+                _arr(i64, 8, 8, 8), 0, None) == ENULL
+    # B^T sources: ldb >= 16, 8 and 24 columns
+    assert pack(p, 0, 8, 16.0, A, la, B, _arr(i64, 16, 8, 23), 1, None) == ESHAPE
+    assert pack(p, 0, 8, 16.0, A, _arr(i64, 64, 64, 60), B, _arr(i64, 16, 8, 24), 1,
+                None) == ESHAPE
 
 
 def test_expand_and_fused_validation(L):
