@@ -21,9 +21,9 @@
  *   the host and returned before anything is launched; no output is touched
  *   then.  LORA_ERR_HIP reports a failed launch.
  * - Row-major storage.  Leading dimensions (`ld*`) are in elements, at least
- *   the row width, and multiples of 8; every tensor base pointer is 16-byte
- *   aligned; d_in and d_out are positive multiples of 8.  Otherwise
- *   LORA_ERR_ALIGN / LORA_ERR_SHAPE.
+ *   the row width, at most LORA_MAX_LD, and multiples of 8; every tensor base
+ *   pointer is 16-byte aligned; d_in and d_out are positive multiples of 8.
+ *   Otherwise LORA_ERR_ALIGN / LORA_ERR_SHAPE.
  * - X, W, Y, A and Bt share the pool's dtype (bf16 or fp32).  H is fp32.
  *   Accumulation is fp32.
  * - Data errors found on the device (a row's slot outside [-1, n_slots) or
@@ -48,6 +48,9 @@ extern "C" {
  * and n_rows * r_max (the entries of its H). */
 #define LORA_STATIC_MAX_ROWS 32768
 #define LORA_STATIC_MAX_H (1 << 21)
+/* Largest leading dimension of X, W, Y (elements): the GEMM addresses a tile's
+ * rows with 32-bit byte offsets from its first row. */
+#define LORA_MAX_LD (1 << 22)
 
 typedef enum {
   LORA_OK = 0,

@@ -379,8 +379,9 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
-  const int kgrp = tid / (kWave * C::NWG);          // K group (wave-uniform)
-  const int wid = (tid / kWave) % C::NWG;           // wave within the group
+  // K group and wave within it (wave-uniform: scalar registers)
+  const int kgrp = __builtin_amdgcn_readfirstlane(tid / (kWave * C::NWG));
+  const int wid = __builtin_amdgcn_readfirstlane((tid / kWave) % C::NWG);
   const int wm = wid / WN, wn = wid % WN;
   const int kg0 = kgrp * BK;                        // the group's offset in a K step
   const int M = g.M, N = g.N, K = g.K;
@@ -410,25 +411,27 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   // Small tiles (two K groups) finish row by row: thread tid owns tile row
   // tid / (BN / 8) and 8 consecutive columns (see the end of the kernel);
   // in larger tiles thread tid < BM holds tile row tid's metadata for the
-  // LoRA term.  The row's segment id is loaded before the first DMA and its
-  // segment's rank, slot and scale right after the first stage has landed,
-  // so all have long arrived by the epilogue.  The loads are issued by hand
-  // (the compiler would sink them to their uses) and waited for explicitly.
+  // LoRA term.  The row's segment id (and, with an FP8 weight, the thread's
+  // 8 column scales) are loaded before the first DMA, and the segment's
+  // rank, slot and scale right after the prologue's wait, so all have
+  // arrived by the epilogue.  They are ordinary loads, waited for by the
+  // compiler: it does not see the DMAs, so its waits count only these loads,
+  // and it can only wait for more than it needs (the column scales are
+  // requested first, so the segment id is the newest load when it is used).
   constexpr bool ROWEPI = KG > 1;
   static_assert(!ROWEPI || C::T * 8 == BM * BN, "row epilogue: 8 outputs per thread");
   static_assert(ROWEPI || C::T >= BM, "one tile row per thread");
   const int e_row = ROWEPI ? tid / (BN / 8) : tid, e_c8 = (tid % (BN / 8)) * 8;
   const bool e_own = ROWEPI || tid < BM;            // the thread holds row e_row's metadata
-  int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
-  if constexpr (LORA != 0)
-    if (e_own) e_seg = gload_b32(g.row_segment + min(m0 + e_row, M - 1));
-  // FP8 weight: the thread's 8 column scales, requested now as well
-  u32x4 e_ws0 = u32x4{0, 0, 0, 0}, e_ws1 = u32x4{0, 0, 0, 0};
+  f32x4 e_ws0 = f32x4{0.f, 0.f, 0.f, 0.f}, e_ws1 = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (ROWEPI && WF8) {
     const float *ws = g.wscale + min(n0 + e_c8, N - 8);
-    e_ws0 = gload_b128(ws);
-    e_ws1 = gload_b128(ws + 4);
+    e_ws0 = *reinterpret_cast<const f32x4 *>(ws);
+    e_ws1 = *reinterpret_cast<const f32x4 *>(ws + 4);
   }
+  int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
+  if constexpr (LORA != 0)
+    if (e_own) e_seg = g.row_segment[min(m0 + e_row, M - 1)];
 
   // DMA sources: lane l of an instruction fills tile row base + l / CH at
   // physical chunk l % CH, i.e. logical chunk swz(l % CH, row) (a function
@@ -480,6 +483,75 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     else
       dma16(b_dst + stage * C::STAGE + (q - C::AI) * 1024, bsrc[q - C::AI] + boff(q - C::AI, k0));
   };
+  // Stage ownership (rings of more than two stages): wave wid of each K
+  // group owns ring buffer wid and alone fills its group's slice of every
+  // stage that lands there -- the slice's A rows, then its B rows, NIG 1 KB
+  // instructions, sources computed per instruction.  A wave therefore never
+  // has more than one stage in flight, and before a stage is read its owners
+  // wait for all of their loads (vmcnt(0)) and then the workgroup passes the
+  // barrier: no wait depends on the order in which DMAs complete.  Two-stage
+  // rings need no owners: at each wait only the stage about to be read is in
+  // flight, so every wave waits vmcnt(0) for its share of it.
+  constexpr bool OWNED = STAGES > 2;
+  static_assert(!OWNED || C::NWG == STAGES, "one owner wave per ring buffer in each K group");
+  constexpr int AIG = BM / C::RPI, NIG = AIG + BN / C::RPIB;   // instructions per slice
+  constexpr int EBW = WF8 ? 1 : 2;                             // bytes per W element
+  // Sources of the owner's instructions: the tile's first A and B rows as
+  // scalar bases, and per lane the byte offset of its row (rows past M / N
+  // clamped to the last) and chunk from them -- below 2^32 because leading
+  // dimensions are below 2^22 elements and tiles have at most 256 rows.
+  const unsigned char *const xa = reinterpret_cast<const unsigned char *>(g.X + (int64_t)m0 * g.ldx);
+  const unsigned char *const wb = reinterpret_cast<const unsigned char *>(g.W) +
+                                  (int64_t)n0 * g.ldw * EBW;
+  uint32_t own_off[OWNED ? NIG : 1];
+  if constexpr (OWNED) {
+#pragma unroll
+    for (int t = 0; t < NIG; ++t) {
+      if (t < AIG) {
+        const int row = t * C::RPI + rr;
+        own_off[t] = (uint32_t)((min(m0 + row, M - 1) - m0) * g.ldx * 2) +
+                     C::swz(l % C::CH, row) * 16;
+      } else {
+        const int row = (t - AIG) * C::RPIB + rrb;
+        own_off[t] = (uint32_t)((min(n0 + row, N - 1) - n0) * g.ldw * EBW) +
+                     C::swzb(l % C::CHB, row) * 16;
+      }
+    }
+  }
+  // instruction t of the group's slice of the stage at K position k0 into
+  // buffer buf; `tail`: the stage reaches past K, where a chunk past K reads
+  // its row's first chunk instead (in bounds; zeroed before use)
+  auto issue_own_one = [&](int t, int buf, int k0, bool tail) __attribute__((always_inline)) {
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane(sbase + buf * C::STAGE + kgrp * C::GSTAGE + t * 1024);
+    if (t < AIG) {
+      if (!tail) {
+        dma16_s(dst, own_off[t], xa + (int64_t)k0 * 2);
+      } else {
+        // the base stays scalar: the K position goes into the lane offsets
+        const int row = t * C::RPI + rr;
+        const int c = C::swz(l % C::CH, row);
+        dma16_s(dst, k0 + c * 8 < K ? own_off[t] + k0 * 2 : own_off[t] - c * 16, xa);
+      }
+    } else {
+      if (!tail) {
+        dma16_s(dst, own_off[t], wb + (int64_t)k0 * EBW);
+      } else {
+        const int row = (t - AIG) * C::RPIB + rrb;
+        const int c = C::swzb(l % C::CHB, row);
+        dma16_s(dst, k0 + c * C::EPCB < K ? own_off[t] + k0 * EBW : own_off[t] - c * 16, wb);
+      }
+    }
+  };
+  auto zero_tail_own = [&](int buf, int k0) {
+    unsigned char *st = smem + buf * C::STAGE + kgrp * C::GSTAGE;
+#pragma unroll
+    for (int t = 0; t < NIG; ++t) {
+      const bool past = t < AIG ? k0 + C::swz(l % C::CH, t * C::RPI + rr) * 8 >= K
+                                : k0 + C::swzb(l % C::CHB, (t - AIG) * C::RPIB + rrb) * C::EPCB >= K;
+      if (past) *reinterpret_cast<u32x4 *>(st + t * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+    }
+  };
   auto zero_tail = [&](int stage, int k0) {
     unsigned char *st = smem + stage * C::STAGE + kgrp * C::GSTAGE;
 #pragma unroll
@@ -527,10 +599,19 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
 
   const int KT = (K + C::KSTEP - 1) / C::KSTEP;
   const bool ktail = (K % C::KSTEP) != 0;
-  // every buffer of the ring is free at the start: fill all of them
+  // every buffer of the ring is free at the start: fill all of them (with
+  // owners, each wave fills its own buffer)
+  if constexpr (OWNED) {
+    if (wid < KT) {
+      const bool tail = ktail && wid == KT - 1;
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < KT) issue(s, s * C::KSTEP + kg0);
+      for (int t = 0; t < NIG; ++t) issue_own_one(t, wid, wid * C::KSTEP + kg0, tail);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < KT) issue(s, s * C::KSTEP + kg0);
+  }
 
   // Software pipeline over K.  Fragments of sub-step kk + 1 are read from
   // LDS while the MFMAs of sub-step kk run.  Before the last sub-step of
@@ -575,24 +656,23 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
   };
 
-  // stage 0 landed (the later stages may stay in flight)
-  // The first stage is waited for together with every prologue stage:
-  // DMAs issued back to back can land out of order (with a one-stage
-  // allowance a stage issued right after stage 0 counted as landed while
-  // part of stage 0 had not, on cold operands), so counts of later DMAs
-  // left in flight are only trusted in the loop, where each was issued at
-  // least one stage after the one waited for.
+  // Every wave waits for all of its prologue loads (its stage, or its share
+  // of each stage, and the metadata above) before the first barrier.
   vm_wait<0>();
   if constexpr (LORA != 0) {
-    // the segment id was loaded before stage 0, so it has landed too
-    asm volatile("" : "+v"(e_seg));
     if (e_own) {
-      e_r = gload_b32(g.seg_rank + e_seg);
-      e_slot = gload_b32(g.seg_slot + e_seg);
-      e_scb = gload_b32(g.seg_scale + e_seg);
+      e_r = g.seg_rank[e_seg];
+      e_slot = g.seg_slot[e_seg];
+      e_scb = __float_as_int(g.seg_scale[e_seg]);
     }
   }
-  if (ktail && KT == 1) zero_tail(0, kg0);
+  if (ktail && KT == 1) {
+    if constexpr (OWNED) {
+      if (wid == 0) zero_tail_own(0, kg0);
+    } else {
+      zero_tail(0, kg0);
+    }
+  }
   lgkm_barrier();
   load_frags(0, smem, 0);
   for (int kt = 0; kt < KT; ++kt) {
@@ -604,10 +684,19 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       interleave();
     }
     if (kt + 1 < KT) {
-      // stages issued so far: 0 .. min(kt - 1 + STAGES, KT - 1); the ones
-      // after kt + 1 may stay in flight
-      wait_ahead<C::IPW>(min(STAGES - 2, KT - 2 - kt));
-      if (ktail && kt + 1 == KT - 1) zero_tail((kt + 1) % STAGES, (kt + 1) * C::KSTEP + kg0);
+      // stage kt + 1 lands: with owners, the owners of its buffer wait for
+      // their one stage in flight; otherwise it is the only stage in flight
+      // and every wave waits for its share
+      if constexpr (OWNED) {
+        if (wid == (kt + 1) % STAGES) {
+          vm_wait<0>();
+          if (ktail && kt + 1 == KT - 1) zero_tail_own(wid, (kt + 1) * C::KSTEP + kg0);
+        }
+      } else {
+        static_assert(STAGES == 2, "without owners only one stage may be in flight");
+        vm_wait<0>();
+        if (ktail && kt + 1 == KT - 1) zero_tail((kt + 1) % STAGES, (kt + 1) * C::KSTEP + kg0);
+      }
       lgkm_barrier();
     }
     // Last sub-step: its MFMAs with the refill of stage kt's buffer, one DMA
@@ -621,11 +710,29 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // stage refill starts as early as possible (measured 3% on the prefill
     // and 70B-shaped products; the two-group decode tiles gain nothing).
     if constexpr (KG == 1) __builtin_amdgcn_s_setprio(1);
-    const bool refill = kt + STAGES < KT;
+    // the freed buffer kt % STAGES takes stage kt + STAGES (with owners, only
+    // its owners issue, their whole slices)
+    const bool refill = kt + STAGES < KT && (!OWNED || wid == kt % STAGES);
     const int k0n = (kt + STAGES) * C::KSTEP + kg0;
+    // the stage reaching past K (at most one) is issued whole, ahead of the
+    // MFMAs, so the interleaved loop below needs no per-instruction test
+    const bool tailn = ktail && kt + STAGES == KT - 1;
+    if constexpr (OWNED) {
+      if (refill && tailn) {
 #pragma unroll
-    for (int q = 0; q < C::FM * C::FN || q < C::IPW; ++q) {
-      if (q < C::IPW && refill) issue_one(q, kt % STAGES, k0n);
+        for (int q = 0; q < NIG; ++q) issue_own_one(q, kt % STAGES, k0n, true);
+      }
+    }
+    const bool refill_fast = refill && (!OWNED || !tailn);
+    constexpr int NIS = OWNED ? NIG : C::IPW;         // instructions per issuing wave
+#pragma unroll
+    for (int q = 0; q < C::FM * C::FN || q < NIS; ++q) {
+      if (q < NIS && refill_fast) {
+        if constexpr (OWNED)
+          issue_own_one(q, kt % STAGES, k0n, false);
+        else
+          issue_one(q, kt % STAGES, k0n);
+      }
       if (q < C::FM * C::FN) {
         const int i = q / C::FN, j = q % C::FN;
         constexpr int b = (KK - 1) & 1;
@@ -656,11 +763,6 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // (k ascending, read in chunks of 8 rank rows; rows at or past r are
     // read inside the slot and skipped), the DoRA factor when the pool has
     // one, and one rounding; the 8 results leave in one 16-byte store.
-    if constexpr (WF8)
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb), "+v"(e_ws0),
-                   "+v"(e_ws1)::"memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
     lgkm_barrier();
     float *red = reinterpret_cast<float *>(smem);
     constexpr int RS = BN + 4;
@@ -693,8 +795,8 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     if constexpr (WF8) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] *= __uint_as_float(e_ws0[e]);
-        o[4 + e] *= __uint_as_float(e_ws1[e]);
+        o[e] *= e_ws0[e];
+        o[4 + e] *= e_ws1[e];
       }
     }
     if constexpr (LORA != 0) {
@@ -777,8 +879,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     int *s_rowslot = reinterpret_cast<int *>(smem + 2 * BM * RBL + BN * RBL + 16);
     auto sw = [](int c, int r) { return ((c ^ ((r >> 1) & 7)) * 16); };
     // this thread's tile row (threads past BM take no row): its segment if
-    // that has a LoRA term (all DMAs and the metadata loads are done)
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(e_seg), "+v"(e_r), "+v"(e_slot), "+v"(e_scb)::"memory");
+    // that has a LoRA term
     const int my_seg = (tid < BM && m0 + tid < M && e_r > 0) ? e_seg : -1;
     int *s_rr = reinterpret_cast<int *>(smem + EPI_META);   // per row: segment, later rank
     int *s_rslot = s_rr + BM;                               //          slot

@@ -14,7 +14,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Direct global -> LDS loads (gfx950 global_load_lds_dwordx4).  Each
 // instruction moves 64 lanes x 16 bytes into 1 KB of LDS starting at M0.
 // Issued through inline asm so that the compiler does not add conservative
-// waits on them; completion is tracked by hand with s_waitcnt vmcnt.
+// waits on them; completion is tracked by hand with s_waitcnt vmcnt(0) only
+// (a wave waits for all of its loads, never for a count of them, so no wait
+// depends on the order in which loads complete).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
@@ -22,6 +24,13 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 
 __device__ __forceinline__ void dma16(uint32_t m0, const void *src) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
+// The same with the source given as a 64-bit scalar base plus a 32-bit
+// per-lane byte offset (the instruction's saddr form).
+__device__ __forceinline__ void dma16_s(uint32_t m0, uint32_t off, const void *base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(base)
                : "memory", "m0");
 }
 
@@ -38,37 +47,6 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void lgkm_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int IPW>
-__device__ __forceinline__ void wait_ahead(int ahead) {
-  // this wave's DMAs of the `ahead` later stages may stay in flight
-  switch (ahead) {
-    case 0: vm_wait<0>(); break;
-    case 1: vm_wait<(IPW < 63 ? IPW : 63)>(); break;
-    case 2: vm_wait<(2 * IPW < 63 ? 2 * IPW : 63)>(); break;
-    case 3: vm_wait<(3 * IPW < 63 ? 3 * IPW : 63)>(); break;
-    case 4: vm_wait<(4 * IPW < 63 ? 4 * IPW : 63)>(); break;
-    case 5: vm_wait<(5 * IPW < 63 ? 5 * IPW : 63)>(); break;
-    default: vm_wait<(6 * IPW < 63 ? 6 * IPW : 63)>(); break;
-  }
-}
-
-
-// 4-byte global load issued where it is written; the caller waits for it
-// (s_waitcnt vmcnt) before the first use of the result.
-__device__ __forceinline__ int gload_b32(const void *p) {
-  int r;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-
-// 16-byte global load issued where it is written; the caller waits for it
-// (s_waitcnt vmcnt) before the first use of the result.
-__device__ __forceinline__ u32x4 gload_b128(const void *p) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
 }
 
 __device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }

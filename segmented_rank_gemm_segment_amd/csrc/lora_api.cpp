@@ -71,7 +71,7 @@ lora_status check_segments(const lora_segments *seg, const lora_pool *pool) {
 lora_status check_matrix(const void *p, int64_t ld, int32_t width, int32_t rows) {
   if (rows == 0) return LORA_OK;
   if (!p) return LORA_ERR_NULL;
-  if (ld < width) return LORA_ERR_SHAPE;
+  if (ld < width || ld > LORA_MAX_LD) return LORA_ERR_SHAPE;
   if (ld % 8 || !aligned16(p)) return LORA_ERR_ALIGN;
   return LORA_OK;
 }
@@ -100,7 +100,7 @@ lora_status check_fp8_weight(const void *Wq, int64_t ldw, const float *w_scale, 
                              int32_t d_out) {
   if (d_in % 16) return LORA_ERR_ALIGN;
   if (!Wq || !w_scale) return LORA_ERR_NULL;
-  if (ldw < d_in) return LORA_ERR_SHAPE;
+  if (ldw < d_in || ldw > LORA_MAX_LD) return LORA_ERR_SHAPE;
   if (ldw % 16 || !aligned16(Wq) || !aligned16(w_scale)) return LORA_ERR_ALIGN;
   (void)d_out;
   return LORA_OK;

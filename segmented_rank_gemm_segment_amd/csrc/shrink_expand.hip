@@ -83,7 +83,13 @@ __global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
 // SM rows x SN rank columns per tile (one 32 x 32 MFMA block per wave),
 // K = d_in streamed through a 6-stage LDS ring with direct global->LDS
 // loads (the row gather is free: every lane supplies its own source
-// address).  Each X row is read once per segment tile instead of once per
+// address).  The workgroup has one wave per ring buffer: the four MFMA
+// waves and two that only load.  Wave w owns ring buffer w and alone fills
+// every stage that lands there, so a wave never has more than one stage in
+// flight, and before a stage is read its owner waits for all of its loads
+// (vmcnt(0)) and the workgroup passes a barrier: no wait depends on the
+// order in which DMAs complete.  Every wave walks the same items and
+// barriers (all control flow is workgroup-uniform).  Each X row is read once per segment tile instead of once per
 // rank row.  Work items are the position blocks of the segment order
 // (seg_item with rb = SM) of segments of at least kLongRows rows, times the
 // rank tiles (blockIdx.x).  Rank rows past R are not fetched (their loads
@@ -91,41 +97,42 @@ __global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
 // ----------------------------------------------------------------------------
 constexpr int kLongRows = 128;   // segments at least this long take the MFMA path
 constexpr int kMfmaShrinkMinBatch = 2048;
-constexpr int kSStages = 6;
+constexpr int kSStages = 6;   // ring buffers = waves of the workgroup
 
 template <int SM, int SN>
-__global__ __launch_bounds__((SM / 32) * (SN / 32) * kWave) void shrink_mfma_kernel(
+__global__ __launch_bounds__(kSStages * kWave) void shrink_mfma_kernel(
     const bf16_t *__restrict__ X, int64_t ldx, const bf16_t *__restrict__ A,
     const int32_t *token_indices, const int32_t *row_segment, const int32_t *seg_off,
     const int32_t *seg_slot, const int32_t *seg_rank, const int32_t *num_segments, int r_max,
     int rs, int d_in, int policy, int nb, int seg_cap, float *__restrict__ H) {
   constexpr int NWN = SN / 32;                      // waves along the rank columns
-  constexpr int NW = (SM / 32) * NWN;
-  constexpr int AI = SM / 8 / NW, BI = SN / 8 / NW, IPW = AI + BI;
-  static_assert(AI >= 1 && BI >= 1 && SM % (8 * NW) == 0 && SN % (8 * NW) == 0, "DMA split");
+  constexpr int NWC = (SM / 32) * NWN;              // MFMA waves
+  constexpr int AI = SM / 8, BI = SN / 8;            // 1 KB instructions of a stage (owner)
+  static_assert(NWC <= kSStages, "one owner wave per ring buffer, MFMA waves among them");
   constexpr int STAGE = (SM + SN) * 128;
   constexpr int BK = 64;
   __shared__ __align__(16) unsigned char smem[kSStages * STAGE];
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  const int wm = wid / NWN, wn = wid % NWN;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool mfma_wave = wid < NWC;
+  const int wm = (wid % NWC) / NWN, wn = wid % NWN;
   // 128-byte LDS rows, chunk c of row r at c ^ ((r >> 1) & 7): 16
   // consecutive rows at one chunk hit 16 distinct bank groups
   const int r8 = l >> 3;
   const uint32_t sbase = lds_offset(smem);
-  const uint32_t a_dst = __builtin_amdgcn_readfirstlane(sbase + wid * AI * 1024);
-  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(sbase + SM * 128 + wid * BI * 1024);
   const int a_row_off = (wm * 32 + (l & 31)) * 128;
   const int b_row_off = SM * 128 + (wn * 32 + (l & 31)) * 128;
   int chunk_off[BK / 16];
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) chunk_off[kk] = (((kk * 2 + (l >> 5)) ^ ((l >> 1) & 7)) * 16);
+  // logical chunk of lane l in instruction i (rows i * 8 + l / 8 of the
+  // stage's A or B part)
   int alc[AI], blc[BI];
 #pragma unroll
-  for (int i = 0; i < AI; ++i) alc[i] = (l & 7) ^ ((((wid * AI + i) * 8 + r8) >> 1) & 7);
+  for (int i = 0; i < AI; ++i) alc[i] = (l & 7) ^ (((i * 8 + r8) >> 1) & 7);
 #pragma unroll
-  for (int i = 0; i < BI; ++i) blc[i] = (l & 7) ^ ((((wid * BI + i) * 8 + r8) >> 1) & 7);
+  for (int i = 0; i < BI; ++i) blc[i] = (l & 7) ^ (((i * 8 + r8) >> 1) & 7);
   const int KT = (d_in + BK - 1) / BK;
   const bool ktail = (d_in % BK) != 0;
   const int S = __builtin_amdgcn_readfirstlane(*num_segments);
@@ -147,7 +154,7 @@ __global__ __launch_bounds__((SM / 32) * (SN / 32) * kWave) void shrink_mfma_ker
     const bf16_t *bsrc[BI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      const int p = min(p0 + (wid * AI + i) * 8 + r8, p1 - 1);
+      const int p = min(p0 + i * 8 + r8, p1 - 1);
       asrc[i] = X + (int64_t)token_indices[p] * ldx + alc[i] * 8;
     }
 #pragma unroll
@@ -155,60 +162,74 @@ __global__ __launch_bounds__((SM / 32) * (SN / 32) * kWave) void shrink_mfma_ker
       // pool rank row kg, kl rows into its projection's block; rows past the
       // processed width R re-read the block's last processed row (in the
       // slot) and are not stored
-      const int kg = rt * SN + (wid * BI + i) * 8 + r8;
+      const int kg = rt * SN + i * 8 + r8;
       const int kl = kg % rs;
       const int k = min(kl < R ? kg : kg - kl + R - 1, r_max - 1);
       bsrc[i] = A + ((int64_t)slot * r_max + k) * d_in + blc[i] * 8;
     }
+    // the whole stage at K position k0 into buffer `stage` (its owner only);
+    // a chunk past d_in reads the row's first chunk instead (in bounds) and
+    // is zeroed before use
     auto issue = [&](int stage, int k0) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + stage * STAGE);
+      if (k0 + BK <= d_in) {
 #pragma unroll
-      for (int i = 0; i < AI; ++i)
-        dma16(a_dst + stage * STAGE + i * 1024, asrc[i] + ((k0 + alc[i] * 8 < d_in) ? k0 : -alc[i] * 8));
+        for (int i = 0; i < AI; ++i) dma16(dst + i * 1024, asrc[i] + k0);
 #pragma unroll
-      for (int i = 0; i < BI; ++i)
-        dma16(b_dst + stage * STAGE + i * 1024, bsrc[i] + ((k0 + blc[i] * 8 < d_in) ? k0 : -blc[i] * 8));
+        for (int i = 0; i < BI; ++i) dma16(dst + SM * 128 + i * 1024, bsrc[i] + k0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+          dma16(dst + i * 1024, asrc[i] + ((k0 + alc[i] * 8 < d_in) ? k0 : -alc[i] * 8));
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+          dma16(dst + SM * 128 + i * 1024, bsrc[i] + ((k0 + blc[i] * 8 < d_in) ? k0 : -blc[i] * 8));
+      }
     };
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-    for (int st = 0; st < kSStages - 1; ++st)
-      if (st < KT) issue(st, st * BK);
+    // prologue: stages 0 .. kSStages - 2, stage w by wave w
+    if (wid < kSStages - 1 && wid < KT) issue(wid, wid * BK);
     for (int kt = 0; kt < KT; ++kt) {
-      // the first step waits for every prologue stage (DMAs issued back to
-      // back can land out of order); later steps leave the stages issued
-      // after the one they wait for in flight
-      if (kt == 0)
+      // stage kt lands: its owner waits for its one stage in flight
+      if (wid == kt % kSStages) {
         vm_wait<0>();
-      else
-        wait_ahead<IPW>(min(kSStages - 2, KT - 1 - kt));
-      if (ktail && kt == KT - 1) {
-        unsigned char *st = smem + (kt % kSStages) * STAGE;
+        if (ktail && kt == KT - 1) {
+          unsigned char *st = smem + wid * STAGE;
 #pragma unroll
-        for (int i = 0; i < AI; ++i)
-          if (kt * BK + alc[i] * 8 >= d_in)
-            *reinterpret_cast<u32x4 *>(st + (wid * AI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+          for (int i = 0; i < AI; ++i)
+            if (kt * BK + alc[i] * 8 >= d_in)
+              *reinterpret_cast<u32x4 *>(st + i * 1024 + l * 16) = u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < BI; ++i)
-          if (kt * BK + blc[i] * 8 >= d_in)
-            *reinterpret_cast<u32x4 *>(st + SM * 128 + (wid * BI + i) * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+          for (int i = 0; i < BI; ++i)
+            if (kt * BK + blc[i] * 8 >= d_in)
+              *reinterpret_cast<u32x4 *>(st + SM * 128 + i * 1024 + l * 16) = u32x4{0, 0, 0, 0};
+        }
       }
       lgkm_barrier();
-      if (kt + kSStages - 1 < KT) issue((kt + kSStages - 1) % kSStages, (kt + kSStages - 1) * BK);
-      const unsigned char *st = smem + (kt % kSStages) * STAGE;
+      // the buffer read in step kt - 1 is free: its owner loads stage
+      // kt + kSStages - 1 into it
+      const int nxt = kt + kSStages - 1;
+      if (nxt < KT && wid == nxt % kSStages) issue(wid, nxt * BK);
+      if (mfma_wave) {
+        const unsigned char *st = smem + (kt % kSStages) * STAGE;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const mfma_bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off + chunk_off[kk]));
-        const mfma_bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off + chunk_off[kk]));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const mfma_bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + a_row_off + chunk_off[kk]));
+          const mfma_bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + b_row_off + chunk_off[kk]));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+        }
       }
     }
-    const int k = rt * SN + wn * 32 + (l & 31);
-    const bool kok = k < r_max && k % rs < r;
+    if (mfma_wave) {
+      const int k = rt * SN + wn * 32 + (l & 31);
+      const bool kok = k < r_max && k % rs < r;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int p = p0 + wm * 32 + acc_row(v, l);
-      if (p < p1 && kok) H[(int64_t)token_indices[p] * r_max + k] = acc[v];
+      for (int v = 0; v < 16; ++v) {
+        const int p = p0 + wm * 32 + acc_row(v, l);
+        if (p < p1 && kok) H[(int64_t)token_indices[p] * r_max + k] = acc[v];
+      }
     }
     lgkm_barrier();  // the next item's loads reuse the stages
   }
@@ -276,14 +297,9 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
     const int yrow = rows[0] * (myq == 0) + rows[1] * (myq == 1) + rows[2] * (myq == 2) +
                      rows[3] * (myq == 3);
     // inactive columns read column 0 of the row (in bounds) and never store.
-    // Issued by hand so it leaves with the H loads rather than next to the
-    // store (the compiler otherwise places it after the arithmetic); it is
-    // waited for explicitly before use.
-    u32x4 y4;
-    asm volatile("global_load_dwordx4 %0, %1, off"
-                 : "=v"(y4)
-                 : "v"(Y + (int64_t)yrow * ldy + (active ? col : 0))
-                 : "memory");
+    // An ordinary load, kept with the H loads (ahead of the arithmetic) by the
+    // scheduling barrier below; the compiler waits for it before its use.
+    const uint4 y4 = ldg16(Y + (int64_t)yrow * ldy + (active ? col : 0));
     float4 hv[kExpSub][NB];
 #pragma unroll
     for (int q = 0; q < kExpSub; ++q)
@@ -342,9 +358,8 @@ __device__ __forceinline__ void expand_item(const float *__restrict__ H, const T
       }
     // the sum is formed in every lane (so the Y load above is not sunk into
     // the guarded store) and stored by the lanes that own a row
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(y4) : : "memory");
     float yv[V];
-    Elem<T>::unpack(make_uint4(y4.x, y4.y, y4.z, y4.w), yv);
+    Elem<T>::unpack(y4, yv);
     float out[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -443,7 +458,7 @@ void launch_shrink_mfma(const void *X, int64_t ldx, const SegView &seg, const Po
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
   const int nrt = (pool.r_max + SN - 1) / SN;        // rank tiles of SN pool rank rows
   dim3 grid(nrt, grid_items(nb + S_bound, nrt));
-  hipLaunchKernelGGL((shrink_mfma_kernel<SM, SN>), grid, dim3((SM / 32) * (SN / 32) * kWave), 0,
+  hipLaunchKernelGGL((shrink_mfma_kernel<SM, SN>), grid, dim3(kSStages * kWave), 0,
                      stream, (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                      seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
                      pool.r_max, pool.proj.rs, pool.d_in, pool.policy, nb, S_bound, H);

@@ -332,3 +332,13 @@ def test_static_call_validation(L):
     assert f(rs, X, 64, W, 64, pp, 10, Y + 8, 32, None) == EALIGN    # Y not 16-byte aligned
     assert f(rs, X, 64, W, 64, pp, 0, Y, 32, None) == OK             # empty batch: no-op
 
+
+def test_leading_dimension_limit(L):
+    """Leading dimensions above LORA_MAX_LD (2^22 elements) are rejected on
+    the host: the GEMM addresses a tile's rows with 32-bit byte offsets."""
+    big = (1 << 22) + 8
+    assert L.lora_base_gemm(P, big, P, 64, P, 32, 10, 64, 32, 1, None) == ESHAPE
+    assert L.lora_base_gemm(P, 64, P, big, P, 32, 10, 64, 32, 1, None) == ESHAPE
+    assert L.lora_base_gemm(P, 64, P, 64, P, big, 10, 64, 32, 1, None) == ESHAPE
+    assert L.lora_base_gemm_fp8w(P, 64, P, big, P, P, 32, 10, 64, 32, None) == ESHAPE
+
