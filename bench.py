@@ -44,6 +44,8 @@ WORKLOAD_NAMES = {
     2: "decode bf16: d_in=d_out=4096, 256 rows (1 token/request), 128 slots r=16, 10% base-only",
     3: "prefill bf16: d_in=4096 -> d_out=14336, 8 requests 512..4096 tokens, ranks 8..64, 1 base-only",
     4: "skewed decode bf16: d=4096, 1024 rows, 1000 slots r in {8,16,32,64}, Zipf(1.0) ids",
+    5: "70B-shaped layer bf16: q/k/v/o/gate/up/down, 2304 rows (2048 prefill + 256 decode), "
+       "64 slots r in {16, 64}",
 }
 
 
@@ -122,6 +124,23 @@ def work_figures(w):
     return f
 
 
+def workload_stats(w, seed):
+    """The batch's structure as the bench ran it: seed, segments (one per
+    distinct slot key, base-only included), their length histogram and the
+    ranks of the adapters used (counted on the host from the mapping)."""
+    keys, counts = np.unique(np.asarray(w.row_slot), return_counts=True)
+    bins = [(1, 1), (2, 3), (4, 7), (8, 15), (16, 63), (64, 255), (256, 1023), (1024, 1 << 30)]
+    hist = {(f"{a}" if a == b else (f"{a}-{b}" if b < (1 << 30) else f"{a}+")):
+            int(np.sum((counts >= a) & (counts <= b))) for a, b in bins}
+    used = [int(k) for k in keys if 0 <= k < w.n_slots]
+    ranks = np.asarray([int(w.slot_rank[k]) for k in used], dtype=np.int64)
+    return {"seed": f"numpy SeedSequence({seed})", "rows": int(w.n), "segments": int(len(keys)),
+            "base_only_rows": int(np.sum(np.asarray(w.row_slot) < 0)),
+            "segment_length_hist": {k: v for k, v in hist.items() if v},
+            "longest_segment": int(counts.max()) if counts.size else 0,
+            "adapter_rank_hist": {str(r): int(np.sum(ranks == r)) for r in sorted(set(ranks.tolist()))}}
+
+
 # ---------------------------------------------------------------------------
 # device state
 # ---------------------------------------------------------------------------
@@ -179,6 +198,13 @@ class Layer:
         c.seg = srg.Segments(self.seg.n_rows, p.n_slots, device)
         c.H, c.Y = torch.zeros_like(self.H), torch.empty_like(self.Y)
         return c
+
+
+def Layer_bytes_estimate(w):
+    """Bytes of one copy of a layer's tensors (X, W, A, Bt, Y, H)."""
+    e = 2 if w.dtype == "bf16" else 4
+    return (w.n * w.d_in + w.d_out * w.d_in + w.n_slots * w.r_max * (w.d_in + w.d_out)
+            + w.n * w.d_out) * e + w.n * w.r_max * 4
 
 
 def k_build(L):
@@ -388,6 +414,11 @@ def roofline_for(kernel, fig, sec, dtype):
             "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}
 
 
+def log(*a):
+    """Progress of the run on stderr (the JSON line alone goes to stdout)."""
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
@@ -467,36 +498,105 @@ def cpu_baseline(w, budget_s=12.0, single_core_s=6.0):
     return out
 
 
-def cpu_baseline_sampled(w, k=128, budget_s=6.0):
-    """The oracle on a large batch, timed on a seeded sample of k rows (the
-    rows are independent) and extrapolated linearly to the whole batch; the
-    metadata build is timed on the whole batch, once per pass."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    rows = np.sort(np.random.default_rng(0).choice(w.n, size=min(k, w.n), replace=False))
-    runs, t_meta, t_rows, t0 = 0, 0.0, 0.0, time.perf_counter()
-    while True:
+        return len(os.sched_getaffinity(0))
+
+
+def _oracle_layer_time(ws, rows, budget_s, min_runs=1, warmup=True):
+    """Seconds per pass of the oracle over `rows` of every projection in ws
+    (metadata built once per pass on the whole batch), median of the passes
+    run within about budget_s (after one warm-up pass unless warmup=False)."""
+    import oracle
+    w0 = ws[0]
+
+    def one():
+        oracle.segment_metadata(w0.row_slot, w0.slot_rank, w0.slot_alpha, w0.r_max)
+        for w in ws:
+            oracle.lora_forward(w.X, w.W, w.A, w.B, w.row_slot, w.slot_rank, w.slot_alpha,
+                                w.r_max, w.dtype, rows=rows)
+    if warmup:
+        one()
+    times, t0 = [], time.perf_counter()
+    while len(times) < min_runs or (time.perf_counter() - t0 < budget_s and len(times) < 7):
         a = time.perf_counter()
-        oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)
-        b = time.perf_counter()
-        oracle.lora_forward(w.X, w.W, w.A, w.B, w.row_slot, w.slot_rank, w.slot_alpha, w.r_max,
-                            w.dtype, rows=rows)
-        c = time.perf_counter()
-        t_meta += b - a
-        t_rows += c - b
-        runs += 1
-        if c - t0 >= budget_s:
-            break
-    per_batch = (t_meta + t_rows * w.n / len(rows)) / runs
-    return {"value": round(w.n / per_batch, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{runs} passes of {len(rows)} seeded rows of the {w.n}-row batch in "
-                      f"{t_rows:.1f} s, extrapolated linearly; metadata on the whole batch "
-                      f"({t_meta:.1f} s)"}
+        one()
+        times.append(time.perf_counter() - a)
+    return float(np.median(times)), len(times)
+
+
+def cpu_baselines(budget_s=3.0):
+    """The float64 oracle on configurations 1, 3, 4 and 5, on all BLAS
+    threads and on one thread, median of the passes after a warm-up.
+    Configurations 1 and 4 run whole; 3 and 5 run a seeded sample of rows and
+    are extrapolated linearly to the batch, since rows are independent: 512
+    rows on all threads (the first and last row of every segment and every
+    decode row of 5 included), 128 (3) or 32 (5) random rows on one thread
+    (no warm-up pass: one pass of 5 takes seconds).  A pass has a part that does not
+    depend on the rows asked for (the metadata of the whole batch, decoding
+    the whole X and W), timed by a pass over no rows: the batch time is
+    t0 + (t_sample - t0) n / sample."""
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    threads = int(_blas_threads())
+
+    def sample(w, k, extra=(), ends=True):
+        rows = set(int(x) for x in extra)
+        if ends:
+            _, first = np.unique(w.row_slot, return_index=True)
+            last = w.n - 1 - np.unique(w.row_slot[::-1], return_index=True)[1]
+            rows |= set(first.tolist()) | set(last.tolist())
+        rng = np.random.default_rng(0)
+        while len(rows) < min(k, w.n):
+            rows.add(int(rng.integers(0, w.n)))
+        return np.array(sorted(rows)[:max(k, len(rows))])
+
+    out = {}
+    for cfg in (1, 4, 3, 5):
+        if cfg == 5:
+            ws = [wl.cfg5_projection(p[0]) for p in wl.CFG5_PROJECTIONS]
+        else:
+            ws = [wl.make_config(cfg)]
+        n = ws[0].n
+        entry = {"workload": WORKLOAD_NAMES.get(cfg, "70B-shaped layer, seven projections"),
+                 "seed": f"numpy SeedSequence({cfg})", "rows": n}
+        for label, k, lim in (("all_cores", 512, None), ("single_core", 128 if cfg == 3 else 32, 1)):
+            if lim == 1 and threadpool_limits is None:
+                continue
+            if cfg in (3, 5):
+                extra = range(2048, 2304) if (cfg == 5 and lim is None) else ()
+                rows = sample(ws[0], k, extra, ends=lim is None)
+            else:
+                rows = None
+            ctx = threadpool_limits(limits=lim) if lim else None
+            if ctx:
+                ctx.__enter__()
+            try:
+                warm = not (lim == 1 and rows is not None)
+                t, runs = _oracle_layer_time(ws, rows, budget_s, warmup=warm)
+                t0 = (_oracle_layer_time(ws, np.zeros(0, dtype=np.int64), 0.0, warmup=False)[0]
+                      if rows is not None else 0.0)
+            finally:
+                if ctx:
+                    ctx.__exit__(None, None, None)
+            done = n if rows is None else len(rows)
+            per_batch = t0 + max(t - t0, 0.0) * (n / done) if rows is not None else t
+            entry[label] = {"value": round(n / per_batch, 2), "unit": "tokens/s",
+                            "cores": threads if lim is None else 1, "kind": "oracle",
+                            "extrapolated": rows is not None,
+                            "sample": (f"median of {runs} passes over all {n} rows" if rows is None
+                                       else f"median of {runs} passes over {done} seeded rows of "
+                                            f"{n} ({t:.2f} s; {t0:.2f} s of it independent of "
+                                            f"the rows), extrapolated linearly")}
+        out[str(cfg)] = entry
+        del ws
+    return out
 
 
 def dora_entry(w, fig, m, paths, args):
@@ -593,10 +693,13 @@ def layer_entry(args, device="cuda:0"):
     flops = sum(2 * n * w.d_in * w.d_out for w in ws.values())
     out = {"workload": "70B-shaped layer: q/k/v/o/gate/up/down, 2304 rows (2048 prefill + 256 "
                        "decode), 64 slots r in {16, 64}",
+           "batch": workload_stats(w0, 5),
            "separate": {"tokens_s": round(n / t_sep, 1), "ms": round(t_sep * 1e3, 4),
-                        "TFLOP_s": round(flops / t_sep / 1e12, 1), "calls": 1 + 2 * len(sep)},
+                        "TFLOP_s": round(flops / t_sep / 1e12, 1), "calls": 1 + 2 * len(sep),
+                        "mfma_frac": round(flops / t_sep / 1e12 / MFMA_BF16_TFLOPS, 4)},
            "stacked": {"tokens_s": round(n / t_stk, 1), "ms": round(t_stk * 1e3, 4),
-                       "TFLOP_s": round(flops / t_stk / 1e12, 1), "calls": 1 + 2 * len(stk)},
+                       "TFLOP_s": round(flops / t_stk / 1e12, 1), "calls": 1 + 2 * len(stk),
+                       "mfma_frac": round(flops / t_stk / 1e12 / MFMA_BF16_TFLOPS, 4)},
            "stacked_speedup": round(t_sep / t_stk, 4)}
     del dev, sep, stk
     torch.cuda.empty_cache()
@@ -613,15 +716,24 @@ def skewed_entry(args):
     f4 = work_figures(w4)
     st = max(10, args.steps // 4)
     out = {"workload": WORKLOAD_NAMES[4], "rows": w4.n,
-           "distinct_adapters": f4["distinct_adapters"], "policies": {}}
+           "distinct_adapters": f4["distinct_adapters"], "batch": workload_stats(w4, 4),
+           "alg_bytes": {"shrink": int(f4["bytes"]["shrink"]), "expand": int(f4["bytes"]["expand"]),
+                         "fused": int(f4["bytes"]["fused"])},
+           "policies": {}}
     for pol in ("exact", "two_buckets", "padded"):
         m4 = measure(w4, ["fused", "separate"], pol, st, max(3, args.warmup // 4), args.rotate_mb,
                      st, not args.eager, kernels=(k_build_shrink, k_shrink, k_fused, k_expand))
         best = min(m4["step"], key=lambda p: m4["step"][p][0])
+        pk = m4["per_kernel_s"]
+        se = f4["bytes"]["shrink"] + f4["bytes"]["expand"]
         out["policies"][pol] = {
             "path": best, "tokens_s": round(w4.n / m4["step"][best][0], 1),
             "step_us_by_path": {p: round(v[0] * 1e6, 3) for p, v in m4["step"].items()},
-            "us": {k: round(v * 1e6, 3) for k, v in m4["per_kernel_s"].items()}}
+            "us": {k: round(v * 1e6, 3) for k, v in pk.items()},
+            "fused_gemm": roofline_for("fused", f4, pk["fused"], "bf16"),
+            "shrink_expand": {"GB_s": round(se / (pk["shrink"] + pk["expand"]) / 1e9, 1),
+                              "hbm_frac": round(se / (pk["shrink"] + pk["expand"]) / 1e9 /
+                                                HBM_PEAK_GBS, 4)}}
     ex, pad = out["policies"]["exact"], out["policies"]["padded"]
     out["padded_over_exact_step"] = round(ex["tokens_s"] / pad["tokens_s"], 4)
     return out
@@ -655,6 +767,7 @@ def main():
     w = wl.make_config(args.config)
     fig = work_figures(w)
     paths = list(PATHS) if args.path == "auto" else [args.path]
+    log(f"configuration {args.config}: steps and kernels")
     m = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
                 args.kernel_loops, not args.eager, vendor=not args.no_vendor and w.dtype == "bf16")
     path = min(paths, key=lambda p: m["step"][p][0])
@@ -686,6 +799,7 @@ def main():
                    "rotated_copies": m["copies"], "launch": "eager" if args.eager else "hip_graph",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "batch": workload_stats(w, args.config),
         "shrink_expand": {"GB_s": round(se_bytes / (sh + ex) / 1e9, 1),
                           "hbm_frac": round(se_bytes / (sh + ex) / 1e9 / HBM_PEAK_GBS, 4),
                           "us": round((sh + ex) * 1e6, 3)},
@@ -696,28 +810,37 @@ def main():
     if vendor_entry(fig, m):
         out["vendor_base_gemm"] = vendor_entry(fig, m)
     if not args.no_prefill and args.config != 3:
+        log("prefill (configuration 3)")
         w3 = wl.make_config(3)
         f3 = work_figures(w3)
         st3 = max(5, args.steps // 10)
-        m3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
+        # two rotated copies (each ~0.75 GB): no call reads what the previous
+        # one left in the 256 MB last-level cache
+        rot3 = 2.0 * Layer_bytes_estimate(w3) / 1e6
+        m3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), rot3, st3,
                      not args.eager, vendor=not args.no_vendor)
         k3 = kernel_table(f3, m3["per_kernel_s"], "bf16")
         out["prefill"] = {
-            "workload": WORKLOAD_NAMES[3], "rows": w3.n,
+            "workload": WORKLOAD_NAMES[3], "rows": w3.n, "rotated_copies": m3["copies"],
+            "batch": workload_stats(w3, 3),
             "tokens_s": round(w3.n / m3["step"]["fused"][0], 1),
             "ms_per_step": round(m3["step"]["fused"][0] * 1e3, 4), "path": "fused",
             "fused_gemm": dict(roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
                                traffic=measured_traffic(3, "fused")),
-            "shrink_expand": {"GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
-                                            (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1)},
+            "shrink_expand": {
+                "GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
+                              (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1),
+                "hbm_frac": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
+                                  (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) /
+                                  1e9 / HBM_PEAK_GBS, 4),
+                "us": round((m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) * 1e6, 3)},
             "kernels": k3,
         }
         if vendor_entry(f3, m3):
             out["prefill"]["vendor_base_gemm"] = vendor_entry(f3, m3)
-        if not args.no_cpu_baseline:
-            out["prefill"]["cpu_baseline"] = cpu_baseline_sampled(w3)
         del w3
     if not args.no_dora:
+        log("DoRA variant")
         out["dora"] = dora_entry(w, fig, m, paths, args)
         if "prefill" in out:
             w3 = wl.make_config(3)
@@ -731,6 +854,7 @@ def main():
                 "step_us": round(md3["step"]["fused"][0] * 1e6, 3)}
             del w3
     if not args.no_fp8w and w.dtype == "bf16":
+        log("FP8-weight variant")
         out["fp8_weight"] = fp8w_entry(w, fig, m, args)
         if "prefill" in out:
             w3 = wl.make_config(3)
@@ -744,11 +868,18 @@ def main():
                 "fused_us": round(mq3["per_kernel_s"]["fused_fp8w"] * 1e6, 3)}
             del w3
     if not args.no_skewed and args.config == 2:
+        log("skewed decode (configuration 4), three rank policies")
         out["skewed_decode"] = skewed_entry(args)
     if not args.no_layer and args.config == 2:
+        log("70B-shaped layer (configuration 5)")
         out["layer_70b"] = layer_entry(args)
     if not args.no_cpu_baseline:
+        log("CPU oracle baseline, headline workload")
         out["cpu_baseline"] = cpu_baseline(w)
+        log("CPU oracle baselines, configurations 1, 4, 3, 5")
+        out["cpu_baselines"] = cpu_baselines()
+        if "prefill" in out:
+            out["prefill"]["cpu_baseline"] = out["cpu_baselines"]["3"]["all_cores"]
     print(json.dumps(out), flush=True)
 
 

@@ -154,13 +154,16 @@ __device__ __forceinline__ SegMeta load_seg_meta(int s, const int32_t *num_segme
 
 // Work items of the segmented kernels: the positions of the segment order
 // (token_indices) in blocks of at most rb, cut at segment boundaries.  Item
-// y < nb is the block of positions [y rb, y rb + rb) inside the segment that
-// holds position y rb, unless that segment starts there; item nb + s is the
-// first block of segment s, from its start to the next multiple of rb (or
-// its end).  Every position lies in exactly one item, so a batch needs at
-// most nb + S items whatever the segment lengths, and no item has more than
-// rb rows.  ok is false for an item without rows (a block where a segment
-// starts, or s >= S).  Items y >= nb need y - nb < cap (the segment arrays'
+// nb + s is segment s's head: the whole segment if it has at most rb rows,
+// else from its start to the next multiple of rb.  Item y < nb is the block
+// of positions [y rb, y rb + rb) inside the segment that holds position
+// y rb, when that segment is longer than rb rows and does not start there.
+// Every position lies in exactly one item, so a batch needs at most nb + S
+// items whatever the segment lengths, and no item has more than rb rows.
+// A short segment (a decode batch's usual case) is one head item: the
+// position items, whose segment is found through two more dependent loads,
+// then carry no rows and load nothing more.  ok is false for an item without
+// rows (including s >= S).  Items y >= nb need y - nb < cap (the segment arrays'
 // capacity); metadata from the build keeps every segment id below it.
 struct SegItem {
   bool ok;
@@ -187,13 +190,14 @@ __device__ __forceinline__ SegItem seg_item(int y, int nb, int rb, int cap,
   it.sc = m.sc;
   it.o0 = m.o0;
   it.o1 = m.o1;
+  const bool whole = m.o1 - m.o0 <= rb;   // short segment: one head item
   if (y < nb) {
     it.p0 = p0;
     it.p1 = min(p0 + rb, m.o1);
-    it.ok = s < m.S && m.o0 != p0 && p0 < it.p1;
+    it.ok = s < m.S && !whole && m.o0 != p0 && p0 < it.p1;
   } else {
     it.p0 = m.o0;
-    it.p1 = min(m.o1, (m.o0 / rb + 1) * rb);
+    it.p1 = whole ? m.o1 : min(m.o1, (m.o0 / rb + 1) * rb);
     it.ok = s < m.S && it.p0 < it.p1;
   }
   return it;
