@@ -86,6 +86,20 @@ struct GemmArgs {
 #ifndef LORA_GEMM_LARGE_F8
 #define LORA_GEMM_LARGE_F8 LORA_GEMM_LARGE
 #endif
+// 192-row large tiles (8 waves of 96 x 64), for batches whose 256 x 256 grid
+// ends in a nearly empty round on the 256 CUs (2304 rows x 8192 columns:
+// 288 tiles of 256 x 256 fill 1.125 rounds, 384 of 192 x 256 fill 1.5).
+#ifndef LORA_GEMM_LARGE192
+#define LORA_GEMM_LARGE192 192, 256, 2, 4, 64, 2, 1
+#endif
+#ifndef LORA_GEMM_LARGE192_F8
+#define LORA_GEMM_LARGE192_F8 LORA_GEMM_LARGE192
+#endif
+// Relative cost per output element of a 192 x 256 tile against a 256 x 256
+// one (more LDS fragment reads per flop), in percent.
+#ifndef LORA_GEMM_192_COST
+#define LORA_GEMM_192_COST 110
+#endif
 // Large and mid tiles with more LoRA runs than this (consecutive rows of one
 // segment; decode rows make one each) finish row by row on the VALU instead
 // of one staged MFMA increment per segment.
@@ -930,7 +944,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           for (int v = 0; v < 16; ++v) wbuf[acc_row(v, l) * WRS + j * 32 + (l & 31)] = acc[i][j][v];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the wave's lanes
         // two items at a time on tiles of at most four fragments per wave; on
-        // 256x256 tiles the second item's registers would spill
+        // 192x256 and 256x256 tiles the second item's registers would spill
         const bool PAIR = C::FM * C::FN <= 4;
         const int NU = PAIR ? 2 : 1;
         for (int it0 = l; it0 < WITEMS; it0 += NU * kWave) {
@@ -1336,9 +1350,17 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
       g.policy = pool->policy;
     }
     const bool mid = ((int64_t)(M + 255) / 256) * ((N + 255) / 256) <= LORA_GEMM_MID_TILES;
+    // Large tiles: 256 x 256, or 192 x 256 when its rounds of kCUs tiles cost
+    // less (rounds times tile area, the narrower tile charged its extra LDS
+    // traffic per flop).
+    const int64_t tn256 = (N + 255) / 256;
+    const int64_t r256 = ((int64_t)(M + 255) / 256 * tn256 + kCUs - 1) / kCUs;
+    const int64_t r192 = ((int64_t)(M + 191) / 192 * tn256 + kCUs - 1) / kCUs;
+    const bool use192 = r192 * 192 * LORA_GEMM_192_COST < r256 * 256 * 100;
     if (wscale) {
       if (M <= LORA_GEMM_SMALL_M) return launch_fp8w<LORA_GEMM_SMALL_F8>(g, lora, stream);
       if (mid) return launch_fp8w<LORA_GEMM_MID_F8>(g, lora, stream);
+      if (use192) return launch_fp8w<LORA_GEMM_LARGE192_F8>(g, lora, stream);
       return launch_fp8w<LORA_GEMM_LARGE_F8>(g, lora, stream);
     }
     if (M <= LORA_GEMM_SMALL_M) {
@@ -1348,6 +1370,7 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
       return launch_bf16<LORA_GEMM_SMALL>(g, lora, stream);
     }
     if (mid) return launch_bf16<LORA_GEMM_MID>(g, lora, stream);
+    if (use192) return launch_bf16<LORA_GEMM_LARGE192>(g, lora, stream);
     return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
   }
   GemmF32Args g{(const float *)X, ldx, (const float *)W, ldw, (float *)Y, ldy, M, K, N,

@@ -65,7 +65,8 @@ CASES = [
     (504, 512, 256, 384, 6, 32, 0.2, True),
     (505, 700, 208, 136, 7, 64, 0.1, True),      # large tiles, K tail (208 % 64), ragged N
     (506, 2100, 336, 264, 5, 32, 0.2, True),
-    (507, 1100, 208, 8200, 7, 64, 0.1, True),    # 256 x 256 tiles with a K tail
+    (507, 1100, 208, 8200, 7, 64, 0.1, True),    # 192 x 256 tiles with a K tail
+    (508, 2040, 208, 7944, 7, 64, 0.1, True),    # 256 x 256 tiles with a K tail
 ]
 
 

@@ -1,5 +1,5 @@
-"""GPU parity of the row-by-row LoRA epilogue of the 128 x 128 and 256 x 256
-tiles of the fused layer (adapter-batching page, Multi-LoRA Serving, section
+"""GPU parity of the row-by-row LoRA epilogue of the 128 x 128, 192 x 256 and
+256 x 256 tiles of the fused layer (adapter-batching page, Multi-LoRA Serving, section
 "一个混合 Batch 的数学形式": every row gets its own adapter's term).  Such a
 tile switches from one staged MFMA increment per segment to the row
 epilogue when its rows hold more than a few LoRA runs (decode rows, each of
@@ -58,8 +58,9 @@ def _runs_per_tile(tile_rows, n_tiles, n_slots, rng, base_run=True):
 MANY = [
     # seed, n, d_in, d_out, n_slots, p_base: random rows (one run per row or so)
     (701, 1024, 256, 1032, 50, 0.1),     # 128 x 128 tiles, ragged N
-    (702, 1100, 200, 8200, 40, 0.1),     # 256 x 256 tiles, K tail, ragged M and N
-    (703, 600, 136, 11008, 70, 0.3),     # 256 x 256 tiles, ragged M
+    (702, 1100, 200, 8200, 40, 0.1),     # 192 x 256 tiles, K tail, ragged M and N
+    (703, 600, 136, 11008, 70, 0.3),     # 192 x 256 tiles, ragged M
+    (708, 2040, 200, 7944, 40, 0.1),     # 256 x 256 tiles, K tail, ragged M and N
 ]
 
 
@@ -77,16 +78,17 @@ def test_many_runs(case, policy):
 
 
 # ---------------------------------------------------------------- around the switch
-@pytest.mark.parametrize("shape", [(1024, 264), (768, 11008)], ids=["tile128", "tile256"])
+@pytest.mark.parametrize("shape", [(1024, 264, 128), (768, 11008, 192), (1024, 12288, 256)],
+                         ids=["tile128", "tile192", "tile256"])
 def test_run_counts_around_the_switch(shape):
-    """Tiles with 1, 2, ..., 8 runs (128-row tiles) or 1, 2, 3 runs
-    (256-row tiles), so tiles on both sides of the switch."""
-    n, d_out = shape
-    tile = 128 if n == 1024 else 256
+    """Tiles with 1, 2, ..., 8 runs (128-row tiles) or 1, 2, 3, 4 runs (192-
+    and 256-row tiles), then more runs in the last 256 rows, so tiles on both
+    sides of the switch."""
+    n, d_out, tile = shape
     rng = np.random.default_rng(704)
     row_slot = _runs_per_tile(tile, n // tile, 12, rng)
-    if tile == 256:               # more runs in the last 256-row tiles
-        row_slot[512:] = _runs_per_tile(32, 8, 12, rng, base_run=False)
+    if tile > 128:               # more runs in the last 256 rows
+        row_slot[n - 256:] = _runs_per_tile(32, 8, 12, rng, base_run=False)
     ranks = [8, 16, 32, 64, 0, 16, 64, 8, 32, 64, 16, 8]
     w = _mapped(704, row_slot, 96, d_out, ranks)
     say("switch", shape)
