@@ -4,7 +4,11 @@
 One step = one pass of the whole hot path over one batch: segment-metadata
 build and shrink (H = X_a A_a^T; one launch for decode-sized batches,
 lora_build_shrink), and the base GEMM with the LoRA expand fused into its
-epilogue (``--path separate``: base GEMM, then expand + scatter-add).  Inputs are resident in HBM before timing starts.  Each step
+epilogue (``--path separate``: base GEMM, then expand + scatter-add;
+``--path layer``: all of it in one call, lora_layer_fused, which is one
+launch for batches of up to 512 rows).  By default every path is timed and
+the fastest is the headline.  Inputs are resident in HBM before timing
+starts.  Each step
 uses the next of several copies of the layer's tensors (like consecutive
 layers of a model), so that the 256 MB last-level cache cannot serve weights
 read in the previous step.
@@ -55,9 +59,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
-    p.add_argument("--path", choices=["auto", "fused", "separate", "overlap"], default="auto",
+    p.add_argument("--path", choices=["auto", "fused", "separate", "overlap", "layer"],
+                   default="auto",
                    help="auto: time every step variant and report the fastest; overlap = "
-                        "separate with the base GEMM on a second stream beside build+shrink")
+                        "separate with the base GEMM on a second stream beside build+shrink; "
+                        "layer = the whole layer in one call (one launch up to 512 rows)")
     p.add_argument("--policy", choices=["exact", "two_buckets", "padded"], default="exact")
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="total size of the rotated copies of the layer tensors")
@@ -106,6 +112,10 @@ def work_figures(w):
             "expand": sum_r_distinct * do * e + sum_r_rows * 4 + 2 * n_lora * do * e,
             "base": do * di * e + n * di * e + n * do * e,
             "fused": do * di * e + n * di * e + n * do * e + sum_r_distinct * do * e + sum_r_rows * 4,
+            # the whole layer in one launch: the fused product's bytes plus
+            # the metadata, the distinct A rows and H written once
+            "layer": (n * 4 + 2 * n * 4 + 2 * w.n_slots * 4) + do * di * e + n * di * e
+                     + n * do * e + sum_r_distinct * (di + do) * e + 2 * sum_r_rows * 4,
             # FP8 base weight: one byte per weight plus a float32 scale per row
             "base_fp8w": do * di + do * 4 + n * di * e + n * do * e,
             "fused_fp8w": do * di + do * 4 + n * di * e + n * do * e + sum_r_distinct * do * e
@@ -117,6 +127,7 @@ def work_figures(w):
             "expand": 2 * sum_r_rows * do,
             "base": 2 * n * di * do,
             "fused": 2 * n * di * do + 2 * sum_r_rows * do,
+            "layer": 2 * n * di * do + 2 * sum_r_rows * (di + do),
             "base_fp8w": 2 * n * di * do,
             "fused_fp8w": 2 * n * di * do + 2 * sum_r_rows * do,
         },
@@ -175,6 +186,7 @@ class Layer:
             self.Wq = torch.from_numpy(codes).to(device)
             self.ws = torch.from_numpy(scale).to(device)
         self.seg = srg.Segments(w.n, w.n_slots, device)
+        self.sync = srg.layer_sync(device)
         dt = self.X.dtype
         self.H = torch.zeros((w.n, w.r_max), dtype=torch.float32, device=device)
         self.Y = torch.empty((w.n, w.d_out), dtype=dt, device=device)
@@ -196,6 +208,7 @@ class Layer:
         if p.dora_scale is not None:
             c.pool.dora_scale.copy_(p.dora_scale)
         c.seg = srg.Segments(self.seg.n_rows, p.n_slots, device)
+        c.sync = srg.layer_sync(device)
         c.H, c.Y = torch.zeros_like(self.H), torch.empty_like(self.Y)
         return c
 
@@ -225,6 +238,11 @@ def k_build_shrink(L):
 def k_fused(L):
     import segmented_rank_gemm_segment_amd as srg
     srg.lora_linear_fused(L.X, L.W, L.H, L.seg, L.pool, L.Y)
+
+
+def k_layer(L):
+    import segmented_rank_gemm_segment_amd as srg
+    srg.lora_layer_fused(L.row_slot, L.X, L.W, L.pool, L.seg, L.H, L.Y, L.sync)
 
 
 def k_base(L):
@@ -280,10 +298,11 @@ class _Overlap:
 
 
 STEP = {"fused": (k_build_shrink, k_fused), "separate": (k_build_shrink, k_base, k_expand),
-        "fused_fp8w": (k_build_shrink, k_fused_fp8w)}
-PATHS = ("fused", "separate", "overlap")
+        "fused_fp8w": (k_build_shrink, k_fused_fp8w), "layer": (k_layer,)}
+PATHS = ("fused", "separate", "overlap", "layer")
 KNAME = {k_build: "build", k_shrink: "shrink", k_build_shrink: "build_shrink", k_fused: "fused",
-         k_base: "base", k_expand: "expand", k_fused_fp8w: "fused_fp8w", k_base_fp8w: "base_fp8w"}
+         k_base: "base", k_expand: "expand", k_fused_fp8w: "fused_fp8w", k_base_fp8w: "base_fp8w",
+         k_layer: "layer"}
 
 
 def _graph(fn_seq, layers, count, start=0):
@@ -352,6 +371,8 @@ def measure(w, paths, policy, steps, warmup, rotate_mb, kernel_loops, use_graph,
     per_kernel = {}
     if kernels is None:
         kernels = STEP["fused"] + STEP["separate"] + (k_build, k_shrink)
+        if "layer" in paths:
+            kernels += STEP["layer"]
     for fn in sorted(set(kernels), key=lambda f: KNAME[f]):
         per_kernel[KNAME[fn]], _ = time_calls((fn,), layers, kl, max(3, warmup // 4), use_graph)
     res = {"step": step, "per_kernel_s": per_kernel, "copies": copies, "layer_bytes": L0.nbytes}
@@ -773,7 +794,8 @@ def main():
     path = min(paths, key=lambda p: m["step"][p][0])
     step_s, wall = m["step"][path]
     kt = kernel_table(fig, m["per_kernel_s"], w.dtype)
-    cand = ("build_shrink", "fused") if path == "fused" else ("build_shrink", "base", "expand")
+    cand = {"fused": ("build_shrink", "fused"), "layer": ("layer",)}.get(
+        path, ("build_shrink", "base", "expand"))
     # (overlap: same kernels as separate, base GEMM concurrent with build + shrink)
     main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)

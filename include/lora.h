@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 6
+#define LORA_ABI_VERSION 7
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 /* Limits of the allocation-free call lora_linear_fused_static: token rows,
@@ -51,6 +51,11 @@ extern "C" {
 /* Largest leading dimension of X, W, Y (elements): the GEMM addresses a tile's
  * rows with 32-bit byte offsets from its first row. */
 #define LORA_MAX_LD (1 << 22)
+
+/* lora_layer_fused: batches of up to this many rows (bf16 pools) run in one
+ * launch; its sync buffer has this many bytes. */
+#define LORA_LAYER_ONE_LAUNCH_ROWS 512
+#define LORA_LAYER_SYNC_BYTES 4096
 
 typedef enum {
   LORA_OK = 0,
@@ -371,6 +376,35 @@ lora_status lora_linear_fused_fp8w(const void *X, int64_t ldx, const void *Wq, i
                                    const float *w_scale, const float *H,
                                    const lora_segments *seg, const lora_pool *pool, void *Y,
                                    int64_t ldy, void *stream);
+
+/*
+ * The whole layer in one call: lora_build_segments, lora_shrink and
+ * lora_linear_fused together (adapter-batching page, sections "一个混合
+ * Batch 的数学形式" and "Segmented Kernel 需要哪些 Metadata"; its section
+ * "Prefill 与 Decode 的 LoRA 形状不同" places decode's cost in launches,
+ * gathers and metadata).  Arguments and layouts as in those three calls:
+ * row_slot device int32 [seg->n_rows] (-1 = base-only), X [n][d_in],
+ * W [d_out][d_in], Y [n][d_out] of the pool's dtype, H fp32 [n][r_max] and
+ * the segment arrays are written.  Outputs: the segment metadata bit for bit
+ * as lora_build_segments writes it, H[i][0:r] for the rows of a LoRA
+ * segment (equal to lora_shrink's up to the order of the fp32 additions),
+ * and Y = X W^T + s_a H[i][0:r] B_a^T with one rounding (rows of base-only
+ * and rank-0 segments equal lora_base_gemm's output bit for bit).
+ * For bf16 pools and 1 <= n <= LORA_LAYER_ONE_LAUNCH_ROWS this is one
+ * kernel launch: every workgroup builds the metadata itself, computes H for
+ * one row and hands it to the tiles that need it through `sync`; otherwise
+ * it is lora_build_shrink followed by lora_linear_fused.
+ * sync: NULL, or a device buffer of LORA_LAYER_SYNC_BYTES bytes, 16-byte
+ * aligned, owned by the caller, zero-filled once before its first use and
+ * then left to the library (it keeps a call counter there and leaves it
+ * ready for the next call).  Calls that share a sync buffer must be ordered
+ * on one stream (they race otherwise); with sync NULL every output tile
+ * computes the H rows it needs itself (same results, more work).
+ * Errors as the three calls; n_rows == 0 writes the empty metadata only.
+ */
+lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
+                             int64_t ldw, const lora_pool *pool, const lora_segments *seg,
+                             float *H, void *Y, int64_t ldy, void *sync, void *stream);
 
 /*
  * The whole layer with no workspace arguments, for callers that cannot

@@ -30,9 +30,11 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 6
+ABI_VERSION = 7
 STATIC_MAX_ROWS = 32768
 STATIC_MAX_H = 1 << 21
+LAYER_ONE_LAUNCH_ROWS = 512
+LAYER_SYNC_BYTES = 4096
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -95,6 +97,7 @@ EXPORTS = (
     "lora_base_gemm_fp8w",
     "lora_linear_fused_fp8w",
     "lora_linear_fused_static",
+    "lora_layer_fused",
 )
 
 
@@ -139,6 +142,8 @@ def lib() -> ctypes.CDLL:
     L.lora_linear_fused_fp8w.argtypes = [vp, i64, vp, i64, vp, vp, SP, PP, vp, i64, vp]
     L.lora_linear_fused_static.restype = i32
     L.lora_linear_fused_static.argtypes = [vp, vp, i64, vp, i64, PP, i32, vp, i64, vp]
+    L.lora_layer_fused.restype = i32
+    L.lora_layer_fused.argtypes = [vp, vp, i64, vp, i64, PP, SP, vp, vp, i64, vp, vp]
     if L.lora_abi_version() != ABI_VERSION:
         raise RuntimeError("liblora ABI version mismatch")
     _lib = L
@@ -485,6 +490,36 @@ def lora_linear_fused(X: torch.Tensor, W: torch.Tensor, H: torch.Tensor, seg: Se
         raise ValueError("H: contiguous float32 [n_rows, r_max]")
     _check(lib().lora_linear_fused(_ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(H), seg.c, pool.c,
                                    _ptr(Y), _ld(Y), _stream(stream)))
+
+
+def layer_sync(device) -> torch.Tensor:
+    """A zero-filled sync buffer for lora_layer_fused (LAYER_SYNC_BYTES)."""
+    return torch.zeros(LAYER_SYNC_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def lora_layer_fused(row_slot: torch.Tensor, X: torch.Tensor, W: torch.Tensor, pool: Pool,
+                     seg: Segments, H: torch.Tensor, Y: torch.Tensor,
+                     sync: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Segment build, shrink and fused product in one call (one launch for
+    bf16 batches of up to LAYER_ONE_LAUNCH_ROWS rows).  sync: a buffer from
+    layer_sync(), reused across calls ordered on one stream; None makes
+    every tile compute its own rows' H."""
+    if row_slot.dtype != torch.int32 or (row_slot.numel() and not row_slot.is_contiguous()):
+        raise ValueError("row_slot: contiguous int32")
+    if row_slot.numel() != seg.n_rows:
+        raise ValueError("row_slot length != seg.n_rows")
+    if not (X.dtype == W.dtype == Y.dtype == pool.dtype):
+        raise ValueError("X, W, Y must share the pool dtype")
+    if X.shape[0] != seg.n_rows or tuple(W.shape) != (pool.d_out, pool.d_in) \
+            or tuple(Y.shape) != (seg.n_rows, pool.d_out):
+        raise ValueError("shapes: X [n, d_in], W [d_out, d_in], Y [n, d_out]")
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    if sync is not None and (sync.numel() * sync.element_size() < LAYER_SYNC_BYTES
+                             or not sync.is_contiguous()):
+        raise ValueError("sync: a contiguous buffer of LAYER_SYNC_BYTES bytes (layer_sync())")
+    _check(lib().lora_layer_fused(_ptr(row_slot), _ptr(X), _ld(X), _ptr(W), _ld(W), pool.c, seg.c,
+                                  _ptr(H), _ptr(Y), _ld(Y), _ptr(sync), _stream(stream)))
 
 
 def lora_base_gemm_fp8w(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, Y: torch.Tensor,

@@ -21,8 +21,13 @@
 // multiplied by MFMA into the accumulators, zero rows standing in for rows
 // of other segments.  Every row gets exactly its own segment's increment,
 // added in fp32 and rounded once with the base product.
+//
+// The small tiles also run the whole layer in one launch (layer.cuh): the
+// segment metadata and H are produced inside the same kernel, before each
+// tile's K loop, and handed between workgroups through per-row flags.
 #include <climits>
 
+#include "layer.cuh"
 #include "lds_dma.cuh"
 #include "lora_device.cuh"
 #include "lora_kernels.h"
@@ -49,6 +54,7 @@ struct GemmArgs {
   const float *dora;   // optional DoRA column factors ([slot][N]) or null
   const float *wscale; // FP8 weight: one scale per output row (W then holds E4M3 codes)
   ProjView proj;       // projections of the output columns (one unless stacked)
+  LayerArgs lay;       // the one-launch layer's inputs and outputs (layer.cuh)
 };
 
 // Tile configurations <BM, BN, waves along M, waves along N, K per group
@@ -180,7 +186,9 @@ __device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi)
 // projection (offsets of projections are multiples of 8, so all 8 columns
 // share it).  Shared by both row epilogues, so both give the same bits.
 // (Loading two chunks per step measured no faster on 64x64 tiles.)
-template <bool DORA>
+// COH: H was written by other workgroups of the same launch and is read
+// with agent-scope loads (layer.cuh).
+template <bool DORA, bool COH = false>
 __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol, int slot, int r,
                                           float sc, float (&o)[8]) {
   const int N = g.N;
@@ -189,9 +197,16 @@ __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol,
   const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
   float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int kc = 0; kc < r; kc += 8) {      // kc < r <= rs: the chunk is in the block
-    const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
-    const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
-    const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    float h[8];
+    if constexpr (COH) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = ld_agent(hp + kc + q);
+    } else {
+      const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hp + kc);
+      const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hp + kc + 4);
+      h[0] = h0[0]; h[1] = h0[1]; h[2] = h0[2]; h[3] = h0[3];
+      h[4] = h1[0]; h[5] = h1[1]; h[6] = h1[2]; h[7] = h1[3];
+    }
     u32x4 b[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) b[q] = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(kc + q) * N);
@@ -376,11 +391,16 @@ __device__ __forceinline__ int heavier_end_tile(const int32_t *row_segment, int 
 // accumulator before the LoRA term is added.
 // LORA: 0 = plain product; 1 = fused LoRA with B gathered from Bt; 2 = fused
 // LoRA with B read from its d_out-major copy.  DORA: rows of rank > 0 are
-// multiplied by their slot's column factors before the rounding.
+// multiplied by their slot's column factors before the rounding.  LAYER
+// (small tiles): the whole layer in one launch (layer.cuh); the row
+// metadata and H come from the launch itself instead of earlier calls.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, bool DORA,
-          bool WF8>
+          bool WF8, bool LAYER = false>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG, WF8 ? 1 : 2>;
+  static_assert(!LAYER || (KG > 1 && LORA == 1 && !WF8 && WM * WN * KG * kWave == kLayerThreads),
+                "the one-launch layer runs on the small tiles");
+  static_assert(!LAYER || C::LDS >= (4 * 4095 + 2) * 4, "the build's tables fit in the ring");
   // LDS: the stage ring, or the fused LoRA epilogue of large tiles if larger:
   // the staged segment operands (EPI_STG bytes) or one 32-row fp32 slot per
   // wave (row stride TN + 4), then per-row rank, slot and scale and a word
@@ -389,7 +409,10 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   constexpr int EPI_META = ((EPI_ROW > EPI_STG ? EPI_ROW : EPI_STG) + 15) / 16 * 16;
   constexpr int LSTG = (LORA != 0 && KG == 1) ? EPI_META + 12 * BM + 16 : 0;
   constexpr int SMEM = C::LDS > LSTG ? C::LDS : LSTG;
-  __shared__ __align__(16) unsigned char smem[SMEM];
+  // the layer's LDS follows the ring (both live at once before the K loop)
+  constexpr int LAYB = LAYER ? (int)sizeof(LayerLds) : 0;
+  __shared__ __align__(16) unsigned char smem[SMEM + LAYB];
+  LayerLds &Lay = *reinterpret_cast<LayerLds *>(smem + SMEM);
 
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
@@ -417,8 +440,11 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     if (tiles_m > 1 && tiles_m <= kHeavyMaxTilesM && tiles_m * tiles_n > kCUs)
       heavy = heavier_end_tile(g.row_segment, M, BM, tiles_m, reinterpret_cast<int *>(smem));
   }
-  int m_idx, n_idx;
-  if (!tile_order(blockIdx.x, tiles_m, tiles_n, heavy, m_idx, n_idx)) return;
+  int m_idx = 0, n_idx = 0;
+  const bool has_tile = tile_order(blockIdx.x, tiles_m, tiles_n, heavy, m_idx, n_idx);
+  // (a layer workgroup without a tile still has its row of the layer to do)
+  if (!LAYER && !has_tile) return;
+  if (LAYER && !has_tile) m_idx = n_idx = 0;
   const int m0 = m_idx * BM;
   const int n0 = n_idx * BN;
 
@@ -444,7 +470,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     e_ws1 = *reinterpret_cast<const f32x4 *>(ws + 4);
   }
   int e_seg = 0, e_r = 0, e_slot = 0, e_scb = 0;
-  if constexpr (LORA != 0)
+  if constexpr (LORA != 0 && !LAYER)
     if (e_own) e_seg = g.row_segment[min(m0 + e_row, M - 1)];
 
   // DMA sources: lane l of an instruction fills tile row base + l / CH at
@@ -615,17 +641,20 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
   const bool ktail = (K % C::KSTEP) != 0;
   // every buffer of the ring is free at the start: fill all of them (with
   // owners, each wave fills its own buffer)
-  if constexpr (OWNED) {
-    if (wid < KT) {
-      const bool tail = ktail && wid == KT - 1;
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (OWNED) {
+      if (wid < KT) {
+        const bool tail = ktail && wid == KT - 1;
 #pragma unroll
-      for (int t = 0; t < NIG; ++t) issue_own_one(t, wid, wid * C::KSTEP + kg0, tail);
+        for (int t = 0; t < NIG; ++t) issue_own_one(t, wid, wid * C::KSTEP + kg0, tail);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s)
+        if (s < KT) issue(s, s * C::KSTEP + kg0);
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < KT) issue(s, s * C::KSTEP + kg0);
-  }
+  };
+  if constexpr (!LAYER) prologue();
 
   // Software pipeline over K.  Fragments of sub-step kk + 1 are read from
   // LDS while the MFMAs of sub-step kk run.  Before the last sub-step of
@@ -670,10 +699,51 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     }
   };
 
+  if constexpr (LAYER) {
+    // The layer's metadata and this workgroup's row of H.  The build's
+    // tables live beside the ring for pools of up to kLayerTabSlots slots,
+    // and the ring fills meanwhile; for larger pools they use the ring's
+    // LDS and the ring is filled afterwards.  The row's first shrink
+    // operands are requested before the build.
+    const bool early = g.lay.n_slots <= kLayerTabSlots;
+    int *tab = early ? Lay.tab : reinterpret_cast<int *>(smem);
+    if (early && has_tile) prologue();
+    BuildRegs br;
+    layer_build_load(g.lay, M, blockIdx.x, br);
+    RowPrefetch pre;
+    layer_prefetch(g.lay, g.X, g.ldx, min((int)blockIdx.x, M - 1), br.slot_mine, pre);
+    pre.valid = pre.valid && (int)blockIdx.x < M;
+    layer_stage(g.lay, br, tab);
+    // this call's generation number (one thread; first needed to publish the row)
+    uint32_t gen = 0;
+    if (tid == 0 && g.lay.sync) gen = ld_agent(g.lay.sync + kSyncGen);
+    layer_build(g.lay, M, blockIdx.x, br, Lay, tab);   // ends with a barrier
+    if ((int)blockIdx.x < M) {
+      const int row = blockIdx.x;
+      const int r = Lay.rk[row];
+      if (r > 0) {
+        layer_row_shrink(g.lay, g.X, g.ldx, row, Lay.key[row] - 1, r, Lay, gen + 1u, pre,
+                         pre.valid);
+      } else if (tid == 0 && g.lay.sync) {
+        st_agent(g.lay.sync + kSyncFlag0 + row, gen + 1u);
+      }
+    }
+    if (tid == 0) Lay.misc[0] = (int)gen;          // for the wait and the exit
+    layer_retire(pre);
+    if (!has_tile) {
+      layer_exit(g.lay, Lay);
+      return;
+    }
+    if (!early) prologue();
+    const int row = min(m0 + e_row, M - 1);
+    e_r = Lay.rk[row];
+    e_slot = Lay.key[row] - 1;
+    e_scb = __float_as_int(Lay.sc[row]);
+  }
   // Every wave waits for all of its prologue loads (its stage, or its share
   // of each stage, and the metadata above) before the first barrier.
   vm_wait<0>();
-  if constexpr (LORA != 0) {
+  if constexpr (LORA != 0 && !LAYER) {
     if (e_own) {
       e_r = g.seg_rank[e_seg];
       e_slot = g.seg_slot[e_seg];
@@ -777,6 +847,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
     // (k ascending, read in chunks of 8 rank rows; rows at or past r are
     // read inside the slot and skipped), the DoRA factor when the pool has
     // one, and one rounding; the 8 results leave in one 16-byte store.
+    if constexpr (LAYER) layer_wait_rows<BM>(g.lay, g.X, g.ldx, m0, M, Lay);
     lgkm_barrier();
     float *red = reinterpret_cast<float *>(smem);
     constexpr int RS = BN + 4;
@@ -814,9 +885,11 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       }
     }
     if constexpr (LORA != 0) {
-      if (live && e_r > 0) lora_row8<DORA>(g, grow, gcol, e_slot, e_r, __int_as_float(e_scb), o);
+      if (live && e_r > 0)
+        lora_row8<DORA, LAYER>(g, grow, gcol, e_slot, e_r, __int_as_float(e_scb), o);
     }
     if (live) stg16(g.Y + (int64_t)grow * g.ldy + gcol, Elem<bf16_t>::pack(o));
+    if constexpr (LAYER) layer_exit(g.lay, Lay);
     return;
   }
 
@@ -1324,6 +1397,22 @@ hipError_t launch_fp8w(const GemmArgs &g, bool lora, hipStream_t stream) {
   return launch_bf16_w<BM, BN, WM, WN, BK, STAGES, KG, true>(g, lora, stream);
 }
 
+// The one-launch layer on small tiles: one workgroup per tile, and at least
+// one per row (workgroups past the tiles only do their row).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
+hipError_t launch_layer_t(const GemmArgs &g, hipStream_t stream) {
+  const int tiles = tile_grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN);
+  dim3 grid(tiles > g.M ? tiles : g.M);
+  dim3 block(WM * WN * KG * kWave);
+  if (g.dora)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true, false, true>),
+                       grid, block, 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false, false, true>),
+                       grid, block, 0, stream, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
@@ -1394,6 +1483,26 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
   else
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, dim3(256), 0, stream, g);
   return hipGetLastError();
+}
+
+hipError_t launch_layer(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                         int64_t ldy, int M, const PoolView &pool, const LayerArgs &lay,
+                         hipStream_t stream) {
+  if (pool.dtype != 1 || M < 1 || M > kLayerMaxRows) return hipErrorNotSupported;
+  const int K = pool.d_in, N = pool.d_out;
+  GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
+             lay.H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
+  g.proj = pool.proj;
+  g.Bt = (const bf16_t *)pool.Bt;
+  g.Bn = (const bf16_t *)pool.B;
+  g.dora = pool.dora;
+  g.r_max = pool.r_max;
+  g.policy = pool.policy;
+  g.lay = lay;
+  using S = TileCfg<LORA_GEMM_SMALL>;
+  const int64_t tiles = (int64_t)((M + S::kBM - 1) / S::kBM) * ((N + S::kBN - 1) / S::kBN);
+  if (tiles > kCUs) return launch_layer_t<LORA_GEMM_SMALL_WIDE>(g, stream);
+  return launch_layer_t<LORA_GEMM_SMALL>(g, stream);
 }
 
 }  // namespace lora

@@ -346,6 +346,58 @@ lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t
                                       static_cast<hipStream_t>(stream)));
 }
 
+lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
+                             int64_t ldw, const lora_pool *pool, const lora_segments *seg,
+                             float *H, void *Y, int64_t ldy, void *sync, void *stream) {
+  lora_status st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  st = check_segments(seg, pool);
+  if (st != LORA_OK) return st;
+  const int32_t n = seg->n_rows;
+  if (n > 0 && !row_slot) return LORA_ERR_NULL;
+  st = check_matrix(X, ldx, pool->d_in, n);
+  if (st != LORA_OK) return st;
+  st = check_matrix(W, ldw, pool->d_in, pool->d_out);
+  if (st != LORA_OK) return st;
+  st = check_matrix(Y, ldy, pool->d_out, n);
+  if (st != LORA_OK) return st;
+  if (n > 0) {
+    if (!H) return LORA_ERR_NULL;
+    if (!aligned16(H)) return LORA_ERR_ALIGN;
+  }
+  if (sync && !aligned16(sync)) return LORA_ERR_ALIGN;
+  if (n == 0) return lora_build_segments(row_slot, pool, seg, stream);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const lora::PoolView pv = pool_view(pool);
+  const lora::LayerArgs lay{row_slot,
+                            pool->A,
+                            pool->slot_rank,
+                            pool->slot_scale,
+                            pool->n_slots,
+                            pool_rs(pool),
+                            pool->d_in,
+                            pool->r_max,
+                            pv.proj.rs,
+                            pv.proj.n_proj,
+                            H,
+                            static_cast<uint32_t *>(sync),
+                            seg->token_indices,
+                            seg->row_segment,
+                            seg->segment_offsets,
+                            seg->segment_slots,
+                            seg->segment_ranks,
+                            seg->segment_scales,
+                            seg->num_segments,
+                            seg->status};
+  const hipError_t e = lora::launch_layer(X, ldx, W, ldw, Y, ldy, n, pv, lay, s);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  // outside the one-launch case: the two calls
+  (void)hipGetLastError();
+  st = lora_build_shrink(row_slot, X, ldx, pool, seg, H, stream);
+  if (st != LORA_OK) return st;
+  return lora_linear_fused(X, ldx, W, ldw, H, seg, pool, Y, ldy, stream);
+}
+
 lora_status lora_linear_fused_static(const int32_t *row_slot, const void *X, int64_t ldx,
                                      const void *W, int64_t ldw, const lora_pool *pool,
                                      int32_t n_rows, void *Y, int64_t ldy, void *stream) {

@@ -109,6 +109,29 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
                        const SegView *seg, const PoolView *pool, hipStream_t stream,
                        const float *wscale = nullptr);
 
+// Inputs and outputs of the one-launch layer beyond the product's own
+// (layer.cuh): the per-row slot ids and the pool's shrink operands, H, the
+// sync buffer (or null) and the segment metadata it writes.
+struct LayerArgs {
+  const int32_t *row_slot;
+  const void *A;              // pool A, [n_slots][r_max][d_in] (bf16)
+  const int32_t *slot_rank;
+  const float *slot_scale;
+  int n_slots, rank_bound;    // rank_bound: ranks above it demote a row to base-only
+  int d_in, r_max, rs, n_proj;
+  float *H;                   // [n][r_max], written and read back
+  uint32_t *sync;             // LORA_LAYER_SYNC_BYTES bytes, or null (no hand-off)
+  int32_t *token_indices, *row_segment, *seg_off, *seg_slot, *seg_rank;
+  float *seg_scale;
+  int32_t *num_segments, *status;
+};
+
+// The whole layer in one launch (segment metadata, H, Y) for bf16 pools and
+// 1 <= M <= 512 rows; hipErrorNotSupported (nothing launched) otherwise.
+hipError_t launch_layer(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                        int64_t ldy, int M, const PoolView &pool, const LayerArgs &lay,
+                        hipStream_t stream);
+
 // Device scratch of the allocation-free call lora_linear_fused_static: byte
 // offsets of its parts, each 256-byte aligned.  H is float [n][r_max]; the
 // segment arrays hold up to LORA_MAX_SLOTS + 1 segments (min(n, n_slots + 1)).

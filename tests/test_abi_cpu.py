@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
               "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
               "lora_base_gemm_fp8w", "lora_linear_fused_fp8w", "lora_status_str",
               "lora_abi_version", "lora_linear_fused_static", "lora_pool_set_scales",
-              "lora_pool_write_b"):
+              "lora_pool_write_b", "lora_layer_fused"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 6
+    assert L.lora_abi_version() == srg.ABI_VERSION == 7
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
@@ -341,4 +341,26 @@ def test_leading_dimension_limit(L):
     assert L.lora_base_gemm(P, 64, P, big, P, 32, 10, 64, 32, 1, None) == ESHAPE
     assert L.lora_base_gemm(P, 64, P, 64, P, big, 10, 64, 32, 1, None) == ESHAPE
     assert L.lora_base_gemm_fp8w(P, 64, P, big, P, P, 32, 10, 64, 32, None) == ESHAPE
+
+
+def test_layer_call_validation(L):
+    """The one-call layer checks the arguments of the three calls it stands
+    for, and its sync buffer's alignment, on the host (fake addresses: nothing
+    is launched)."""
+    f = L.lora_layer_fused
+    rs, X, W, H, Y, SY = P + 0xC000, P + 0xD000, P + 0xE000, P + 0xF000, P + 0x10000, P + 0x11000
+    p, sg = ctypes.byref(pool()), ctypes.byref(segs())
+    assert f(rs, X, 64, W, 64, None, sg, H, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, W, 64, p, None, H, Y, 32, SY, None) == ENULL
+    assert f(None, X, 64, W, 64, p, sg, H, Y, 32, SY, None) == ENULL
+    assert f(rs, None, 64, W, 64, p, sg, H, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, None, 64, p, sg, H, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, W, 64, p, sg, None, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, W, 64, p, sg, H, None, 32, SY, None) == ENULL
+    assert f(rs, X, 60, W, 64, p, sg, H, Y, 32, SY, None) == ESHAPE       # ldx < d_in
+    assert f(rs, X, 64, W, 64, p, sg, H + 8, Y, 32, SY, None) == EALIGN
+    assert f(rs, X, 64, W, 64, p, sg, H, Y, 32, SY + 4, None) == EALIGN   # sync alignment
+    assert f(rs, X, 64, W, 64, ctypes.byref(pool(rank_policy=5)), sg, H, Y, 32, SY, None) == EPOLICY
+    assert f(rs, X, 64, W, 64, p, ctypes.byref(segs(max_segments=4)), H, Y, 32, SY, None) == ECAP
+    assert srg.LAYER_SYNC_BYTES == 4096 and srg.LAYER_ONE_LAUNCH_ROWS == 512
 
