@@ -118,6 +118,17 @@ struct GemmArgs {
 #ifndef LORA_GEMM_SMALL_M
 #define LORA_GEMM_SMALL_M 512
 #endif
+// Tail split: a large batch whose 256 x 256 grid ends in a partial round of
+// the CUs runs the rows of its whole rounds on the large tiles and the
+// remaining rows (at most LORA_GEMM_SMALL_M) on the small tiles, as a
+// second launch, when that remainder has at most this many small tiles
+// (their per-CU bytes then stay under one round of large tiles).
+#ifndef LORA_GEMM_TAIL_SPLIT
+#define LORA_GEMM_TAIL_SPLIT 1
+#endif
+#ifndef LORA_GEMM_TAIL_TILES
+#define LORA_GEMM_TAIL_TILES 1024
+#endif
 
 // KG wave groups split each K step: group g takes the g-th BK-wide slice of
 // it with its own WM x WN waves and its own slice of the stage, and the
@@ -1413,6 +1424,47 @@ hipError_t launch_layer_t(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows that go to the large tiles when the batch is split (0: no split).
+int tail_split_rows(int M, int N) {
+  if (!LORA_GEMM_TAIL_SPLIT || M <= LORA_GEMM_SMALL_M) return 0;
+  const int64_t tn = (N + 255) / 256, tm = (M + 255) / 256;
+  const int64_t tiles = tm * tn;
+  if (tm * tn <= LORA_GEMM_MID_TILES || tiles % kCUs == 0 || tiles < kCUs) return 0;
+  const int64_t a = tiles / kCUs * kCUs / tn;   // 256-row M-tiles inside the whole rounds
+  const int64_t M2 = M - a * 256;
+  if (a < 1 || M2 <= 0 || M2 > LORA_GEMM_SMALL_M) return 0;
+  const int64_t small_tiles = (M2 + 63) / 64 * ((N + 63) / 64);
+  return small_tiles <= LORA_GEMM_TAIL_TILES ? (int)(a * 256) : 0;
+}
+
+// Tile configuration for a batch of g.M rows, and the launch.
+hipError_t launch_bf16_rows(const GemmArgs &g, bool lora, hipStream_t stream) {
+  const int M = g.M, N = g.N;
+  const bool mid = ((int64_t)(M + 255) / 256) * ((N + 255) / 256) <= LORA_GEMM_MID_TILES;
+  // Large tiles: 256 x 256, or 192 x 256 when its rounds of kCUs tiles cost
+  // less (rounds times tile area, the narrower tile charged its extra LDS
+  // traffic per flop).
+  const int64_t tn256 = (N + 255) / 256;
+  const int64_t r256 = ((int64_t)(M + 255) / 256 * tn256 + kCUs - 1) / kCUs;
+  const int64_t r192 = ((int64_t)(M + 191) / 192 * tn256 + kCUs - 1) / kCUs;
+  const bool use192 = r192 * 192 * LORA_GEMM_192_COST < r256 * 256 * 100;
+  if (g.wscale) {
+    if (M <= LORA_GEMM_SMALL_M) return launch_fp8w<LORA_GEMM_SMALL_F8>(g, lora, stream);
+    if (mid) return launch_fp8w<LORA_GEMM_MID_F8>(g, lora, stream);
+    if (use192) return launch_fp8w<LORA_GEMM_LARGE192_F8>(g, lora, stream);
+    return launch_fp8w<LORA_GEMM_LARGE_F8>(g, lora, stream);
+  }
+  if (M <= LORA_GEMM_SMALL_M) {
+    using S = TileCfg<LORA_GEMM_SMALL>;
+    const int64_t tiles = (int64_t)((M + S::kBM - 1) / S::kBM) * ((N + S::kBN - 1) / S::kBN);
+    if (tiles > kCUs) return launch_bf16<LORA_GEMM_SMALL_WIDE>(g, lora, stream);
+    return launch_bf16<LORA_GEMM_SMALL>(g, lora, stream);
+  }
+  if (mid) return launch_bf16<LORA_GEMM_MID>(g, lora, stream);
+  if (use192) return launch_bf16<LORA_GEMM_LARGE192>(g, lora, stream);
+  return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
@@ -1438,29 +1490,23 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
       g.r_max = pool->r_max;
       g.policy = pool->policy;
     }
-    const bool mid = ((int64_t)(M + 255) / 256) * ((N + 255) / 256) <= LORA_GEMM_MID_TILES;
-    // Large tiles: 256 x 256, or 192 x 256 when its rounds of kCUs tiles cost
-    // less (rounds times tile area, the narrower tile charged its extra LDS
-    // traffic per flop).
-    const int64_t tn256 = (N + 255) / 256;
-    const int64_t r256 = ((int64_t)(M + 255) / 256 * tn256 + kCUs - 1) / kCUs;
-    const int64_t r192 = ((int64_t)(M + 191) / 192 * tn256 + kCUs - 1) / kCUs;
-    const bool use192 = r192 * 192 * LORA_GEMM_192_COST < r256 * 256 * 100;
-    if (wscale) {
-      if (M <= LORA_GEMM_SMALL_M) return launch_fp8w<LORA_GEMM_SMALL_F8>(g, lora, stream);
-      if (mid) return launch_fp8w<LORA_GEMM_MID_F8>(g, lora, stream);
-      if (use192) return launch_fp8w<LORA_GEMM_LARGE192_F8>(g, lora, stream);
-      return launch_fp8w<LORA_GEMM_LARGE_F8>(g, lora, stream);
+    const int M1 = tail_split_rows(M, N);
+    if (M1 > 0) {
+      // rows [0, M1) on the large tiles, rows [M1, M) on the small ones
+      GemmArgs g2 = g;
+      g.M = M1;
+      g2.M = M - M1;
+      g2.X += (int64_t)M1 * ldx;
+      g2.Y += (int64_t)M1 * ldy;
+      if (lora) {
+        g2.row_segment += M1;
+        g2.H += (int64_t)M1 * g.r_max;
+      }
+      const hipError_t e = launch_bf16_rows(g, lora, stream);
+      if (e != hipSuccess) return e;
+      return launch_bf16_rows(g2, lora, stream);
     }
-    if (M <= LORA_GEMM_SMALL_M) {
-      using S = TileCfg<LORA_GEMM_SMALL>;
-      const int64_t tiles = (int64_t)((M + S::kBM - 1) / S::kBM) * ((N + S::kBN - 1) / S::kBN);
-      if (tiles > kCUs) return launch_bf16<LORA_GEMM_SMALL_WIDE>(g, lora, stream);
-      return launch_bf16<LORA_GEMM_SMALL>(g, lora, stream);
-    }
-    if (mid) return launch_bf16<LORA_GEMM_MID>(g, lora, stream);
-    if (use192) return launch_bf16<LORA_GEMM_LARGE192>(g, lora, stream);
-    return launch_bf16<LORA_GEMM_LARGE>(g, lora, stream);
+    return launch_bf16_rows(g, lora, stream);
   }
   GemmF32Args g{(const float *)X, ldx, (const float *)W, ldw, (float *)Y, ldy, M, K, N,
                 H, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};

@@ -119,9 +119,12 @@ FAMILIES = [
     ("t128_staged", 1100, 200, 1032, 128, [1, 2, 3, 4]),
     ("t128_rows", 1100, 200, 1032, 128, [5, 9, 30, 128]),
     ("t128_mixed", 1100, 200, 1032, 128, [1, 7, 4, 64, 2]),
-    ("t192_staged", 2100, 136, 8200, 192, [1, 2, 3, 4]),   # 11 x 33 tiles of 192 x 256
-    ("t192_rows", 2100, 136, 8200, 192, [5, 40, 192]),
-    ("t192_mixed", 2100, 136, 8200, 192, [4, 192, 1, 6]),
+    ("t192_staged", 1100, 136, 8200, 192, [1, 2, 3, 4]),   # 6 x 33 tiles of 192 x 256
+    ("t192_rows", 1100, 136, 8200, 192, [5, 40, 192]),
+    ("t192_mixed", 1100, 136, 8200, 192, [4, 192, 1, 6]),
+    # rows [0, 1792) on 7 x 33 tiles of 256 x 256, rows [1792, 2100) on 64 x 64 tiles
+    ("split_staged", 2100, 136, 8200, 256, [1, 2, 3, 4]),
+    ("split_rows", 2100, 136, 8200, 256, [5, 40, 256]),
     ("t256_staged", 2040, 136, 7944, 256, [1, 2, 3, 4]),   # 8 x 32 tiles of 256 x 256
     ("t256_rows", 2040, 136, 7944, 256, [5, 40, 256]),
     ("t256_mixed", 2040, 136, 7944, 256, [4, 256, 1, 6]),

@@ -61,6 +61,7 @@ MANY = [
     (702, 1100, 200, 8200, 40, 0.1),     # 192 x 256 tiles, K tail, ragged M and N
     (703, 600, 136, 11008, 70, 0.3),     # 192 x 256 tiles, ragged M
     (708, 2040, 200, 7944, 40, 0.1),     # 256 x 256 tiles, K tail, ragged M and N
+    (709, 2100, 200, 8200, 40, 0.1),     # split: 256 x 256 tiles, then 64 x 64 from row 1792
 ]
 
 
