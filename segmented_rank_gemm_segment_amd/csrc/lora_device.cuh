@@ -170,19 +170,36 @@ struct SegItem {
   int r, slot, o0, o1, p0, p1;
   float sc;
 };
+// Positions [p0, p1) of item y given its segment s = [o0, o1) among S.
+__device__ __forceinline__ bool item_span(int y, int nb, int rb, int s, int S, int o0, int o1,
+                                          int &p0, int &p1) {
+  const bool whole = o1 - o0 <= rb;   // short segment: one head item
+  if (y < nb) {
+    p0 = y * rb;
+    p1 = min(p0 + rb, o1);
+    return s < S && !whole && o0 != p0 && p0 < p1;
+  }
+  p0 = o0;
+  p1 = whole ? o1 : min(o1, (o0 / rb + 1) * rb);
+  return s < S && p0 < p1;
+}
+// Segment of item y (clamped into the arrays for position items).
+__device__ __forceinline__ int item_segment(int y, int nb, int rb, int cap,
+                                            const int32_t *token_indices,
+                                            const int32_t *row_segment) {
+  if (y >= nb) return y - nb;
+  const int s = row_segment[token_indices[y * rb]];
+  return min(max(s, 0), cap - 1);
+}
+// One item per wave (y wave-uniform; the segment's fields are read by
+// separate lanes).
 __device__ __forceinline__ SegItem seg_item(int y, int nb, int rb, int cap,
                                             const int32_t *token_indices,
                                             const int32_t *row_segment,
                                             const int32_t *num_segments, const int32_t *seg_rank,
                                             const int32_t *seg_off, const int32_t *seg_slot,
                                             const float *seg_scale) {
-  int s, p0 = y * rb;
-  if (y < nb) {
-    s = row_segment[token_indices[p0]];
-    s = min(max(s, 0), cap - 1);
-  } else {
-    s = y - nb;
-  }
+  const int s = item_segment(y, nb, rb, cap, token_indices, row_segment);
   const SegMeta m = load_seg_meta(s, num_segments, seg_rank, seg_off, seg_slot, seg_scale);
   SegItem it;
   it.r = m.r;
@@ -190,16 +207,23 @@ __device__ __forceinline__ SegItem seg_item(int y, int nb, int rb, int cap,
   it.sc = m.sc;
   it.o0 = m.o0;
   it.o1 = m.o1;
-  const bool whole = m.o1 - m.o0 <= rb;   // short segment: one head item
-  if (y < nb) {
-    it.p0 = p0;
-    it.p1 = min(p0 + rb, m.o1);
-    it.ok = s < m.S && !whole && m.o0 != p0 && p0 < it.p1;
-  } else {
-    it.p0 = m.o0;
-    it.p1 = whole ? m.o1 : min(m.o1, (m.o0 / rb + 1) * rb);
-    it.ok = s < m.S && it.p0 < it.p1;
-  }
+  it.ok = item_span(y, nb, rb, s, m.S, m.o0, m.o1, it.p0, it.p1);
+  return it;
+}
+// One item per lane (y per lane, S given).
+__device__ __forceinline__ SegItem seg_item_lane(int y, int nb, int rb, int cap, int S,
+                                                 const int32_t *token_indices,
+                                                 const int32_t *row_segment,
+                                                 const int32_t *seg_rank, const int32_t *seg_off,
+                                                 const int32_t *seg_slot, const float *seg_scale) {
+  const int s = item_segment(y, nb, rb, cap, token_indices, row_segment);
+  SegItem it;
+  it.r = seg_rank[s];
+  it.slot = seg_slot[s];
+  it.sc = seg_scale[s];
+  it.o0 = seg_off[s];
+  it.o1 = seg_off[s + 1];
+  it.ok = item_span(y, nb, rb, s, S, it.o0, it.o1, it.p0, it.p1);
   return it;
 }
 

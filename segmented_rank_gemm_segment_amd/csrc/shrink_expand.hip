@@ -20,6 +20,7 @@
 // every load of a work item is issued before its arithmetic, so a work item
 // costs about one memory round trip.  Each token row lives in exactly one
 // segment, so Y is updated without atomics and results are deterministic.
+#include <algorithm>
 #include <climits>
 
 #include "lds_dma.cuh"
@@ -448,6 +449,253 @@ inline int grid_items(int items, int x) {
   return items < cap ? (items > 0 ? items : 1) : cap;
 }
 
+// ----------------------------------------------------------------------------
+// Expand of large bf16 batches (at least kMfmaShrinkMinBatch rows) whose pool
+// keeps B d_out-major: per work item (at most kRowBlk rows of one segment,
+// the items of the GEMV expand) and 256 output columns, the increment is a
+// product over the rank, taken on the matrix cores in the orientation
+// D^T = B_a (columns x ranks) (s_a H)^T (ranks x rows), with the item's Y as
+// the accumulator's initial value: D = Y + s_a H B_a^T in fp32, times the
+// DoRA factor, rounded once.  s_a H is fp32, so each value enters as a bf16
+// high part plus the bf16 remainder (two products; about 16 significant
+// bits, while B is bf16 and exact).  Rank entries past r are zeroed in both
+// operands (a padded slot's values there are never used); the launcher
+// gives each workgroup's columns a single projection.
+//
+// Y moves between HBM and the workgroup only in whole 512-byte row pieces
+// (16 bytes per lane, 32 lanes per row), through an LDS tile: the
+// accumulators read their start values from it and write the rounded
+// results back in place, and the rows leave it the way they came.  The
+// tile's 16-byte chunks are XOR-swizzled by row so that the accumulator
+// layout (lanes along rows) spreads its reads and writes over the banks (at
+// most two lanes of a half-wave on one bank).
+// The item's s_a H rows are split into LDS once; each wave reads its
+// operand fragments from there and its 64 columns of B from memory.
+//
+// A workgroup walks the items blockIdx.y + t gridDim.y.  It first reads the
+// metadata of all of them at once (one item per thread) into an LDS table
+// of the items that have rows; each item's row indices are requested during
+// the previous item.
+// ----------------------------------------------------------------------------
+constexpr int kXmCols = 256;   // columns per workgroup: 4 waves x 64
+constexpr int kXmPitch = 144;  // bytes per LDS row of 64 bf16 ranks (+16: spreads the banks)
+constexpr int kXmItems = 64;   // items per workgroup at most (its metadata table)
+constexpr int kXmRowBytes = kXmCols * 2;
+static_assert(kRowBlk == 64, "an item's rows fill the two 32-row blocks of a lane");
+
+__device__ __forceinline__ int xm_chunk(int row, int c) { return c ^ (row & 31); }
+
+template <bool DORA>
+__global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
+    const float *__restrict__ H, const bf16_t *__restrict__ Bn, const float *__restrict__ dora,
+    const int32_t *token_indices, const int32_t *row_segment, const int32_t *seg_off,
+    const int32_t *seg_slot, const int32_t *seg_rank, const float *seg_scale,
+    const int32_t *num_segments, int r_max, int d_out, int policy, int nb, int seg_cap,
+    bf16_t *__restrict__ Y, int64_t ldy, ProjView proj) {
+  __shared__ __align__(16) unsigned char s_y[kRowBlk * kXmRowBytes];  // the item's Y tile
+  __shared__ __align__(16) unsigned char s_h[2][kRowBlk * kXmPitch];  // s_a H: high, low parts
+  __shared__ int s_tab[5][kXmItems];     // slot, rank, scale bits, p0, p1 of the items with rows
+  __shared__ int s_rows[2][kRowBlk];     // row indices of the current and the next item
+  __shared__ int s_cnt[4];
+  const int tid = threadIdx.x;
+  const int l = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int l32 = l & 31, hf = l >> 5;
+  const int c0 = blockIdx.x * kXmCols;               // the workgroup's first column
+  const int nw = c0 + wave * 64;                     // the wave's first column
+  const int rs = proj.rs;
+  const int qoff = proj_of(proj, min(c0, d_out - 1)) * rs;
+  {
+    // item blockIdx.y + tid gridDim.y (the launcher keeps the walk within
+    // kXmItems), kept if it has rows and a nonzero rank
+    const int S = *num_segments;
+    const int y = blockIdx.y + tid * gridDim.y;
+    bool keep = false;
+    SegItem it{};
+    if (tid < kXmItems && y < nb + seg_cap && (y < nb || y - nb < S)) {
+      it = seg_item_lane(y, nb, kRowBlk, seg_cap, S, token_indices, row_segment, seg_rank,
+                         seg_off, seg_slot, seg_scale);
+      keep = it.ok && rank_bucket(it.r, policy, rs) > 0;
+    }
+    // compact in item order: wave prefix by ballot, then the waves' counts
+    const uint64_t bal = __ballot(keep);
+    const int before = __popcll(bal & ((1ull << l) - 1ull));
+    if (l == 0) s_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_cnt[w];
+    if (keep) {
+      const int k = base + before;
+      s_tab[0][k] = it.slot;
+      s_tab[1][k] = it.r;
+      s_tab[2][k] = __float_as_int(it.sc);
+      s_tab[3][k] = it.p0;
+      s_tab[4][k] = it.p1;
+    }
+    __syncthreads();
+  }
+  const int K = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  if (K == 0) return;
+  // row index of row t of item k (past the item's end: its last row, never stored)
+  auto row_of = [&](int k, int t) {
+    const int p0 = s_tab[3][k], nrow = s_tab[4][k] - p0;
+    return token_indices[p0 + min(t, nrow - 1)];
+  };
+  if (tid < kRowBlk) s_rows[0][tid] = row_of(0, tid);
+  __syncthreads();
+  const int hm = tid >> 2, hc = (tid & 3) * 16;   // the H row and first rank this thread splits
+  const int yr = tid >> 5, yc = tid & 31;         // Y pieces: rows yr + 8 i, chunk yc
+  const int ycol = min(c0 + yc * 8, d_out - 8);   // (clamped into the row; never stored past it)
+  const int hk = min(hc, rs - 16 > 0 ? rs - 16 : 0);
+  // the row loads of item k: Y rows in 16-byte pieces, this thread's 16
+  // ranks of H row hm (ranks past r, and past rs, zeroed where used), the
+  // next item's row indices (the last item reads its own again)
+  u32x4 ly[kRowBlk / 8];
+  float4 lh[4];
+  int lnxt;
+  auto load_rows = [&](int k) __attribute__((always_inline)) {
+    const int cq = k & 1;
+#pragma unroll
+    for (int i = 0; i < kRowBlk / 8; ++i)
+      ly[i] = *reinterpret_cast<const u32x4 *>(Y + (int64_t)s_rows[cq][yr + 8 * i] * ldy + ycol);
+    const int hrow = s_rows[cq][hm];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      lh[c] = *reinterpret_cast<const float4 *>(H + (int64_t)hrow * r_max + qoff +
+                                                min(hk + 4 * c, rs - 4));
+    lnxt = row_of(min(k + 1, K - 1), tid & (kRowBlk - 1));
+  };
+  load_rows(0);
+  for (int k = 0; k < K; ++k) {
+    const int cur = k & 1;
+    const int slot = __builtin_amdgcn_readfirstlane(s_tab[0][k]);
+    const int r = __builtin_amdgcn_readfirstlane(s_tab[1][k]);
+    const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_tab[2][k]));
+    const int nrow = __builtin_amdgcn_readfirstlane(s_tab[4][k] - s_tab[3][k]);
+    const int R = rank_bucket(r, policy, rs);
+    // B rows of the wave's columns, every rank step (ranks past r zeroed below)
+    const bf16_t *bs = Bn + (int64_t)slot * d_out * r_max + qoff;
+    u32x4 bv[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(nw + 32 * j + l32, d_out - 1);
+        const int kc = min(ks * 16 + hf * 8, rs - 8);
+        bv[ks][j] = *reinterpret_cast<const u32x4 *>(bs + (int64_t)n * r_max + kc);
+      }
+    {
+      const float hv[16] = {lh[0].x, lh[0].y, lh[0].z, lh[0].w, lh[1].x, lh[1].y, lh[1].z, lh[1].w,
+                            lh[2].x, lh[2].y, lh[2].z, lh[2].w, lh[3].x, lh[3].y, lh[3].z, lh[3].w};
+      u32x4 phi[2], plo[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const int kk = hc + 2 * e2;
+        const float v0 = kk < r ? sc * hv[2 * e2] : 0.f;
+        const float v1 = kk + 1 < r ? sc * hv[2 * e2 + 1] : 0.f;
+        const uint32_t hw = pack_bf16x2(v0, v1);
+        phi[e2 >> 2][e2 & 3] = hw;
+        plo[e2 >> 2][e2 & 3] = pack_bf16x2(v0 - bf16_lo(hw), v1 - bf16_hi(hw));
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        *reinterpret_cast<u32x4 *>(s_h[0] + hm * kXmPitch + (hc + 8 * h2) * 2) = phi[h2];
+        *reinterpret_cast<u32x4 *>(s_h[1] + hm * kXmPitch + (hc + 8 * h2) * 2) = plo[h2];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowBlk / 8; ++i) {
+      const int row = yr + 8 * i;
+      *reinterpret_cast<u32x4 *>(s_y + row * kXmRowBytes + xm_chunk(row, yc) * 16) = ly[i];
+    }
+    if (tid < kRowBlk) s_rows[cur ^ 1][tid] = lnxt;
+    __syncthreads();
+    // accumulators start at Y (accumulator v = 4 g + e of block (j, mb):
+    // column nw + 32 j + 8 g + 4 hf + e, row m = l32 + 32 mb; its 8 bytes in
+    // the tile at chunk wave * 8 + 4 j + g, offset 8 hf)
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = l32 + 32 * mb;
+          const uint2 y = *reinterpret_cast<const uint2 *>(
+              s_y + m * kXmRowBytes + xm_chunk(m, wave * 8 + 4 * j + g) * 16 + hf * 8);
+          acc[j][mb][4 * g + 0] = bf16_lo(y.x);
+          acc[j][mb][4 * g + 1] = bf16_hi(y.x);
+          acc[j][mb][4 * g + 2] = bf16_lo(y.y);
+          acc[j][mb][4 * g + 3] = bf16_hi(y.y);
+        }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks * 16 >= R) break;
+      const int k0 = ks * 16 + hf * 8;              // the lane's first rank of the step
+      mfma_bf16x8 a[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 v = bv[ks][j];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int kk = k0 + 2 * e2;
+          v[e2] &= (kk < r ? 0x0000ffffu : 0u) | (kk + 1 < r ? 0xffff0000u : 0u);
+        }
+        a[j] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int off = (l32 + 32 * mb) * kXmPitch + k0 * 2;
+        const mfma_bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_h[0] + off));
+        const mfma_bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_h[1] + off));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bh, acc[j][mb], 0, 0, 0);
+          acc[j][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bl, acc[j][mb], 0, 0, 0);
+        }
+      }
+    }
+    // rounded results back into the tile, each lane where it read
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float gv[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (DORA) {
+          const int n = nw + 32 * j + 8 * g + 4 * hf;
+          const float4 t = *reinterpret_cast<const float4 *>(
+              dora + (int64_t)slot * d_out + min(n, d_out - 4));
+          gv[0] = t.x; gv[1] = t.y; gv[2] = t.z; gv[3] = t.w;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int m = l32 + 32 * mb;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = acc[j][mb][4 * g + e];
+            if constexpr (DORA) o[e] *= gv[e];
+          }
+          *reinterpret_cast<uint2 *>(s_y + m * kXmRowBytes + xm_chunk(m, wave * 8 + 4 * j + g) * 16 +
+                                     hf * 8) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+      }
+    __syncthreads();
+    // the next item's loads go out before this item's stores, so waiting for
+    // them later never waits for the stores (the last item loads itself again)
+    load_rows(min(k + 1, K - 1));
+    // the rows leave in 16-byte pieces
+#pragma unroll
+    for (int i = 0; i < kRowBlk / 8; ++i) {
+      const int row = yr + 8 * i;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(s_y + row * kXmRowBytes + xm_chunk(row, yc) * 16);
+      if (row < nrow && c0 + yc * 8 < d_out)
+        *reinterpret_cast<u32x4 *>(Y + (int64_t)s_rows[cur][row] * ldy + c0 + yc * 8) = v;
+    }
+    __syncthreads();   // the tile, the H split and s_rows[cur] are rewritten for the next item
+  }
+}
+
 }  // namespace
 
 template <int SM, int SN>
@@ -540,12 +788,42 @@ void launch_expand_r(const float *H, const SegView &seg, const PoolView &pool, v
   }
 }
 
+// The MFMA expand takes large bf16 batches of pools with the d_out-major B
+// whose projections each start at a multiple of its 256-column blocks.
+inline bool expand_on_mfma(int n, const PoolView &pool) {
+  if (pool.dtype != 1 || !pool.B || n < kMfmaShrinkMinBatch) return false;
+  for (int q = 1; q < pool.proj.n_proj; ++q)
+    if (pool.proj.col_off[q] % kXmCols) return false;
+  return true;
+}
+
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
                          int64_t ldy, hipStream_t stream) {
   const int n = seg.n_rows;
   const int rb = row_block(n);
   const int nb = (n + rb - 1) / rb;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
+  if (expand_on_mfma(n, pool)) {
+    // rb = kRowBlk here (n >= kLargeBatch)
+    // at most kXmItems items per workgroup (its metadata table)
+    const int gx = (pool.d_out + kXmCols - 1) / kXmCols;
+    const int items = nb + S_bound;
+    const int gy = std::max(grid_items(items, gx), (items + kXmItems - 1) / kXmItems);
+    const dim3 grid(gx, gy);
+    if (pool.dora)
+      hipLaunchKernelGGL(expand_mfma_kernel<true>, grid, dim3(4 * kWave), 0, stream, H,
+                         (const bf16_t *)pool.B, pool.dora, seg.token_indices, seg.row_segment,
+                         seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
+                         pool.r_max, pool.d_out, pool.policy, nb, S_bound, (bf16_t *)Y, ldy,
+                         pool.proj);
+    else
+      hipLaunchKernelGGL(expand_mfma_kernel<false>, grid, dim3(4 * kWave), 0, stream, H,
+                         (const bf16_t *)pool.B, nullptr, seg.token_indices, seg.row_segment,
+                         seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
+                         pool.r_max, pool.d_out, pool.policy, nb, S_bound, (bf16_t *)Y, ldy,
+                         pool.proj);
+    return hipGetLastError();
+  }
   if (pool.dtype == 1)
     launch_expand_r<bf16_t>(H, seg, pool, Y, ldy, rb, nb, S_bound, stream);
   else
