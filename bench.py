@@ -465,17 +465,50 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
+# The translation unit each timed kernel is compiled in.
+KERNEL_UNIT = {"layer": "gemm.hip", "fused": "gemm.hip", "base": "gemm.hip",
+               "fused_fp8w": "gemm.hip", "base_fp8w": "gemm.hip",
+               "shrink": "shrink_expand.hip", "shrink_mfma": "shrink_expand.hip",
+               "expand": "shrink_expand.hip", "build": "build_segments.hip",
+               "build_shrink": "build_segments.hip"}
+
+
+def unit_source_sha(unit):
+    """sha256 over the code (comments dropped) of one translation unit and
+    every local header it includes, directly or not."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "segmented_rank_gemm_segment_amd", "csrc")
+    seen, todo = [], [os.path.normpath(os.path.join(csrc, unit))]
+    while todo:
+        path = todo.pop()
+        if path in seen:
+            continue
+        seen.append(path)
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        for inc in re.findall(r'^\s*#include\s+"([^"]+)"', text, flags=re.M):
+            todo.append(os.path.normpath(os.path.join(os.path.dirname(path), inc)))
+    h = hashlib.sha256()
+    for path in sorted(seen):
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.relpath(path, ROOT).encode() + b"\0" + _code_only(f.read()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(config, kernel):
     """HBM bytes per launch of `kernel` on `config` from rocprofv3 FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch, each scaled by the reading of a plain
     copy of known size), or None when no counters were taken for the current
-    kernel sources."""
+    code of the kernel's translation unit (and the headers it includes)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_sha():
+    unit = KERNEL_UNIT.get(kernel)
+    shas = t.get("unit_sha256", {})
+    if unit is None or unit not in shas or shas[unit] != unit_source_sha(unit):
         return None
     k = t.get("configs", {}).get(str(config), {}).get(kernel)
     if not k:
