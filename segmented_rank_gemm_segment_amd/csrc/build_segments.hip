@@ -16,6 +16,7 @@
 // 1024 threads) or as block 0 of the combined build + shrink launch.
 #include <climits>
 
+#include "lds_dma.cuh"
 #include "lora_device.cuh"
 #include "lora_kernels.h"
 #include "shrink_rows.cuh"
@@ -28,8 +29,17 @@ constexpr int kMaxKeys = 4096;  // n_slots + 1 (slot keys plus the base-only key
 
 // Keys of the first kRegChunks chunks of rows stay in registers between the
 // passes; rows past that keep theirs in row_segment (read back by the same
-// thread).  Slot tables are staged in LDS once.
+// thread, two chunks ahead of their use).  Slot tables are staged in LDS
+// once.  (More register chunks unroll the passes into more code than the
+// instruction cache holds, which slows small batches down.)
 constexpr int kRegChunks = 4;
+// Batches up to kBitRows rows number their segments from a bitmap of the
+// keys' first rows (one pass, no per-chunk barriers).
+constexpr int kBitRows = 65536;
+// Builds of at most kFastSegs segments place rows through a per-wave,
+// per-segment count table (two barriers per chunk); more segments take the
+// serial walk over the waves' group leaders.
+constexpr int kFastSegs = 256;
 
 struct Tables {
   int *first, *cnt, *off, *rank, *lead_key, *lead_cnt, *lead_base, *wave;
@@ -52,21 +62,27 @@ __device__ __forceinline__ int row_key(int slot, const BuildArgs &a, const Table
   return slot + 1;
 }
 
-}  // namespace
-
-// LDS words the routine needs for a pool of n_slots and a block of nthr
-// threads.
-int build_lds_words(int n_slots, int nthr) {
+// LDS words the routine needs for a pool of n_slots, n rows and a block of
+// nthr threads; `table`: room for the per-wave segment counts.
+int build_lds_words(int n_slots, int nthr, int n, bool table) {
   const int K = n_slots + 1;
-  return 5 * K + 1 + 3 * nthr + nthr / kWave + 2;
+  const int bits = n <= kBitRows ? 2 * ((n + 31) / 32) : 0;
+  return 5 * K + 1 + 3 * nthr + nthr / kWave + 2 + bits +
+         (table ? 2 * (nthr / kWave) * kFastSegs : 0);
 }
 
+}  // namespace
+
 // The whole build by one workgroup (blockDim.x = 64..1024 threads, a
-// multiple of 64) with `lds` pointing at build_lds_words(...) words.
-__device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *lds) {
+// multiple of 64) with `lds` pointing at build_lds_words(..., table) words.
+__device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *lds, bool table) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  const int nwaves = nthr / kWave;
   const int Kw = a.n_slots + 1;
+  const int n = a.n;
+  const int nbw = n <= kBitRows ? (n + 31) / 32 : 0;   // bitmap words (LDS layout)
+  const bool bitmap = nbw > 0 && n > nthr;              // one chunk: numbered as it is walked
   int *s_first = lds;                   // first row of a key; later -(segment + 1)
   int *s_cnt = s_first + Kw;            // rows of a key; later the per-key cursor
   int *s_off = s_cnt + Kw;              // segment lengths, then exclusive offsets (Kw + 1)
@@ -76,20 +92,22 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
   int *s_lead_cnt = s_lead_key + nthr;
   int *s_lead_base = s_lead_cnt + nthr;
   int *s_wave = s_lead_base + nthr;
-  int &s_bad = s_wave[nthr / kWave];
-  int &s_total = s_wave[nthr / kWave + 1];
+  int &s_bad = s_wave[nwaves];
+  int &s_total = s_wave[nwaves + 1];
+  uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_wave + nwaves + 2);  // [nbw]
+  int *s_bpre = reinterpret_cast<int *>(s_bits + nbw);                    // [nbw]
+  int *s_wcnt = s_bpre + nbw;            // [nwaves][kFastSegs] (table only)
+  int *s_wbase = s_wcnt + nwaves * kFastSegs;
 
-  const int nwaves = nthr / kWave;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int K = a.n_slots + 1;
-  const int n = a.n;
   const int nchunks = (n + nthr - 1) / nthr;
   const Tables t{s_first, s_cnt, s_off, s_rank, s_lead_key, s_lead_cnt, s_lead_base, s_wave,
                  s_scale};
 
   // Stage 0: one round of global loads: row slots of the register chunks and
-  // the slot tables.
+  // the slot tables; LDS tables cleared.
   int keyreg[kRegChunks];
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
@@ -104,6 +122,9 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
     s_first[k] = INT_MAX;
     s_cnt[k] = 0;
   }
+  for (int w = tid; w < nbw; w += nthr) s_bits[w] = 0u;
+  if (table)
+    for (int e = tid; e < nwaves * kFastSegs; e += nthr) s_wcnt[e] = 0;
   if (tid == 0) {
     s_bad = 0;
     s_total = 0;
@@ -113,6 +134,24 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
   // Pass 1: validate, remember keys, first row and row count per key.  One
   // LDS atomic per group of equal keys in a wave; min/add commute, so the
   // result does not depend on the order they land in.
+  // Chunks past the registers, in groups of kGrp: the next group's values
+  // are requested before this group is processed, so a chunk never waits a
+  // memory round trip for its own.
+  constexpr int kGrp = 4;
+  auto walk = [&](auto load, auto body) {
+    int cur[kGrp], nxt[kGrp];
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) cur[u] = load(kRegChunks + u);
+    for (int g = kRegChunks; g < nchunks; g += kGrp) {
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) nxt[u] = load(g + kGrp + u);
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u)
+        if (g + u < nchunks) body(g + u, cur[u]);
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) cur[u] = nxt[u];
+    }
+  };
   uint64_t peersreg[kRegChunks];  // pass-1 groups of the register chunks, reused in pass 4
   auto pass1 = [&](int c, int slot, uint64_t &peers_out) -> int {
     const int i = c * nthr + tid;
@@ -134,49 +173,93 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
     peersreg[c] = 0;
     if (c < nchunks) keyreg[c] = pass1(c, keyreg[c], peersreg[c]);
   }
-  for (int c = kRegChunks; c < nchunks; ++c) {
-    const int i = c * nthr + tid;
-    uint64_t unused;
-    const int key = pass1(c, i < n ? a.row_slot[i] : -1, unused);
-    if (i < n) a.row_segment[i] = key;
-  }
+  walk([&](int c) { const int i = c * nthr + tid; return i < n ? a.row_slot[i] : -1; },
+       [&](int c, int slot) {
+         const int i = c * nthr + tid;
+         uint64_t unused;
+         const int key = pass1(c, slot, unused);
+         if (i < n) a.row_segment[i] = key;
+       });
   __syncthreads();
 
-  // Pass 2: a row is the head of its segment iff it is its key's first row.
-  // Segment ids are the running count of heads: first-appearance order.
-  auto pass2 = [&](int c, int key) {
-    const int i = c * nthr + tid;
-    const bool valid = i < n;
-    const bool head = valid && s_first[key] == i;
-    const uint64_t hm = __ballot(head);
-    if (lane == 0) s_wave[wave] = __popcll(hm);
-    __syncthreads();
-    int before = s_total;
-    for (int w = 0; w < wave; ++w) before += s_wave[w];
-    if (head) {
-      const int s = before + __popcll(hm & lanemask_lt());
-      const int slot = key - 1;
-      const int r = key == 0 ? 0 : s_rank[slot];
-      a.seg_slot[s] = slot;
-      a.seg_rank[s] = r;
-      a.seg_scale[s] = r > 0 ? s_scale[slot] : 0.0f;
-      s_off[s] = s_cnt[key];
-      s_first[key] = -(s + 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int w = 0; w < nwaves; ++w) tot += s_wave[w];
-      s_total += tot;
-    }
-    __syncthreads();
+  // From here on the barriers order LDS only (lgkm_barrier): the global
+  // stores of pass 4 are read by no other thread, and pass 1's stores of the
+  // keys were completed by the barrier above.
+  // key of this thread's row in chunk c past the registers (row_segment holds
+  // it from pass 1 until pass 4 overwrites it with the segment id; a chunk's
+  // keys are read before its own pass 4 and before any later chunk's)
+  auto key_at = [&](int c) { const int i = c * nthr + tid; return i < n ? a.row_segment[i] : 0; };
+
+  // Pass 2: a row is the head of its segment iff it is its key's first row,
+  // and segment ids count the heads in row order (first-appearance order).
+  // Writes the segments' slot, rank, scale and length; s_first[key] becomes
+  // -(segment + 1).
+  auto head_out = [&](int key, int s) {
+    const int slot = key - 1;
+    const int r = key == 0 ? 0 : s_rank[slot];
+    a.seg_slot[s] = slot;
+    a.seg_rank[s] = r;
+    a.seg_scale[s] = r > 0 ? s_scale[slot] : 0.0f;
+    s_off[s] = s_cnt[key];
+    s_first[key] = -(s + 1);
   };
+  if (bitmap) {
+    // heads as bits of a row bitmap; a head's id is the number of set bits
+    // before it (a block scan of the words' popcounts)
+    for (int k = tid; k < K; k += nthr) {
+      const int f = s_first[k];
+      if (f != INT_MAX) atomicOr(&s_bits[f >> 5], 1u << (f & 31));
+    }
+    lgkm_barrier();
+    const int wpt = (nbw + nthr - 1) / nthr;     // words per thread, consecutive
+    const int w0 = min(tid * wpt, nbw), w1 = min(w0 + wpt, nbw);
+    int mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __popc(s_bits[w]);
+    int incl = mine;
 #pragma unroll
-  for (int c = 0; c < kRegChunks; ++c)
-    if (c < nchunks) pass2(c, keyreg[c]);
-  for (int c = kRegChunks; c < nchunks; ++c) {
-    const int i = c * nthr + tid;
-    pass2(c, i < n ? a.row_segment[i] : 0);
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    lgkm_barrier();
+    int before = incl - mine;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    for (int w = w0; w < w1; ++w) {
+      s_bpre[w] = before;
+      before += __popc(s_bits[w]);
+    }
+    if (tid == nthr - 1) s_total = before;       // the last thread's end: all heads
+    lgkm_barrier();
+    for (int k = tid; k < K; k += nthr) {
+      const int f = s_first[k];
+      if (f != INT_MAX)
+        head_out(k, s_bpre[f >> 5] + __popc(s_bits[f >> 5] & ((1u << (f & 31)) - 1u)));
+    }
+    lgkm_barrier();
+  } else {
+    auto pass2 = [&](int c, int key) {
+      const int i = c * nthr + tid;
+      const bool valid = i < n;
+      const bool head = valid && s_first[key] == i;
+      const uint64_t hm = __ballot(head);
+      if (lane == 0) s_wave[wave] = __popcll(hm);
+      lgkm_barrier();
+      int before = s_total;
+      for (int w = 0; w < wave; ++w) before += s_wave[w];
+      if (head) head_out(key, before + __popcll(hm & lanemask_lt()));
+      lgkm_barrier();
+      if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < nwaves; ++w) tot += s_wave[w];
+        s_total += tot;
+      }
+      lgkm_barrier();
+    };
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c)
+      if (c < nchunks) pass2(c, keyreg[c]);
+    walk(key_at, pass2);
   }
   const int S = s_total;
 
@@ -193,7 +276,7 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
       if (lane >= d) incl += u;
     }
     if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
+    lgkm_barrier();
     int before = carry;
     int chunk = 0;
     for (int w = 0; w < nwaves; ++w) {
@@ -206,53 +289,90 @@ __device__ __forceinline__ void build_segments_block(const BuildArgs &a, int *ld
       a.seg_off[s] = excl;
     }
     carry += chunk;
-    __syncthreads();
+    lgkm_barrier();
   }
   if (tid == 0) s_off[S] = n;
-  __syncthreads();
+  lgkm_barrier();
 
   // Pass 4: position = segment offset + rows of the same key in earlier
-  // chunks and waves + rows of the same key in lower lanes.  Wave 0 walks
-  // the 16 waves' group leaders in order, so the cross-wave part follows
-  // row order exactly.
-  auto pass4 = [&](int c, int key, uint64_t peers) {
-    const int i = c * nthr + tid;
-    const bool valid = i < n;
-    const int local = __popcll(peers & lanemask_lt());
-    s_lead_cnt[tid] = (valid && local == 0) ? __popcll(peers) : 0;
-    s_lead_key[tid] = key;
-    __syncthreads();
-    if (wave == 0) {
-      // waves past the last row of the chunk hold no leaders
-      const int wend = min(nwaves, (n - c * nthr + kWave - 1) / kWave);
-      for (int w = 0; w < wend; ++w) {
-        const int u = w * kWave + lane;
-        const int cnt = s_lead_cnt[u];
-        if (cnt > 0) {
-          const int k = s_lead_key[u];
-          const int b = s_cnt[k];
-          s_cnt[k] = b + cnt;
-          s_lead_base[u] = b;
+  // chunks and waves + rows of the same key in lower lanes, so rows keep
+  // their order inside a segment.
+  if (table && S <= kFastSegs) {
+    // Each wave's group leaders put their counts in the wave's row of a
+    // [wave][segment] table; thread s turns column s into bases in wave
+    // order, carrying the segment's running count (s_cnt[s]) across chunks.
+    auto pass4t = [&](int c, int key, uint64_t peers) {
+      const int i = c * nthr + tid;
+      const bool valid = i < n;
+      const int local = __popcll(peers & lanemask_lt());
+      const int seg = -s_first[key] - 1;
+      if (valid && local == 0) s_wcnt[wave * kFastSegs + seg] = __popcll(peers);
+      lgkm_barrier();
+      if (tid < S) {
+        // the column's reads first, then its writes (no LDS round trip per wave)
+        int v[kThreads / kWave];
+#pragma unroll
+        for (int w = 0; w < kThreads / kWave; ++w)
+          v[w] = w < nwaves ? s_wcnt[w * kFastSegs + tid] : 0;
+        int run = s_cnt[tid];
+#pragma unroll
+        for (int w = 0; w < kThreads / kWave; ++w) {
+          if (w < nwaves) {
+            s_wcnt[w * kFastSegs + tid] = 0;
+            s_wbase[w * kFastSegs + tid] = run;
+          }
+          run += v[w];
+        }
+        s_cnt[tid] = run;
+      }
+      lgkm_barrier();
+      if (valid) {
+        a.token_indices[s_off[seg] + s_wbase[wave * kFastSegs + seg] + local] = i;
+        a.row_segment[i] = seg;
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c)
+      if (c < nchunks) pass4t(c, keyreg[c], peersreg[c]);
+    walk(key_at, [&](int c, int key) { pass4t(c, key, match_key(key, c * nthr + tid < n)); });
+  } else {
+    // Wave 0 walks the waves' group leaders in order, so the cross-wave
+    // part follows row order exactly.
+    auto pass4 = [&](int c, int key, uint64_t peers) {
+      const int i = c * nthr + tid;
+      const bool valid = i < n;
+      const int local = __popcll(peers & lanemask_lt());
+      s_lead_cnt[tid] = (valid && local == 0) ? __popcll(peers) : 0;
+      s_lead_key[tid] = key;
+      lgkm_barrier();
+      if (wave == 0) {
+        // waves past the last row of the chunk hold no leaders
+        const int wend = min(nwaves, (n - c * nthr + kWave - 1) / kWave);
+        for (int w = 0; w < wend; ++w) {
+          const int u = w * kWave + lane;
+          const int cnt = s_lead_cnt[u];
+          if (cnt > 0) {
+            const int k = s_lead_key[u];
+            const int b = s_cnt[k];
+            s_cnt[k] = b + cnt;
+            s_lead_base[u] = b;
+          }
         }
       }
-    }
-    __syncthreads();
-    if (valid) {
-      const int seg = -s_first[key] - 1;
-      const int lt = wave * kWave + (__ffsll((unsigned long long)peers) - 1);
-      const int pos = s_off[seg] + s_lead_base[lt] + local;
-      a.token_indices[pos] = i;
-      a.row_segment[i] = seg;
-    }
-    __syncthreads();
-  };
+      lgkm_barrier();
+      if (valid) {
+        const int seg = -s_first[key] - 1;
+        const int lt = wave * kWave + (__ffsll((unsigned long long)peers) - 1);
+        const int pos = s_off[seg] + s_lead_base[lt] + local;
+        a.token_indices[pos] = i;
+        a.row_segment[i] = seg;
+      }
+      lgkm_barrier();
+    };
 #pragma unroll
-  for (int c = 0; c < kRegChunks; ++c)
-    if (c < nchunks) pass4(c, keyreg[c], peersreg[c]);
-  for (int c = kRegChunks; c < nchunks; ++c) {
-    const int i = c * nthr + tid;
-    const int key = i < n ? a.row_segment[i] : 0;
-    pass4(c, key, match_key(key, i < n));
+    for (int c = 0; c < kRegChunks; ++c)
+      if (c < nchunks) pass4(c, keyreg[c], peersreg[c]);
+    walk(key_at, [&](int c, int key) { pass4(c, key, match_key(key, c * nthr + tid < n)); });
   }
 
   if (tid == 0) {
@@ -266,7 +386,7 @@ namespace {
 
 __global__ __launch_bounds__(kThreads) void build_segments_kernel(BuildArgs a) {
   extern __shared__ int lds[];
-  build_segments_block(a, lds);
+  build_segments_block(a, lds, true);
 }
 
 // ----------------------------------------------------------------------------
@@ -291,7 +411,7 @@ __global__ __launch_bounds__(kBSThreads) void build_shrink_kernel(BuildArgs a, c
                                                                   int nkb, float *H) {
   extern __shared__ int lds[];
   if (blockIdx.x == 0) {
-    build_segments_block(a, lds);
+    build_segments_block(a, lds, false);
     return;
   }
   const int b = blockIdx.x - 1;
@@ -350,7 +470,7 @@ hipError_t launch_build_shrink(const BuildArgs &a, const void *X, int64_t ldx,
   const int nrb = (a.n + kRowBlk - 1) / kRowBlk;
   const long blocks = 1 + (long)pool.n_slots * nkb * nrb;
   if (blocks > 16384) return hipErrorNotSupported;
-  const int words_build = build_lds_words(a.n_slots, kBSThreads);
+  const int words_build = build_lds_words(a.n_slots, kBSThreads, a.n, false);
   const int words_shrink = kShW * kShNP + kShW + a.n;
   const size_t lds = (size_t)(words_build > words_shrink ? words_build : words_shrink) * 4;
   if (pool.dtype == 1)
@@ -375,7 +495,7 @@ hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, in
   // one wave per 64 rows up to 16 waves
   int threads = ((n + kWave - 1) / kWave) * kWave;
   threads = threads < kWave ? kWave : (threads > kThreads ? kThreads : threads);
-  const size_t lds = (size_t)build_lds_words(n_slots, threads) * 4;
+  const size_t lds = (size_t)build_lds_words(n_slots, threads, n, true) * 4;
   hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(threads), lds, stream, a);
   return hipGetLastError();
 }

@@ -58,10 +58,6 @@ struct BuildArgs {
   int32_t *num_segments, *status;
 };
 
-// LDS words the segment build needs for a pool of n_slots and a workgroup
-// of nthr threads.
-int build_lds_words(int n_slots, int nthr);
-
 hipError_t launch_build_segments(const int32_t *row_slot, int n, int n_slots, int r_max,
                                  const int32_t *slot_rank, const float *slot_scale,
                                  int32_t *token_indices, int32_t *row_segment, int32_t *seg_off,
