@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
 // ----------------------------------------------------------------------------
 constexpr int kLongRows = 128;   // segments at least this long take the MFMA path
 constexpr int kMfmaShrinkMinBatch = 2048;
+constexpr int kMfmaShrinkFillTiles = 256;   // 64 x 64 work items that fill the CUs
 constexpr int kSStages = 6;   // ring buffers = waves of the workgroup
 
 template <int SM, int SN>
@@ -751,9 +752,19 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
                        pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
                        long_min, H);
   }
-  // (32 x 32 tiles, one wave each, measured slower at d_in 8192: 61 against
-  // about 50 us, too few bytes in flight per CU)
-  if (use_mfma) launch_shrink_mfma<64, 64>(X, ldx, seg, pool, H, stream);
+  // 64 x 64 tiles when their work items fill the CUs; 32 x 32 tiles (one
+  // MFMA wave each, four times the workgroups) when they would not, as for a
+  // few long requests in a batch of a few thousand rows, where each of the
+  // few 64 x 64 workgroups streams megabytes of X and A alone.  (On batches
+  // that do fill the CUs the small tiles measured slower, 61 against about
+  // 50 us at d_in 8192: too few bytes in flight per CU.)
+  if (use_mfma) {
+    const int tiles64 = ((n + 63) / 64) * ((pool.r_max + 63) / 64);
+    if (tiles64 < kMfmaShrinkFillTiles)
+      launch_shrink_mfma<32, 32>(X, ldx, seg, pool, H, stream);
+    else
+      launch_shrink_mfma<64, 64>(X, ldx, seg, pool, H, stream);
+  }
   return hipGetLastError();
 }
 
