@@ -784,7 +784,9 @@ def skewed_entry(args):
             "path": best, "tokens_s": round(w4.n / m4["step"][best][0], 1),
             "step_us_by_path": {p: round(v[0] * 1e6, 3) for p, v in m4["step"].items()},
             "us": {k: round(v * 1e6, 3) for k, v in pk.items()},
-            "fused_gemm": roofline_for("fused", f4, pk["fused"], "bf16"),
+            # counters were taken with the exact policy
+            "fused_gemm": dict(roofline_for("fused", f4, pk["fused"], "bf16"),
+                               traffic=measured_traffic(4, "fused") if pol == "exact" else None),
             "shrink_expand": {"GB_s": round(se / (pk["shrink"] + pk["expand"]) / 1e9, 1),
                               "hbm_frac": round(se / (pk["shrink"] + pk["expand"]) / 1e9 /
                                                 HBM_PEAK_GBS, 4)}}
