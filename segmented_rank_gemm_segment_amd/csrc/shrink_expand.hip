@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kShW * kWave, 3) void shrink_kernel(
 constexpr int kLongRows = 128;   // segments at least this long take the MFMA path
 constexpr int kMfmaShrinkMinBatch = 2048;
 constexpr int kMfmaShrinkFillTiles = 256;   // 64 x 64 work items that fill the CUs
+constexpr int kShortRowBlk = 8;             // rows per GEMV item beside the MFMA kernel
 constexpr int kSStages = 6;   // ring buffers = waves of the workgroup
 
 template <int SM, int SN>
@@ -734,7 +735,13 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
   // after its metadata read).  With the MFMA kernel on the long segments, the
   // GEMV kernel walks the first blocks of every segment (nb of them below
   // kLongRows rows) instead of the position blocks.
-  const int nb_g = use_mfma ? (kLongRows + rb - 1) / rb : nb;
+  // The short segments of such a batch (decode rows beside prefill requests)
+  // go in blocks of kShortRowBlk rows, so that the row groups of one segment
+  // run in separate workgroups instead of one after another (each group
+  // reads the adapter's rank rows over all of d_in, tens of KB per rank
+  // block at d_in 8192 and more).
+  const int rb_g = use_mfma ? kShortRowBlk : rb;
+  const int nb_g = use_mfma ? (kLongRows + rb_g - 1) / rb_g : nb;
   const int items = use_mfma ? nb_g * S_bound : nb + S_bound;
   const int gx = (pool.r_max + kShRB - 1) / kShRB;
   dim3 grid(gx, grid_items(items, gx));
@@ -743,13 +750,13 @@ hipError_t launch_shrink(const void *X, int64_t ldx, const SegView &seg, const P
     hipLaunchKernelGGL((shrink_kernel<bf16_t>), grid, block, 0, stream,
                        (const bf16_t *)X, ldx, (const bf16_t *)pool.A, seg.token_indices,
                        seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
-                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
+                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb_g, nb_g, S_bound,
                        long_min, H);
   } else {
     hipLaunchKernelGGL((shrink_kernel<float>), grid, block, 0, stream,
                        (const float *)X, ldx, (const float *)pool.A, seg.token_indices,
                        seg.row_segment, seg.seg_off, seg.seg_slot, seg.seg_rank, seg.num_segments,
-                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb, nb_g, S_bound,
+                       pool.r_max, pool.proj.rs, pool.d_in, pool.policy, rb_g, nb_g, S_bound,
                        long_min, H);
   }
   // 64 x 64 tiles when their work items fill the CUs; 32 x 32 tiles (one
