@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 7
+#define LORA_ABI_VERSION 8
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 /* Limits of the allocation-free call lora_linear_fused_static: token rows,
@@ -405,6 +405,25 @@ lora_status lora_linear_fused_fp8w(const void *X, int64_t ldx, const void *Wq, i
 lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
                              int64_t ldw, const lora_pool *pool, const lora_segments *seg,
                              float *H, void *Y, int64_t ldy, void *sync, void *stream);
+
+/*
+ * lora_layer_fused with the base weight as FP8 E4M3 codes and one float32
+ * scale per output row, as in lora_linear_fused_fp8w (quantized base with a
+ * bf16 LoRA path, LoRA/QLoRA 多租户GPU推理服务化实战 section 1.2: the low-rank
+ * term of the unquantized activations is added to the quantized base
+ * product).  Wq uint8 [d_out][ldw] (ldw % 16 == 0, d_in % 16 == 0),
+ * w_scale device float32 [d_out]; bf16 pools only (LORA_ERR_DTYPE
+ * otherwise).  Metadata and H as lora_layer_fused writes them; Y as
+ * lora_linear_fused_fp8w computes it, with one rounding (rows of base-only
+ * and rank-0 segments equal lora_base_gemm_fp8w's output bit for bit).
+ * One launch for 1 <= n <= LORA_LAYER_ONE_LAUNCH_ROWS, else
+ * lora_build_shrink followed by lora_linear_fused_fp8w; sync and errors as
+ * lora_layer_fused.
+ */
+lora_status lora_layer_fused_fp8w(const int32_t *row_slot, const void *X, int64_t ldx,
+                                  const void *Wq, int64_t ldw, const float *w_scale,
+                                  const lora_pool *pool, const lora_segments *seg, float *H,
+                                  void *Y, int64_t ldy, void *sync, void *stream);
 
 /*
  * The whole layer with no workspace arguments, for callers that cannot

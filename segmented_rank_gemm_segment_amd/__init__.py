@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 7
+ABI_VERSION = 8
 STATIC_MAX_ROWS = 32768
 STATIC_MAX_H = 1 << 21
 LAYER_ONE_LAUNCH_ROWS = 512
@@ -98,6 +98,7 @@ EXPORTS = (
     "lora_linear_fused_fp8w",
     "lora_linear_fused_static",
     "lora_layer_fused",
+    "lora_layer_fused_fp8w",
 )
 
 
@@ -144,6 +145,8 @@ def lib() -> ctypes.CDLL:
     L.lora_linear_fused_static.argtypes = [vp, vp, i64, vp, i64, PP, i32, vp, i64, vp]
     L.lora_layer_fused.restype = i32
     L.lora_layer_fused.argtypes = [vp, vp, i64, vp, i64, PP, SP, vp, vp, i64, vp, vp]
+    L.lora_layer_fused_fp8w.restype = i32
+    L.lora_layer_fused_fp8w.argtypes = [vp, vp, i64, vp, i64, vp, PP, SP, vp, vp, i64, vp, vp]
     if L.lora_abi_version() != ABI_VERSION:
         raise RuntimeError("liblora ABI version mismatch")
     _lib = L
@@ -520,6 +523,33 @@ def lora_layer_fused(row_slot: torch.Tensor, X: torch.Tensor, W: torch.Tensor, p
         raise ValueError("sync: a contiguous buffer of LAYER_SYNC_BYTES bytes (layer_sync())")
     _check(lib().lora_layer_fused(_ptr(row_slot), _ptr(X), _ld(X), _ptr(W), _ld(W), pool.c, seg.c,
                                   _ptr(H), _ptr(Y), _ld(Y), _ptr(sync), _stream(stream)))
+
+
+def lora_layer_fused_fp8w(row_slot: torch.Tensor, X: torch.Tensor, Wq: torch.Tensor,
+                          w_scale: torch.Tensor, pool: Pool, seg: Segments, H: torch.Tensor,
+                          Y: torch.Tensor, sync: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """lora_layer_fused with the FP8 E4M3 base weight (Wq uint8 codes
+    [d_out, d_in], w_scale float32 [d_out])."""
+    if row_slot.dtype != torch.int32 or (row_slot.numel() and not row_slot.is_contiguous()):
+        raise ValueError("row_slot: contiguous int32")
+    if row_slot.numel() != seg.n_rows:
+        raise ValueError("row_slot length != seg.n_rows")
+    if not (X.dtype == Y.dtype == pool.dtype == torch.bfloat16):
+        raise ValueError("X and Y must be bf16, as the pool")
+    if Wq.dtype != torch.uint8 or w_scale.dtype != torch.float32 or not w_scale.is_contiguous():
+        raise ValueError("Wq uint8 E4M3 codes, w_scale contiguous float32")
+    if X.shape[0] != seg.n_rows or tuple(Wq.shape) != (pool.d_out, pool.d_in) \
+            or tuple(Y.shape) != (seg.n_rows, pool.d_out) or w_scale.numel() != pool.d_out:
+        raise ValueError("shapes: X [n, d_in], Wq [d_out, d_in], w_scale [d_out], Y [n, d_out]")
+    if H.dtype != torch.float32 or tuple(H.shape) != (seg.n_rows, pool.r_max) or not H.is_contiguous():
+        raise ValueError("H: contiguous float32 [n_rows, r_max]")
+    if sync is not None and (sync.numel() * sync.element_size() < LAYER_SYNC_BYTES
+                             or not sync.is_contiguous()):
+        raise ValueError("sync: a contiguous buffer of LAYER_SYNC_BYTES bytes (layer_sync())")
+    _check(lib().lora_layer_fused_fp8w(_ptr(row_slot), _ptr(X), _ld(X), _ptr(Wq), _ld(Wq),
+                                       _ptr(w_scale), pool.c, seg.c, _ptr(H), _ptr(Y), _ld(Y),
+                                       _ptr(sync), _stream(stream)))
 
 
 def lora_base_gemm_fp8w(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, Y: torch.Tensor,

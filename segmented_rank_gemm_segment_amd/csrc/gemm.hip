@@ -409,7 +409,7 @@ template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG, int LORA, 
           bool WF8, bool LAYER = false>
 __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES, KG, WF8 ? 1 : 2>;
-  static_assert(!LAYER || (KG > 1 && LORA == 1 && !WF8 && WM * WN * KG * kWave == kLayerThreads),
+  static_assert(!LAYER || (KG > 1 && LORA == 1 && WM * WN * KG * kWave == kLayerThreads),
                 "the one-launch layer runs on the small tiles");
   static_assert(!LAYER || C::LDS >= (4 * 4095 + 2) * 4, "the build's tables fit in the ring");
   // LDS: the stage ring, or the fused LoRA epilogue of large tiles if larger:
@@ -1410,16 +1410,16 @@ hipError_t launch_fp8w(const GemmArgs &g, bool lora, hipStream_t stream) {
 
 // The one-launch layer on small tiles: one workgroup per tile, and at least
 // one per row (workgroups past the tiles only do their row).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
+template <bool WF8, int BM, int BN, int WM, int WN, int BK, int STAGES, int KG>
 hipError_t launch_layer_t(const GemmArgs &g, hipStream_t stream) {
   const int tiles = tile_grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN);
   dim3 grid(tiles > g.M ? tiles : g.M);
   dim3 block(WM * WN * KG * kWave);
   if (g.dora)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true, false, true>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, true, WF8, true>),
                        grid, block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false, false, true>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, STAGES, KG, 1, false, WF8, true>),
                        grid, block, 0, stream, g);
   return hipGetLastError();
 }
@@ -1532,12 +1532,13 @@ hipError_t launch_gemm(const void *X, int64_t ldx, const void *W, int64_t ldw, v
 }
 
 hipError_t launch_layer(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
-                         int64_t ldy, int M, const PoolView &pool, const LayerArgs &lay,
-                         hipStream_t stream) {
+                        int64_t ldy, int M, const PoolView &pool, const LayerArgs &lay,
+                        hipStream_t stream, const float *wscale) {
   if (pool.dtype != 1 || M < 1 || M > kLayerMaxRows) return hipErrorNotSupported;
   const int K = pool.d_in, N = pool.d_out;
   GemmArgs g{(const bf16_t *)X, ldx, (const bf16_t *)W, ldw, (bf16_t *)Y, ldy, M, K, N,
              lay.H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
+  g.wscale = wscale;
   g.proj = pool.proj;
   g.Bt = (const bf16_t *)pool.Bt;
   g.Bn = (const bf16_t *)pool.B;
@@ -1547,8 +1548,11 @@ hipError_t launch_layer(const void *X, int64_t ldx, const void *W, int64_t ldw, 
   g.lay = lay;
   using S = TileCfg<LORA_GEMM_SMALL>;
   const int64_t tiles = (int64_t)((M + S::kBM - 1) / S::kBM) * ((N + S::kBN - 1) / S::kBN);
-  if (tiles > kCUs) return launch_layer_t<LORA_GEMM_SMALL_WIDE>(g, stream);
-  return launch_layer_t<LORA_GEMM_SMALL>(g, stream);
+  // FP8 weights: the four-stage ring only (the two-stage ring of codes is
+  // too small to hold a large pool's build tables)
+  if (wscale) return launch_layer_t<true, LORA_GEMM_SMALL_F8>(g, stream);
+  if (tiles > kCUs) return launch_layer_t<false, LORA_GEMM_SMALL_WIDE>(g, stream);
+  return launch_layer_t<false, LORA_GEMM_SMALL>(g, stream);
 }
 
 }  // namespace lora

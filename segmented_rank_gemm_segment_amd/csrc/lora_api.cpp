@@ -346,18 +346,24 @@ lora_status lora_linear_fused(const void *X, int64_t ldx, const void *W, int64_t
                                       static_cast<hipStream_t>(stream)));
 }
 
-lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
-                             int64_t ldw, const lora_pool *pool, const lora_segments *seg,
-                             float *H, void *Y, int64_t ldy, void *sync, void *stream) {
+namespace {
+
+// Both layer calls: W is bf16 (wscale NULL) or FP8 E4M3 codes with row scales.
+lora_status layer_call(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
+                       int64_t ldw, const float *wscale, const lora_pool *pool,
+                       const lora_segments *seg, float *H, void *Y, int64_t ldy, void *sync,
+                       void *stream) {
   lora_status st = check_pool(pool);
   if (st != LORA_OK) return st;
+  if (wscale && pool->dtype != LORA_BF16) return LORA_ERR_DTYPE;
   st = check_segments(seg, pool);
   if (st != LORA_OK) return st;
   const int32_t n = seg->n_rows;
   if (n > 0 && !row_slot) return LORA_ERR_NULL;
   st = check_matrix(X, ldx, pool->d_in, n);
   if (st != LORA_OK) return st;
-  st = check_matrix(W, ldw, pool->d_in, pool->d_out);
+  st = wscale ? check_fp8_weight(W, ldw, wscale, pool->d_in, pool->d_out)
+              : check_matrix(W, ldw, pool->d_in, pool->d_out);
   if (st != LORA_OK) return st;
   st = check_matrix(Y, ldy, pool->d_out, n);
   if (st != LORA_OK) return st;
@@ -389,13 +395,30 @@ lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx
                             seg->segment_scales,
                             seg->num_segments,
                             seg->status};
-  const hipError_t e = lora::launch_layer(X, ldx, W, ldw, Y, ldy, n, pv, lay, s);
+  const hipError_t e = lora::launch_layer(X, ldx, W, ldw, Y, ldy, n, pv, lay, s, wscale);
   if (e != hipErrorNotSupported) return hip_status(e);
   // outside the one-launch case: the two calls
   (void)hipGetLastError();
   st = lora_build_shrink(row_slot, X, ldx, pool, seg, H, stream);
   if (st != LORA_OK) return st;
-  return lora_linear_fused(X, ldx, W, ldw, H, seg, pool, Y, ldy, stream);
+  return wscale ? lora_linear_fused_fp8w(X, ldx, W, ldw, wscale, H, seg, pool, Y, ldy, stream)
+                : lora_linear_fused(X, ldx, W, ldw, H, seg, pool, Y, ldy, stream);
+}
+
+}  // namespace
+
+lora_status lora_layer_fused(const int32_t *row_slot, const void *X, int64_t ldx, const void *W,
+                             int64_t ldw, const lora_pool *pool, const lora_segments *seg,
+                             float *H, void *Y, int64_t ldy, void *sync, void *stream) {
+  return layer_call(row_slot, X, ldx, W, ldw, nullptr, pool, seg, H, Y, ldy, sync, stream);
+}
+
+lora_status lora_layer_fused_fp8w(const int32_t *row_slot, const void *X, int64_t ldx,
+                                  const void *Wq, int64_t ldw, const float *w_scale,
+                                  const lora_pool *pool, const lora_segments *seg, float *H,
+                                  void *Y, int64_t ldy, void *sync, void *stream) {
+  if (!w_scale) return LORA_ERR_NULL;
+  return layer_call(row_slot, X, ldx, Wq, ldw, w_scale, pool, seg, H, Y, ldy, sync, stream);
 }
 
 lora_status lora_linear_fused_static(const int32_t *row_slot, const void *X, int64_t ldx,

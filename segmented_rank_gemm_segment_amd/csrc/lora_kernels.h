@@ -124,9 +124,11 @@ struct LayerArgs {
 
 // The whole layer in one launch (segment metadata, H, Y) for bf16 pools and
 // 1 <= M <= 512 rows; hipErrorNotSupported (nothing launched) otherwise.
+// With wscale, W holds FP8 E4M3 codes and row j of the weight is wscale[j]
+// times its codes.
 hipError_t launch_layer(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
                         int64_t ldy, int M, const PoolView &pool, const LayerArgs &lay,
-                        hipStream_t stream);
+                        hipStream_t stream, const float *wscale = nullptr);
 
 // Device scratch of the allocation-free call lora_linear_fused_static: byte
 // offsets of its parts, each 256-byte aligned.  H is float [n][r_max]; the

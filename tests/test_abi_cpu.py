@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
               "lora_base_gemm", "lora_pool_pack_slot", "lora_pool_dora_prepare", "lora_build_shrink",
               "lora_base_gemm_fp8w", "lora_linear_fused_fp8w", "lora_status_str",
               "lora_abi_version", "lora_linear_fused_static", "lora_pool_set_scales",
-              "lora_pool_write_b", "lora_layer_fused"):
+              "lora_pool_write_b", "lora_layer_fused", "lora_layer_fused_fp8w"):
         assert n in names
     assert set(names) == set(srg.EXPORTS)
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 7
+    assert L.lora_abi_version() == srg.ABI_VERSION == 8
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"
@@ -364,3 +364,19 @@ def test_layer_call_validation(L):
     assert f(rs, X, 64, W, 64, p, ctypes.byref(segs(max_segments=4)), H, Y, 32, SY, None) == ECAP
     assert srg.LAYER_SYNC_BYTES == 4096 and srg.LAYER_ONE_LAUNCH_ROWS == 512
 
+
+
+def test_fp8_layer_call_validation(L):
+    """The FP8-weight layer call checks the same arguments, the weight's
+    scales and code layout, and bf16 pools only, before any launch."""
+    f = L.lora_layer_fused_fp8w
+    rs, X, Wq, WS, H, Y, SY = (P + 0xC000, P + 0xD000, P + 0xE000, P + 0x12000, P + 0xF000,
+                               P + 0x10000, P + 0x11000)
+    p, sg = ctypes.byref(pool()), ctypes.byref(segs())
+    assert f(rs, X, 64, Wq, 64, None, p, sg, H, Y, 32, SY, None) == ENULL     # no scales
+    assert f(rs, X, 64, None, 64, WS, p, sg, H, Y, 32, SY, None) == ENULL
+    assert f(None, X, 64, Wq, 64, WS, p, sg, H, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, Wq, 64, WS, p, sg, None, Y, 32, SY, None) == ENULL
+    assert f(rs, X, 64, Wq, 60, WS, p, sg, H, Y, 32, SY, None) != 0          # ldw < d_in
+    assert f(rs, X, 64, Wq, 64, WS, p, sg, H, Y, 32, SY + 4, None) == EALIGN
+    assert f(rs, X, 64, Wq, 64, WS, ctypes.byref(pool(dtype=0)), sg, H, Y, 32, SY, None) == EDTYPE
