@@ -452,10 +452,11 @@ inline int grid_items(int items, int x) {
 }
 
 // ----------------------------------------------------------------------------
-// Expand of large bf16 batches (at least kMfmaShrinkMinBatch rows) whose pool
-// keeps B d_out-major: per work item (at most kRowBlk rows of one segment,
-// the items of the GEMV expand) and 256 output columns, the increment is a
-// product over the rank, taken on the matrix cores in the orientation
+// Expand of bf16 batches whose pool keeps B d_out-major (the batches are
+// chosen by expand_on_mfma): per work item (at most kRowBlk rows of one
+// segment: position blocks of kRowBlk rows and segment heads, as the GEMV
+// expand cuts its items) and 256 output columns, the increment is a product
+// over the rank, taken on the matrix cores in the orientation
 // D^T = B_a (columns x ranks) (s_a H)^T (ranks x rows), with the item's Y as
 // the accumulator's initial value: D = Y + s_a H B_a^T in fp32, times the
 // DoRA factor, rounded once.  s_a H is fp32, so each value enters as a bf16
@@ -555,6 +556,8 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
   u32x4 ly[kRowBlk / 8];
   float4 lh[4];
   int lnxt;
+  // (the loads are unconditional: rows past the item's end repeat its last
+  // row; skipping them by branches measured heavy register spills)
   auto load_rows = [&](int k) __attribute__((always_inline)) {
     const int cq = k & 1;
 #pragma unroll
@@ -586,6 +589,11 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
         const int kc = min(ks * 16 + hf * 8, rs - 8);
         bv[ks][j] = *reinterpret_cast<const u32x4 *>(bs + (int64_t)n * r_max + kc);
       }
+    // the 32-row blocks holding the item's rows: only those are computed,
+    // and only the item's 8-row groups enter and leave the tile (tile rows
+    // past its end keep stale values, which reach only accumulator rows that
+    // are never stored: each output row depends on its own H and Y rows)
+    const int nmb = nrow > 32 ? 2 : 1;
     {
       const float hv[16] = {lh[0].x, lh[0].y, lh[0].z, lh[0].w, lh[1].x, lh[1].y, lh[1].z, lh[1].w,
                             lh[2].x, lh[2].y, lh[2].z, lh[2].w, lh[3].x, lh[3].y, lh[3].z, lh[3].w};
@@ -608,7 +616,8 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < kRowBlk / 8; ++i) {
       const int row = yr + 8 * i;
-      *reinterpret_cast<u32x4 *>(s_y + row * kXmRowBytes + xm_chunk(row, yc) * 16) = ly[i];
+      if (8 * i < nrow)
+        *reinterpret_cast<u32x4 *>(s_y + row * kXmRowBytes + xm_chunk(row, yc) * 16) = ly[i];
     }
     if (tid < kRowBlk) s_rows[cur ^ 1][tid] = lnxt;
     __syncthreads();
@@ -647,6 +656,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
+        if (mb >= nmb) break;
         const int off = (l32 + 32 * mb) * kXmPitch + k0 * 2;
         const mfma_bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_h[0] + off));
         const mfma_bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4 *>(s_h[1] + off));
@@ -671,6 +681,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
+          if (mb >= nmb) break;
           const int m = l32 + 32 * mb;
           float o[4];
 #pragma unroll
@@ -690,6 +701,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < kRowBlk / 8; ++i) {
       const int row = yr + 8 * i;
+      if (8 * i >= nrow) break;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(s_y + row * kXmRowBytes + xm_chunk(row, yc) * 16);
       if (row < nrow && c0 + yc * 8 < d_out)
         *reinterpret_cast<u32x4 *>(Y + (int64_t)s_rows[cur][row] * ldy + c0 + yc * 8) = v;
@@ -806,13 +818,25 @@ void launch_expand_r(const float *H, const SegView &seg, const PoolView &pool, v
   }
 }
 
-// The MFMA expand takes large bf16 batches of pools with the d_out-major B
-// whose projections each start at a multiple of its 256-column blocks.
-inline bool expand_on_mfma(int n, const PoolView &pool) {
-  if (pool.dtype != 1 || !pool.B || n < kMfmaShrinkMinBatch) return false;
+// The MFMA expand takes bf16 pools with the d_out-major B whose projections
+// each start at a multiple of its 256-column blocks, for the batches where it
+// beats the GEMV expand.  Its cost per work item hardly depends on the rank
+// (a 64-row Y tile per item), while the GEMV expand's grows with the rank
+// rows each item reads (d = 4096, uniform slots, us MFMA / GEMV: rank 16
+// from 256 to 4096 rows 16 / 7 ... 46 / 40; rank 32 at 512 rows 19 / 15, at
+// 1024 rows 20 / 24; rank 64 at 512 rows 25 / 35, at 2048 rows 42 / 90;
+// rank 16 with segments of tens of rows at 2048 rows 12 / 35).  So: ranks of
+// 32 and more once rank x rows reaches kXmMinRankRows, or segments of at
+// least kXmMinSegRows rows on average (the segment bound taken as the count).
+constexpr int kXmMinRankRows = 32768;
+constexpr int kXmMinSegRows = 16;
+inline bool expand_on_mfma(int n, int S_bound, const PoolView &pool) {
+  if (pool.dtype != 1 || !pool.B || n == 0) return false;
   for (int q = 1; q < pool.proj.n_proj; ++q)
     if (pool.proj.col_off[q] % kXmCols) return false;
-  return true;
+  const int rs = pool.proj.rs;
+  if (rs >= 32 && (int64_t)rs * n >= kXmMinRankRows) return true;
+  return n >= (int64_t)kXmMinSegRows * std::max(S_bound, 1);
 }
 
 hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &pool, void *Y,
@@ -821,24 +845,25 @@ hipError_t launch_expand(const float *H, const SegView &seg, const PoolView &poo
   const int rb = row_block(n);
   const int nb = (n + rb - 1) / rb;
   const int S_bound = seg_bound(n, pool.n_slots, seg.max_segments);
-  if (expand_on_mfma(n, pool)) {
-    // rb = kRowBlk here (n >= kLargeBatch)
+  if (expand_on_mfma(n, S_bound, pool)) {
+    // items of kRowBlk rows whatever the batch size
     // at most kXmItems items per workgroup (its metadata table)
+    const int nbx = (n + kRowBlk - 1) / kRowBlk;
     const int gx = (pool.d_out + kXmCols - 1) / kXmCols;
-    const int items = nb + S_bound;
+    const int items = nbx + S_bound;
     const int gy = std::max(grid_items(items, gx), (items + kXmItems - 1) / kXmItems);
     const dim3 grid(gx, gy);
     if (pool.dora)
       hipLaunchKernelGGL(expand_mfma_kernel<true>, grid, dim3(4 * kWave), 0, stream, H,
                          (const bf16_t *)pool.B, pool.dora, seg.token_indices, seg.row_segment,
                          seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
-                         pool.r_max, pool.d_out, pool.policy, nb, S_bound, (bf16_t *)Y, ldy,
+                         pool.r_max, pool.d_out, pool.policy, nbx, S_bound, (bf16_t *)Y, ldy,
                          pool.proj);
     else
       hipLaunchKernelGGL(expand_mfma_kernel<false>, grid, dim3(4 * kWave), 0, stream, H,
                          (const bf16_t *)pool.B, nullptr, seg.token_indices, seg.row_segment,
                          seg.seg_off, seg.seg_slot, seg.seg_rank, seg.seg_scale, seg.num_segments,
-                         pool.r_max, pool.d_out, pool.policy, nb, S_bound, (bf16_t *)Y, ldy,
+                         pool.r_max, pool.d_out, pool.policy, nbx, S_bound, (bf16_t *)Y, ldy,
                          pool.proj);
     return hipGetLastError();
   }

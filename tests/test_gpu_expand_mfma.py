@@ -1,6 +1,7 @@
-"""GPU parity of the matrix-core expand: large bf16 batches whose pool keeps B
-d_out-major (adapter-batching page, section "Segmented Kernel 需要哪些
-Metadata": Delta Y_a = s_a H_a B_a^T added back to the rows of segment a).
+"""GPU parity of the matrix-core expand: bf16 batches whose pool keeps B
+d_out-major, large ones and decode-sized ones of rank 32 and more
+(adapter-batching page, section "Segmented Kernel 需要哪些 Metadata":
+Delta Y_a = s_a H_a B_a^T added back to the rows of segment a).
 
 The increment alone (the expand onto Y = 0) is checked element by element
 against the oracle's float64 Delta Y: the kernel rounds once to bf16 (at most
@@ -111,6 +112,11 @@ CASES = [
     (803, 2304, 128, 264, 40, 16, 0.2, False),    # many short segments, rank-16 pool
     (804, 2500, 136, 776, 5, 8, 0.1, True),       # r_max 8: half of each K step masked
     (805, 4100, 64, 2056, 300, 64, 0.3, False),   # 300 slots, mostly single-row items
+    # decode-sized batches that take the matrix-core expand by their rank
+    # (rank >= 32 and rank x rows >= 32768), with items of each length class:
+    (806, 700, 128, 776, 20, 64, 0.0, True),      # request runs: 64-row and partial items
+    (807, 1100, 128, 520, 60, 32, 0.1, False),    # about 16 rows per segment: 9..32-row items
+    (808, 600, 256, 1000, 200, 64, 0.2, False),   # 1..8-row items, ragged column block
 ]
 
 
