@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 8
+#define LORA_ABI_VERSION 9
 /* Largest pool: the segment builder keeps per-slot tables in LDS. */
 #define LORA_MAX_SLOTS 4095
 /* Limits of the allocation-free call lora_linear_fused_static: token rows,
@@ -90,12 +90,13 @@ typedef enum {
  * "Adapter的统一尺寸对齐": one preallocated buffer, uniform slot size, O(1)
  * lookup by slot offset).  Slot a holds, rank-major,
  *   A [n_slots][r_max][d_in]   row k = row k of A_a      (A_a in R^{r x d_in})
- *   Bt[n_slots][r_max][d_out]  row k = column k of B_a   (B_a in R^{d_out x r})
+ *   Bt[n_slots][rs][d_out]     row k = column k of B_a   (B_a in R^{d_out x r})
+ * with rs = r_max for a single projection (stacked pools below).
  * Rows k >= slot_rank[a] are padding and are never multiplied in.
  * slot_scale[a] is s_a = alpha_a / r_a (0 for a rank-0 slot), written by the
  * library (lora_pool_pack_slot, lora_pool_set_scales), never by the caller.
  * Optionally the pool also carries B in its own d_out-major layout,
- *   B [n_slots][d_out][r_max]  row j = row j of B_a   (the layout of the
+ *   B [n_slots][d_out][rs]     row j = row j of B_a   (the layout of the
  *                              adapter's up-projection weight),
  * the same values as Bt (written by lora_pool_pack_slot, or from Bt by
  * lora_pool_write_b).  lora_linear_fused then reads whole 16-byte runs of
@@ -122,8 +123,10 @@ typedef enum {
  * pool serves P projections of the same input at once: output columns
  * [proj_cols[q], proj_cols[q + 1]) are projection q's, and with
  * rs = r_max / P, rank rows [q rs, q rs + r) of a slot are projection q's A
- * rows; Bt rows [q rs, (q + 1) rs) are zero outside projection q's columns
- * (the d_out-major B likewise).  A slot's rank r (<= rs) and scale are
+ * rows, while the slot's rs rank rows of Bt hold in each column that
+ * column's own projection's B^T (every column belongs to one projection, so
+ * Bt and B take no more room than one projection's would: [n_slots][rs]
+ * [d_out] and [n_slots][d_out][rs]).  A slot's rank r (<= rs) and scale are
  * shared by its projections; H is [n][r_max] with projection q's ranks at
  * columns [q rs, q rs + r).  Every call then computes, for each projection,
  * exactly what it computes for a single one.  Requirements: proj_cols[0] =
@@ -134,16 +137,16 @@ typedef enum {
  */
 typedef struct {
   int32_t n_slots;           /* 1 .. LORA_MAX_SLOTS */
-  int32_t r_max;             /* 8, 16, 32 or 64 (times n_proj for stacked pools) */
+  int32_t r_max;             /* rs = 8, 16, 32 or 64 (times n_proj for stacked pools) */
   int32_t d_in;
   int32_t d_out;
   int32_t dtype;             /* lora_dtype */
   int32_t rank_policy;       /* lora_rank_policy */
   const void *A;             /* device */
-  const void *Bt;            /* device */
+  const void *Bt;            /* device, [n_slots][rs][d_out] */
   const int32_t *slot_rank;  /* device, [n_slots] */
   const float *slot_scale;   /* device, [n_slots] */
-  const void *B;             /* device, optional (NULL): [n_slots][d_out][r_max] */
+  const void *B;             /* device, optional (NULL): [n_slots][d_out][rs] */
   const float *dora_scale;   /* device, optional (NULL): fp32 [n_slots][d_out] DoRA g */
   int32_t n_proj;            /* 0 or 1: one projection; 2..8: stacked projections */
   const int32_t *proj_cols;  /* HOST, [n_proj + 1] column offsets (stacked pools only) */
@@ -261,9 +264,10 @@ typedef enum {
  *             or its transpose [rank][ldb[q]] (LORA_B_RANK_ROWS),
  * with d_out_q the projection's column count (d_out for a single projection).
  * Writes, per projection q with rs = r_max / P: A rank rows [q rs, q rs + rank)
- * and zeros up to (q + 1) rs; Bt rank rows [q rs, q rs + rank) = B_q^T in the
- * projection's columns and zeros elsewhere and past the rank; the pool's
- * d_out-major B when it has one, likewise; ones in the slot's dora_scale row
+ * and zeros up to (q + 1) rs; Bt rank rows [0, rank) = B_q^T in the
+ * projection's columns and zeros up to rs there (the other projections'
+ * columns are left as they are); the pool's d_out-major B when it has one,
+ * likewise; ones in the slot's dora_scale row
  * when the pool has that array (the new adapter starts as plain LoRA;
  * lora_pool_dora_prepare makes it DoRA).  Then, by a later kernel on the same
  * stream, slot_rank[slot] = rank and slot_scale[slot] = alpha / rank (the
@@ -299,7 +303,7 @@ lora_status lora_pool_set_scales(const lora_pool *pool, const double *slot_alpha
 
 /*
  * The pool's d_out-major copy of B from its Bt, for every slot:
- * B[a][j][k] = Bt[a][k][j] (adapter-batching page, "Adapter 不是一块连续
+ * B[a][j][k] = Bt[a][k][j], k < rs (adapter-batching page, "Adapter 不是一块连续
  * Weight": B_a in R^{d_out x r} is the adapter weight's own layout).  pool->B
  * must be non-NULL (LORA_ERR_NULL).  Asynchronous on `stream`; writes B only.
  */

@@ -30,7 +30,7 @@ LORA_F32, LORA_BF16 = 0, 1
 RANK_EXACT, RANK_TWO_BUCKETS, RANK_PADDED = 0, 1, 2
 RANK_POLICIES = {"exact": RANK_EXACT, "two_buckets": RANK_TWO_BUCKETS, "padded": RANK_PADDED}
 MAX_SLOTS = 4095
-ABI_VERSION = 8
+ABI_VERSION = 9
 STATIC_MAX_ROWS = 32768
 STATIC_MAX_H = 1 << 21
 LAYER_ONE_LAUNCH_ROWS = 512
@@ -189,25 +189,30 @@ def _ld(t: torch.Tensor) -> int:
 class Pool:
     """Fixed-slot adapter pool resident on the device.
 
-    ``A``  [n_slots, r_max, d_in]  and  ``Bt`` [n_slots, r_max, d_out]
-    (rank-major; row k of Bt[a] is column k of B_a), ``slot_rank`` int32
-    [n_slots] and ``slot_scale`` float32 [n_slots], which the library writes
-    from the slots' alphas (lora_pool_set_scales, lora_pool_pack_slot).
-    With ``natural_b`` (default) the pool also keeps B in its d_out-major
-    layout, ``B`` [n_slots, d_out, r_max], for the fused GEMM (written by
-    the library: lora_pool_write_b, lora_pool_pack_slot).  With ``dora`` it
+    ``A``  [n_slots, r_max, d_in]  and  ``Bt`` [n_slots, rs, d_out]
+    (rank-major; row k of Bt[a] is column k of B_a; rs = r_max for one
+    projection), ``slot_rank`` int32 [n_slots] and ``slot_scale`` float32
+    [n_slots], which the library writes from the slots' alphas
+    (lora_pool_set_scales, lora_pool_pack_slot).  With ``natural_b``
+    (default) the pool also keeps B in its d_out-major layout, ``B``
+    [n_slots, d_out, rs], for the fused GEMM (written by the library:
+    lora_pool_write_b, lora_pool_pack_slot).  With ``dora`` it
     keeps DoRA column factors ``dora_scale`` float32 [n_slots, d_out], all
     ones (plain LoRA) until ``dora_prepare`` sets a slot's.  A pool of
     stacked projections (``empty(..., proj_outs=...)``, ``stacked``) serves
     several projections of one input; its ``proj_cols`` are the host column
-    offsets.  torch only allocates here: every value is written by liblora.
+    offsets, A holds the P projections' rank rows (r_max = P rs) and Bt each
+    column's own projection in rs rank rows.  torch only allocates here:
+    every value is written by liblora.
     """
 
     def __init__(self, A: torch.Tensor, Bt: torch.Tensor, slot_rank: torch.Tensor,
                  slot_alpha, rank_policy: str = "exact", natural_b: bool = True,
                  dora: bool = False, proj_outs=None, stream=None):
-        if A.dim() != 3 or Bt.dim() != 3 or A.shape[:2] != Bt.shape[:2]:
-            raise ValueError("A [n_slots, r_max, d_in] and Bt [n_slots, r_max, d_out] expected")
+        P = len(proj_outs) if proj_outs is not None and len(proj_outs) >= 2 else 1
+        if A.dim() != 3 or Bt.dim() != 3 or A.shape[0] != Bt.shape[0] \
+                or A.shape[1] != P * Bt.shape[1]:
+            raise ValueError("A [n_slots, P rs, d_in] and Bt [n_slots, rs, d_out] expected")
         if A.dtype != Bt.dtype or not A.is_contiguous() or not Bt.is_contiguous():
             raise ValueError("A and Bt: same dtype, contiguous")
         dev = A.device
@@ -215,7 +220,7 @@ class Pool:
         self.n_slots, self.r_max, self.d_in = A.shape
         self.d_out = Bt.shape[2]
         self.dtype = A.dtype
-        self.B = (torch.empty((self.n_slots, self.d_out, self.r_max), dtype=A.dtype, device=dev)
+        self.B = (torch.empty((self.n_slots, self.d_out, Bt.shape[1]), dtype=A.dtype, device=dev)
                   if natural_b else None)
         self.dora_scale = (torch.ones((self.n_slots, self.d_out), dtype=torch.float32, device=dev)
                            if dora else None)
@@ -257,7 +262,7 @@ class Pool:
         if P > 1:
             d_out = sum(int(c) for c in proj_outs)
         A = torch.zeros((n_slots, P * r_max, d_in), dtype=dtype, device=device)
-        Bt = torch.zeros((n_slots, P * r_max, d_out), dtype=dtype, device=device)
+        Bt = torch.zeros((n_slots, r_max, d_out), dtype=dtype, device=device)
         rank = torch.zeros(n_slots, dtype=torch.int32, device=device)
         return cls(A, Bt, rank, 0.0, rank_policy, natural_b, dora,
                    proj_outs=proj_outs if P > 1 else None)

@@ -41,10 +41,11 @@ __global__ __launch_bounds__(kThreads) void dora_prepare_kernel(
   r = (r < 0 || r > proj.rs) ? 0 : r;
   const float sc = r > 0 ? slot_scale[slot] : 0.f;
   // the workgroup's output features belong to one projection (offsets are
-  // multiples of 8): its rank rows start at qoff
+  // multiples of 8): its A rows start at qoff in the slot; the slot's rs
+  // rank rows of Bt hold every column's own projection
   const int qoff = proj_of(proj, j0) * proj.rs;
   const T *a_slot = A + ((int64_t)slot * r_max + qoff) * d_in;
-  const T *bt_slot = Bt + ((int64_t)slot * r_max + qoff) * d_out;
+  const T *bt_slot = Bt + (int64_t)slot * proj.rs * d_out;
   // B_a[j0 + jj][k] for k < r (Bt row k is column k of B_a)
   for (int it = tid; it < kRows * 64; it += kThreads) {
     const int jj = it / 64, k = it - (it / 64) * 64;

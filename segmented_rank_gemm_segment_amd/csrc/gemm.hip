@@ -47,7 +47,7 @@ struct GemmArgs {
   // fused LoRA
   const float *H;
   const bf16_t *Bt;
-  const bf16_t *Bn;   // optional d_out-major copy of B ([slot][d_out][r_max]) or null
+  const bf16_t *Bn;   // optional d_out-major copy of B ([slot][d_out][rs]) or null
   const int32_t *row_segment, *seg_slot, *seg_rank;
   const float *seg_scale;
   int r_max, policy;
@@ -189,13 +189,13 @@ __device__ __forceinline__ mfma_bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi)
 }
 
 // LoRA term of one output row over 8 consecutive columns, added to o in fp32:
-// o[e] += sc sum_{k < r} H[grow][qoff + k] Bt_slot[qoff + k][gcol + e], k
+// o[e] += sc sum_{k < r} H[grow][qoff + k] Bt_slot[k][gcol + e], k
 // ascending, read in chunks of 8 rank rows; then, with DoRA, the slot's
 // column factors.  r need not be a multiple of 8: a chunk's rank rows at or
-// past r are read inside the projection's block (whose width rs is a
-// multiple of 8) and skipped.  qoff is the rank offset of the columns'
-// projection (offsets of projections are multiples of 8, so all 8 columns
-// share it).  Shared by both row epilogues, so both give the same bits.
+// past r are read inside the slot's rs rank rows (rs a multiple of 8) and
+// skipped.  qoff is the offset of the columns' projection in H's rank
+// entries (offsets of projections are multiples of 8, so all 8 columns share
+// it); Bt holds every column's own projection in rank rows [0, rs).  Shared by both row epilogues, so both give the same bits.
 // (Loading two chunks per step measured no faster on 64x64 tiles.)
 // COH: H was written by other workgroups of the same launch and is read
 // with agent-scope loads (layer.cuh).
@@ -204,7 +204,7 @@ __device__ __forceinline__ void lora_row8(const GemmArgs &g, int grow, int gcol,
                                           float sc, float (&o)[8]) {
   const int N = g.N;
   const int qoff = proj_of(g.proj, gcol) * g.proj.rs;
-  const bf16_t *bt = g.Bt + ((int64_t)slot * g.r_max + qoff) * N + gcol;
+  const bf16_t *bt = g.Bt + (int64_t)slot * g.proj.rs * N + gcol;
   const float *hp = g.H + (int64_t)grow * g.r_max + qoff;
   float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int kc = 0; kc < r; kc += 8) {      // kc < r <= rs: the chunk is in the block
@@ -256,7 +256,7 @@ __device__ __forceinline__ void lora_row8_pair(const GemmArgs &g, const int (&gr
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int qoff = proj_of(g.proj, gcol[u]) * g.proj.rs;
-    bt[u] = g.Bt + ((int64_t)slot[u] * g.r_max + qoff) * N + gcol[u];
+    bt[u] = g.Bt + (int64_t)slot[u] * g.proj.rs * N + gcol[u];
     hp[u] = g.H + (int64_t)grow[u] * g.r_max + qoff;
   }
   float d[2][8];
@@ -1143,7 +1143,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       constexpr int JB = (BN * 8 + C::T - 1) / C::T;
       u32x4 bv[JB];
       if constexpr (LORA == 2) {
-        const bf16_t *bn = g.Bn + (int64_t)slot * N * g.r_max;
+        const bf16_t *bn = g.Bn + (int64_t)slot * N * rs;
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
           const int it = min(tid + j * C::T, BN * NC - 1);
@@ -1151,8 +1151,7 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
           const int colc = min(n0 + col, N - 1);     // columns past N: never stored
           // a chunk past rs (only when rs = 8) is read from the block's
           // first chunk and masked below
-          bv[j] = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * g.r_max + qoff +
-                                                   min(c * 8, rs - 8));
+          bv[j] = *reinterpret_cast<const u32x4 *>(bn + (int64_t)colc * rs + min(c * 8, rs - 8));
         }
       }
       if constexpr (LORA == 2) {
@@ -1174,14 +1173,14 @@ __global__ __launch_bounds__(WM *WN *KG *kWave) void gemm_bf16_kernel(GemmArgs g
       } else {
         // from the rank-major Bt: 8 columns of one rank row per item,
         // transposed into the column rows with 2-byte stores
-        const bf16_t *bt = g.Bt + (int64_t)slot * g.r_max * N;
+        const bf16_t *bt = g.Bt + (int64_t)slot * rs * N;
         constexpr int CC = BN / 8;
         for (int it = tid; it < 8 * NC * CC; it += C::T) {
           const int k = it / CC, cc = it - (it / CC) * CC;
           const int col0 = n0 + cc * 8;
           u32x4 v = u32x4{0, 0, 0, 0};
           if (k < r && col0 >= c_lo && col0 < c_hi)
-            v = *reinterpret_cast<const u32x4 *>(bt + (int64_t)(qoff + k) * N + min(col0, N - 8));
+            v = *reinterpret_cast<const u32x4 *>(bt + (int64_t)k * N + min(col0, N - 8));
           const int c = k >> 3, kin = k & 7;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -1354,7 +1353,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
       if (r > 0) {
         const float sc = g.seg_scale[s];
         const float *hrow = g.H + (int64_t)row * g.r_max;
-        const float *bt = g.Bt + (int64_t)g.seg_slot[s] * g.r_max * g.N;
+        const float *bt = g.Bt + (int64_t)g.seg_slot[s] * g.proj.rs * g.N;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = n0 + tx * 4 + j;
@@ -1362,7 +1361,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
           const int qoff = proj_of(g.proj, col) * g.proj.rs;
           float d = 0.f;
           for (int k = 0; k < r; ++k)
-            d = fmaf(hrow[qoff + k], bt[(int64_t)(qoff + k) * g.N + col], d);
+            d = fmaf(hrow[qoff + k], bt[(int64_t)k * g.N + col], d);
           acc[i][j] += sc * d;
           if (g.dora) acc[i][j] *= g.dora[(int64_t)g.seg_slot[s] * g.N + col];
         }

@@ -34,8 +34,8 @@ struct ProjView {
 struct PoolView {
   int n_slots, r_max, d_in, d_out, dtype, policy;
   const void *A;
-  const void *Bt;
-  const void *B;   // optional d_out-major copy of B ([n_slots][d_out][r_max]) or null
+  const void *Bt;  // [n_slots][rs][d_out]: column j's rank rows are its own projection's
+  const void *B;   // optional d_out-major copy of B ([n_slots][d_out][rs]) or null
   const float *dora;   // optional DoRA column factors ([n_slots][d_out]) or null
   ProjView proj;
 };

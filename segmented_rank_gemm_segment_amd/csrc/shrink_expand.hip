@@ -397,7 +397,8 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
   const int col = ((blockIdx.x * kExpWaves + wave) * 16 + (lane & 15)) * V;
   const bool active = col < d_out;
   // the lane's columns belong to one projection (its offsets are multiples
-  // of 8): its rank rows start at q * rs in the slot and in H
+  // of 8): its rank entries start at q * rs in each H row; the slot's rs
+  // rank rows of Bt hold every column's own projection
   const int qoff = proj_of(proj, active ? col : 0) * proj.rs;
   // position blocks first, then the segments' first blocks (seg_item), in
   // ascending order: heads past the batch's segment count are empty, and so
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(kExpWaves * kWave) void expand_kernel(
     const int R = rank_bucket(r, policy, proj.rs);
     if (R == 0) continue;
     const int p0 = it.p0, p1 = it.p1;
-    const T *bt = Bt + ((int64_t)slot * r_max + qoff) * d_out + (active ? col : 0);
+    const T *bt = Bt + (int64_t)slot * proj.rs * d_out + (active ? col : 0);
     const float *gp = DORA ? dora + (int64_t)slot * d_out + (active ? col : 0) : nullptr;
     const float *Hq = H + qoff;   // the projection's ranks in each H row
     const int rs = proj.rs;
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
     const int nrow = __builtin_amdgcn_readfirstlane(s_tab[4][k] - s_tab[3][k]);
     const int R = rank_bucket(r, policy, rs);
     // B rows of the wave's columns, every rank step (ranks past r zeroed below)
-    const bf16_t *bs = Bn + (int64_t)slot * d_out * r_max + qoff;
+    const bf16_t *bs = Bn + (int64_t)slot * d_out * rs;
     u32x4 bv[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -587,7 +588,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
       for (int j = 0; j < 2; ++j) {
         const int n = min(nw + 32 * j + l32, d_out - 1);
         const int kc = min(ks * 16 + hf * 8, rs - 8);
-        bv[ks][j] = *reinterpret_cast<const u32x4 *>(bs + (int64_t)n * r_max + kc);
+        bv[ks][j] = *reinterpret_cast<const u32x4 *>(bs + (int64_t)n * rs + kc);
       }
     // the 32-row blocks holding the item's rows: only those are computed,
     // and only the item's 8-row groups enter and leave the tile (tile rows

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lora_abi_version() == srg.ABI_VERSION == 8
+    assert L.lora_abi_version() == srg.ABI_VERSION == 9
     for code in (OK, ENULL, ESHAPE, ERANK, EALIGN, EDTYPE, ECAP, EHIP, EPOLICY, ESCRATCH):
         s = L.lora_status_str(code).decode()
         assert s and s != "unknown status"

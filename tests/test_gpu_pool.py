@@ -8,8 +8,9 @@ target projection has its own A and B):
   alphas that make the quotient inexact too;
 * lora_pool_write_b: the d_out-major B is exactly Bt transposed;
 * lora_pool_pack_slot on a stacked pool: per-projection sources in either B
-  layout give the stacked layout (zeros outside each projection's columns
-  and past the rank) and the oracle's outputs per projection.
+  layout give the stacked layout (A: each projection's own rank rows; Bt and
+  B: each column's own projection in one projection's rank rows, zeros past
+  the rank) and the oracle's outputs per projection.
 """
 import numpy as np
 import pytest
@@ -89,8 +90,12 @@ def test_pack_stacked_pool(b_layout, dtype):
             Bs = [wl.to_torch(w.Bt[a, :r], dtype, DEV) for w in ws]
         pool.pack(a, As, Bs, 16.0, b_layout=b_layout)
     torch.cuda.synchronize()
-    # layout: projection q's A rows at [32 q, 32 q + r), B^T rows there over its
-    # own columns only, zeros elsewhere; the d_out-major copy likewise
+    # layout: projection q's A rows at [32 q, 32 q + r); B^T in rank rows
+    # [0, r) over projection q's own columns (each column holds its own
+    # projection, so Bt and B take one projection's 32 rank rows), zeros past
+    # the rank; the d_out-major copy likewise
+    assert tuple(pool.Bt.shape) == (b.n_slots, 32, sum(outs))
+    assert tuple(pool.B.shape) == (b.n_slots, sum(outs), 32)
     it = torch.int16 if dtype == "bf16" else torch.int32
     cols = np.cumsum((0,) + outs)
     Aref = torch.zeros_like(pool.A)
@@ -100,7 +105,7 @@ def test_pack_stacked_pool(b_layout, dtype):
         for a in range(b.n_slots):
             r = int(b.slot_rank[a])
             Aref[a, 32 * q:32 * q + r] = dq["A"][a, :r]
-            Btref[a, 32 * q:32 * q + r, cols[q]:cols[q + 1]] = dq["Bt"][a, :r]
+            Btref[a, :r, cols[q]:cols[q + 1]] = dq["Bt"][a, :r]
     assert torch.equal(pool.A.view(it), Aref.view(it))
     assert torch.equal(pool.Bt.view(it), Btref.view(it))
     assert torch.equal(pool.B.view(it), Btref.view(it).transpose(1, 2).contiguous())
