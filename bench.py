@@ -708,7 +708,8 @@ def fp8w_entry(w, fig, m, args):
         "step_us_by_path": {p: round(v[0] * 1e6, 3) for p, v in mq["step"].items()},
         "step_vs_bf16": round(st / bf16, 4) if bf16 else None,
         "kernels": kt,
-        "roofline": roofline_for(main_k, fig, mq["per_kernel_s"][main_k], w.dtype),
+        "roofline": dict(roofline_for(main_k, fig, mq["per_kernel_s"][main_k], w.dtype),
+                         traffic=measured_traffic(args.config, main_k)),
     }
 
 
