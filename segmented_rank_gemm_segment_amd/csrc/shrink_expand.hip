@@ -579,7 +579,9 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
     const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_tab[2][k]));
     const int nrow = __builtin_amdgcn_readfirstlane(s_tab[4][k] - s_tab[3][k]);
     const int R = rank_bucket(r, policy, rs);
-    // B rows of the wave's columns, every rank step (ranks past r zeroed below)
+    // B rows of the wave's columns, every rank step (ranks past r zeroed
+    // below); the steps past the rank bucket R read a chunk inside [0, R)
+    // instead (unused), so no load reaches sectors of ranks the item lacks
     const bf16_t *bs = Bn + (int64_t)slot * d_out * rs;
     u32x4 bv[4][2];
 #pragma unroll
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(4 * kWave, 3) void expand_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = min(nw + 32 * j + l32, d_out - 1);
-        const int kc = min(ks * 16 + hf * 8, rs - 8);
+        const int kc = min(ks * 16 + hf * 8, R - 8);
         bv[ks][j] = *reinterpret_cast<const u32x4 *>(bs + (int64_t)n * rs + kc);
       }
     // the 32-row blocks holding the item's rows: only those are computed,
