@@ -27,7 +27,7 @@ Prints one JSON line (rank 0; one GPU):
   cpu_baseline = the float64 CPU oracle on a bounded sample of the headline
                workload, on this host's cores
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--path fused]
+    python bench.py [--steps K] [--warmup W] [--workload decode] [--path fused]
 """
 from __future__ import annotations
 
@@ -44,12 +44,15 @@ MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 F32_TFLOPS = 157.3
 
 WORKLOAD_NAMES = {
-    1: "tiny fp32: d_in=d_out=512, 32 rows in 4 segments [0,8,12,28,32] (r 8/base/16/8)",
-    2: "decode bf16: d_in=d_out=4096, 256 rows (1 token/request), 128 slots r=16, 10% base-only",
-    3: "prefill bf16: d_in=4096 -> d_out=14336, 8 requests 512..4096 tokens, ranks 8..64, 1 base-only",
-    4: "skewed decode bf16: d=4096, 1024 rows, 1000 slots r in {8,16,32,64}, Zipf(1.0) ids",
-    5: "70B-shaped layer bf16: q/k/v/o/gate/up/down, 2304 rows (2048 prefill + 256 decode), "
-       "64 slots r in {16, 64}",
+    "tiny_f32": "tiny fp32: d_in=d_out=512, 32 rows in 4 segments [0,8,12,28,32] (r 8/base/16/8)",
+    "decode": "decode bf16: d_in=d_out=4096, 256 rows (1 token/request), 128 slots r=16, "
+              "10% base-only",
+    "prefill": "prefill bf16: d_in=4096 -> d_out=14336, 8 requests 512..4096 tokens, ranks 8..64, "
+               "1 base-only",
+    "skewed_decode": "skewed decode bf16: d=4096, 1024 rows, 1000 slots r in {8,16,32,64}, "
+                     "Zipf(1.0) ids",
+    "layer70b": "70B-shaped layer bf16: q/k/v/o/gate/up/down, 2304 rows (2048 prefill + 256 "
+                "decode), 64 slots r in {16, 64}",
 }
 
 
@@ -58,7 +61,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--workload", default="decode",
+                   choices=["tiny_f32", "decode", "prefill", "skewed_decode"])
     p.add_argument("--path", choices=["auto", "fused", "separate", "overlap", "layer"],
                    default="auto",
                    help="auto: time every step variant and report the fastest; overlap = "
@@ -74,7 +78,7 @@ def parse():
     p.add_argument("--no-fp8w", action="store_true",
                    help="skip the FP8-weight variant of the base product")
     p.add_argument("--no-skewed", action="store_true",
-                   help="skip the skewed large-pool decode entry (configuration 4, three rank policies)")
+                   help="skip the skewed large-pool decode entry (three rank policies)")
     p.add_argument("--no-layer", action="store_true",
                    help="skip the 70B-shaped layer (seven projections, separate vs stacked)")
     p.add_argument("--no-vendor", action="store_true",
@@ -506,8 +510,8 @@ def unit_source_sha(unit):
     return h.hexdigest()
 
 
-def measured_traffic(config, kernel):
-    """HBM bytes per launch of `kernel` on `config` from rocprofv3 FETCH_SIZE
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from rocprofv3 FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch, each scaled by the reading of a plain
     copy of known size), or None when no counters were taken for the current
     code of the kernel's translation unit (and the headers it includes)."""
@@ -520,7 +524,7 @@ def measured_traffic(config, kernel):
     shas = t.get("unit_sha256", {})
     if unit is None or unit not in shas or shas[unit] != unit_source_sha(unit):
         return None
-    k = t.get("configs", {}).get(str(config), {}).get(kernel)
+    k = t.get("workloads", {}).get(workload, {}).get(kernel)
     if not k:
         return None
     return int(round((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024))
@@ -593,13 +597,15 @@ def _oracle_layer_time(ws, rows, budget_s, min_runs=1, warmup=True):
 
 
 def cpu_baselines(budget_s=3.0):
-    """The float64 oracle on configurations 1, 3, 4 and 5, on all BLAS
-    threads and on one thread, median of the passes after a warm-up.
-    Configurations 1 and 4 run whole; 3 and 5 run a seeded sample of rows and
-    are extrapolated linearly to the batch, since rows are independent: 512
-    rows on all threads (the first and last row of every segment and every
-    decode row of 5 included), 128 (3) or 32 (5) random rows on one thread
-    (no warm-up pass: one pass of 5 takes seconds).  A pass has a part that does not
+    """The float64 oracle on the tiny fp32, skewed-decode, prefill and
+    70B-shaped workloads, on all BLAS threads and on one thread, median of
+    the passes after a warm-up.  The tiny and skewed workloads run whole; the
+    prefill and 70B-shaped ones run a seeded sample of rows and are
+    extrapolated linearly to the batch, since rows are independent: 512 rows
+    on all threads (the first and last row of every segment and every decode
+    row of the 70B-shaped batch included), 128 (prefill) or 32 (70B-shaped)
+    random rows on one thread (no warm-up pass: one 70B-shaped pass takes
+    seconds).  A pass has a part that does not
     depend on the rows asked for (the metadata of the whole batch, decoding
     the whole X and W), timed by a pass over no rows: the batch time is
     t0 + (t_sample - t0) n / sample."""
@@ -622,19 +628,21 @@ def cpu_baselines(budget_s=3.0):
         return np.array(sorted(rows)[:max(k, len(rows))])
 
     out = {}
-    for cfg in (1, 4, 3, 5):
-        if cfg == 5:
-            ws = [wl.cfg5_projection(p[0]) for p in wl.CFG5_PROJECTIONS]
+    for name in ("tiny_f32", "skewed_decode", "prefill", "layer70b"):
+        if name == "layer70b":
+            ws = [wl.layer70b_projection(p[0]) for p in wl.LAYER70B_PROJECTIONS]
         else:
-            ws = [wl.make_config(cfg)]
+            ws = [wl.make_workload(name)]
         n = ws[0].n
-        entry = {"workload": WORKLOAD_NAMES.get(cfg, "70B-shaped layer, seven projections"),
-                 "seed": f"numpy SeedSequence({cfg})", "rows": n}
-        for label, k, lim in (("all_cores", 512, None), ("single_core", 128 if cfg == 3 else 32, 1)):
+        entry = {"workload": WORKLOAD_NAMES[name], "seed": f"numpy SeedSequence({wl.SEEDS[name]})",
+                 "rows": n}
+        sampled = name in ("prefill", "layer70b")
+        for label, k, lim in (("all_cores", 512, None),
+                              ("single_core", 128 if name == "prefill" else 32, 1)):
             if lim == 1 and threadpool_limits is None:
                 continue
-            if cfg in (3, 5):
-                extra = range(2048, 2304) if (cfg == 5 and lim is None) else ()
+            if sampled:
+                extra = range(2048, 2304) if (name == "layer70b" and lim is None) else ()
                 rows = sample(ws[0], k, extra, ends=lim is None)
             else:
                 rows = None
@@ -658,7 +666,7 @@ def cpu_baselines(budget_s=3.0):
                                        else f"median of {runs} passes over {done} seeded rows of "
                                             f"{n} ({t:.2f} s; {t0:.2f} s of it independent of "
                                             f"the rows), extrapolated linearly")}
-        out[str(cfg)] = entry
+        out[name] = entry
         del ws
     return out
 
@@ -709,7 +717,7 @@ def fp8w_entry(w, fig, m, args):
         "step_vs_bf16": round(st / bf16, 4) if bf16 else None,
         "kernels": kt,
         "roofline": dict(roofline_for(main_k, fig, mq["per_kernel_s"][main_k], w.dtype),
-                         traffic=measured_traffic(args.config, main_k)),
+                         traffic=measured_traffic(args.workload, main_k)),
     }
 
 
@@ -723,8 +731,8 @@ def layer_entry(args, device="cuda:0"):
     import torch
     import segmented_rank_gemm_segment_amd as srg
     import workloads as wl
-    names = [p[0] for p in wl.CFG5_PROJECTIONS]
-    ws = {nm: wl.cfg5_projection(nm) for nm in names}
+    names = [p[0] for p in wl.LAYER70B_PROJECTIONS]
+    ws = {nm: wl.layer70b_projection(nm) for nm in names}
     for a, b in (("k_proj", "q_proj"), ("v_proj", "q_proj"), ("up_proj", "gate_proj")):
         ws[a].X = ws[b].X
     w0 = ws["q_proj"]
@@ -780,16 +788,17 @@ def layer_entry(args, device="cuda:0"):
 
 
 def skewed_entry(args):
-    """Configuration 4 (1024 decode rows, 1000 resident slots of mixed rank,
-    Zipf adapter ids) under each rank policy: per-rank buckets (exact), the
+    """The skewed decode workload (1024 decode rows, 1000 resident slots of
+    mixed rank, Zipf adapter ids) under each rank policy: per-rank buckets (exact), the
     two buckets {8,16} / {32,64}, and every slot padded to rank 64.  Step on
     each path (the fastest one named) and the shrink / fused GEMM per policy."""
     import workloads as wl
-    w4 = wl.make_config(4)
+    w4 = wl.make_workload("skewed_decode")
     f4 = work_figures(w4)
     st = max(10, args.steps // 4)
-    out = {"workload": WORKLOAD_NAMES[4], "rows": w4.n,
-           "distinct_adapters": f4["distinct_adapters"], "batch": workload_stats(w4, 4),
+    out = {"workload": WORKLOAD_NAMES["skewed_decode"], "rows": w4.n,
+           "distinct_adapters": f4["distinct_adapters"],
+           "batch": workload_stats(w4, wl.SEEDS["skewed_decode"]),
            "alg_bytes": {"shrink": int(f4["bytes"]["shrink"]), "expand": int(f4["bytes"]["expand"]),
                          "fused": int(f4["bytes"]["fused"])},
            "policies": {}}
@@ -805,7 +814,8 @@ def skewed_entry(args):
             "us": {k: round(v * 1e6, 3) for k, v in pk.items()},
             # counters were taken with the exact policy
             "fused_gemm": dict(roofline_for("fused", f4, pk["fused"], "bf16"),
-                               traffic=measured_traffic(4, "fused") if pol == "exact" else None),
+                               traffic=(measured_traffic("skewed_decode", "fused")
+                                        if pol == "exact" else None)),
             "shrink_expand": {"GB_s": round(se / (pk["shrink"] + pk["expand"]) / 1e9, 1),
                               "hbm_frac": round(se / (pk["shrink"] + pk["expand"]) / 1e9 /
                                                 HBM_PEAK_GBS, 4)}}
@@ -839,10 +849,10 @@ def main():
         return
     srg.lib()
 
-    w = wl.make_config(args.config)
+    w = wl.make_workload(args.workload)
     fig = work_figures(w)
     paths = list(PATHS) if args.path == "auto" else [args.path]
-    log(f"configuration {args.config}: steps and kernels")
+    log(f"{args.workload}: steps and kernels")
     m = measure(w, paths, args.policy, args.steps, args.warmup, args.rotate_mb,
                 args.kernel_loops, not args.eager, vendor=not args.no_vendor and w.dtype == "bf16")
     path = min(paths, key=lambda p: m["step"][p][0])
@@ -853,7 +863,7 @@ def main():
     # (overlap: same kernels as separate, base GEMM concurrent with build + shrink)
     main_k = max(cand, key=lambda k: m["per_kernel_s"][k])
     roof = roofline_for(main_k, fig, m["per_kernel_s"][main_k], w.dtype)
-    roof["traffic"] = measured_traffic(args.config, main_k)
+    roof["traffic"] = measured_traffic(args.workload, main_k)
     sh, ex = m["per_kernel_s"]["shrink"], m["per_kernel_s"]["expand"]
     se_bytes = fig["bytes"]["shrink"] + fig["bytes"]["expand"]
     out = {
@@ -869,13 +879,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded normals; mapping per the workload recipe)",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "path": path,
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "path": path,
                    "rank_policy": args.policy, "rows": w.n, "lora_rows": fig["n_lora_rows"],
                    "distinct_adapters": fig["distinct_adapters"],
                    "rotated_copies": m["copies"], "launch": "eager" if args.eager else "hip_graph",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "batch": workload_stats(w, args.config),
+        "batch": workload_stats(w, wl.SEEDS[args.workload]),
         "shrink_expand": {"GB_s": round(se_bytes / (sh + ex) / 1e9, 1),
                           "hbm_frac": round(se_bytes / (sh + ex) / 1e9 / HBM_PEAK_GBS, 4),
                           "us": round((sh + ex) * 1e6, 3)},
@@ -885,9 +895,9 @@ def main():
     }
     if vendor_entry(fig, m):
         out["vendor_base_gemm"] = vendor_entry(fig, m)
-    if not args.no_prefill and args.config != 3:
-        log("prefill (configuration 3)")
-        w3 = wl.make_config(3)
+    if not args.no_prefill and args.workload != "prefill":
+        log("prefill")
+        w3 = wl.make_workload("prefill")
         f3 = work_figures(w3)
         st3 = max(5, args.steps // 10)
         # two rotated copies (each ~0.75 GB): no call reads what the previous
@@ -897,12 +907,12 @@ def main():
                      not args.eager, vendor=not args.no_vendor)
         k3 = kernel_table(f3, m3["per_kernel_s"], "bf16")
         out["prefill"] = {
-            "workload": WORKLOAD_NAMES[3], "rows": w3.n, "rotated_copies": m3["copies"],
-            "batch": workload_stats(w3, 3),
+            "workload": WORKLOAD_NAMES["prefill"], "rows": w3.n, "rotated_copies": m3["copies"],
+            "batch": workload_stats(w3, wl.SEEDS["prefill"]),
             "tokens_s": round(w3.n / m3["step"]["fused"][0], 1),
             "ms_per_step": round(m3["step"]["fused"][0] * 1e3, 4), "path": "fused",
             "fused_gemm": dict(roofline_for("fused", f3, m3["per_kernel_s"]["fused"], "bf16"),
-                               traffic=measured_traffic(3, "fused")),
+                               traffic=measured_traffic("prefill", "fused")),
             "shrink_expand": {
                 "GB_s": round((f3["bytes"]["shrink"] + f3["bytes"]["expand"]) /
                               (m3["per_kernel_s"]["shrink"] + m3["per_kernel_s"]["expand"]) / 1e9, 1),
@@ -919,7 +929,7 @@ def main():
         log("DoRA variant")
         out["dora"] = dora_entry(w, fig, m, paths, args)
         if "prefill" in out:
-            w3 = wl.make_config(3)
+            w3 = wl.make_workload("prefill")
             st3 = max(5, args.steps // 10)
             md3 = measure(w3, ["fused"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
                           not args.eager, dora=True)
@@ -933,7 +943,7 @@ def main():
         log("FP8-weight variant")
         out["fp8_weight"] = fp8w_entry(w, fig, m, args)
         if "prefill" in out:
-            w3 = wl.make_config(3)
+            w3 = wl.make_workload("prefill")
             f3 = work_figures(w3)
             st3 = max(5, args.steps // 10)
             mq3 = measure(w3, ["fused_fp8w"], args.policy, st3, max(2, args.warmup // 4), 0.0, st3,
@@ -943,19 +953,19 @@ def main():
                 "fused_gemm": roofline_for("fused_fp8w", f3, mq3["per_kernel_s"]["fused_fp8w"], "bf16"),
                 "fused_us": round(mq3["per_kernel_s"]["fused_fp8w"] * 1e6, 3)}
             del w3
-    if not args.no_skewed and args.config == 2:
-        log("skewed decode (configuration 4), three rank policies")
+    if not args.no_skewed and args.workload == "decode":
+        log("skewed decode, three rank policies")
         out["skewed_decode"] = skewed_entry(args)
-    if not args.no_layer and args.config == 2:
-        log("70B-shaped layer (configuration 5)")
+    if not args.no_layer and args.workload == "decode":
+        log("70B-shaped layer")
         out["layer_70b"] = layer_entry(args)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline, headline workload")
         out["cpu_baseline"] = cpu_baseline(w)
-        log("CPU oracle baselines, configurations 1, 4, 3, 5")
+        log("CPU oracle baselines: tiny fp32, skewed decode, prefill, 70B-shaped layer")
         out["cpu_baselines"] = cpu_baselines()
         if "prefill" in out:
-            out["prefill"]["cpu_baseline"] = out["cpu_baselines"]["3"]["all_cores"]
+            out["prefill"]["cpu_baseline"] = out["cpu_baselines"]["prefill"]["all_cores"]
     print(json.dumps(out), flush=True)
 
 

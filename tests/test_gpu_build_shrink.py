@@ -92,7 +92,7 @@ def test_one_call_equals_two_calls(case, policy):
 
 
 def test_decode_workload():
-    w = wl.make_config(2)
+    w = wl.make_workload("decode")
     _, H = _same(w)
     say("decode H error", _oracle_H(w, H))
 

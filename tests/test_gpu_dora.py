@@ -223,7 +223,7 @@ def test_empty_batch_with_dora_pool():
 # ---------------------------------------------------------------- full-size workloads
 def test_dora_decode_full():
     """Decode workload (d 4096, 256 rows, 128 rank-16 slots), every row."""
-    w = wl.make_config(2)
+    w = wl.make_workload("decode")
     mag = _magnitudes(w, 2)
     d = wl.device_tensors(w, DEV)
     out = _forward(w, d, _dora_pool(w, d, mag))
@@ -236,7 +236,7 @@ def test_dora_decode_full():
 def test_dora_prefill_sampled():
     """Prefill workload (d 4096 -> 14336, eight requests, ranks 8..64, one
     base-only request) on the large-tile fused kernel, sampled rows."""
-    w = wl.make_config(3)
+    w = wl.make_workload("prefill")
     mag = _magnitudes(w, 3, p_plain=0.0)
     d = wl.device_tensors(w, DEV)
     out = _forward(w, d, _dora_pool(w, d, mag), separate=False)

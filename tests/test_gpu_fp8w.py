@@ -112,14 +112,14 @@ def test_fp8w_exact_on_small_integers(n):
 
 
 def test_fp8w_decode_workload():
-    w = wl.make_config(2)
+    w = wl.make_workload("decode")
     codes, scale = wl.make_fp8_weight(2, w.d_out, w.d_in)
     Yf, Yb = _run(w, codes, scale)
     say("fp8w decode", _check(w, codes, scale, Yf, Yb))
 
 
 def test_fp8w_prefill_sampled():
-    w = wl.make_config(3)
+    w = wl.make_workload("prefill")
     codes, scale = wl.make_fp8_weight(3, w.d_out, w.d_in)
     Yf, Yb = _run(w, codes, scale)
     meta = oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)

@@ -252,8 +252,8 @@ def test_term_stacked(n):
 
 @pytest.mark.parametrize("n", [32, 300])
 def test_term_f32(n):
-    """The fp32 product's LoRA term (configuration 1's layout at n = 32)."""
-    w = _zero_base(wl.make_config(1) if n == 32 else
+    """The fp32 product's LoRA term (the tiny fp32 case's layout at n = 32)."""
+    w = _zero_base(wl.make_workload("tiny_f32") if n == 32 else
                    wl.make_random(895, n, 136, 200, 9, 32, p_base=0.1, dtype="f32",
                                   x_std=0.02, runs=True))
     d = wl.device_tensors(w, DEV)

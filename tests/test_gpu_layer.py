@@ -64,9 +64,9 @@ def full_check(w, r):
 
 def test_decode_configuration():
     """Decode workload (256 rows, d 4096, 128 slots of rank 16): one launch."""
-    w = wl.make_config(2)
+    w = wl.make_workload("decode")
     r = run_layer(w)
-    say("layer cfg2", full_check(w, r))
+    say("layer decode", full_check(w, r))
     # the same product as the two calls, up to the order of H's additions
     d = r.d
     seg = srg.Segments(w.n, w.n_slots, DEV)

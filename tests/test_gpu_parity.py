@@ -29,79 +29,79 @@ def _gpu():
 
 
 # ---------------------------------------------------------------- the configurations
-def test_cfg1_tiny_f32():
-    w = wl.make_config(1)
-    say("cfg1", w.n, w.d_in, w.d_out)
+def test_tiny_f32():
+    w = wl.make_workload("tiny_f32")
+    say("tiny f32", w.n, w.d_in, w.d_out)
     r = run_hip(w)
     ref = check_metadata(w, r)
     assert ref["segment_offsets"].tolist() == [0, 8, 12, 28, 32]
     e = check_values(w, r)
     base_rows_bitwise(w, r)
-    say("cfg1 errors", e)
+    say("tiny f32 errors", e)
 
 
-def test_cfg2_decode_bf16():
-    w = wl.make_config(2)
-    say("cfg2", w.n, w.d_in, w.d_out)
+def test_decode_bf16():
+    w = wl.make_workload("decode")
+    say("decode", w.n, w.d_in, w.d_out)
     r = run_hip(w)
     check_metadata(w, r)
     e = check_values(w, r)
     assert base_rows_bitwise(w, r) > 0
-    say("cfg2 errors", e)
+    say("decode errors", e)
 
 
 _CACHE = {}
 
 
-def _cfg4():
-    if "cfg4" not in _CACHE:
-        _CACHE["cfg4"] = wl.make_config(4)
-    return _CACHE["cfg4"]
+def _skewed():
+    if "skewed" not in _CACHE:
+        _CACHE["skewed"] = wl.make_workload("skewed_decode")
+    return _CACHE["skewed"]
 
 
 @pytest.mark.parametrize("policy", ["exact", "two_buckets", "padded"])
-def test_cfg4_skewed_decode_bf16(policy):
-    w = _cfg4()
-    say("cfg4", policy, w.n, w.d_in, w.d_out, w.n_slots)
+def test_skewed_decode_bf16(policy):
+    w = _skewed()
+    say("skewed decode", policy, w.n, w.d_in, w.d_out, w.n_slots)
     r = run_hip(w, policy)
     check_metadata(w, r)
     e = check_values(w, r)
-    say("cfg4 errors", policy, e)
+    say("skewed decode errors", policy, e)
 
 
-def test_cfg3_prefill_structure_small():
-    """Configuration 3's structure (d 4096 -> 14336, ranks 8..64, request 7
+def test_prefill_structure_small():
+    """The prefill workload's structure (d 4096 -> 14336, ranks 8..64, request 7
     base-only) with short, ragged requests so the oracle runs every row."""
-    w = wl._cfg3(lengths_override=[300, 17, 150, 1, 64, 200, 33, 90])
-    say("cfg3 small", w.n, w.d_in, w.d_out)
+    w = wl.prefill(lengths_override=[300, 17, 150, 1, 64, 200, 33, 90])
+    say("prefill small", w.n, w.d_in, w.d_out)
     r = run_hip(w)
     check_metadata(w, r)
     e = check_values(w, r)
     assert base_rows_bitwise(w, r) == 90
-    say("cfg3 small errors", e)
+    say("prefill small errors", e)
 
 
-def test_cfg3_prefill_full_sampled():
-    w = wl.make_config(3)
-    say("cfg3 full", w.n, w.d_in, w.d_out, w.meta)
+def test_prefill_full_sampled():
+    w = wl.make_workload("prefill")
+    say("prefill full", w.n, w.d_in, w.d_out, w.meta)
     r = run_hip(w, separate=False)
     ref = check_metadata(w, r)
     rows = sample_rows(w, ref, 512)
     e = check_values(w, r, rows=rows)
     assert torch.isfinite(r.Yf.float()).all()
-    say("cfg3 full errors (sampled rows)", len(rows), e)
+    say("prefill full errors (sampled rows)", len(rows), e)
 
 
-@pytest.mark.parametrize("proj", [p[0] for p in wl.CFG5_PROJECTIONS])
-def test_cfg5_projection_sampled(proj):
-    w = wl.cfg5_projection(proj)
-    say("cfg5", proj, w.n, w.d_in, w.d_out)
+@pytest.mark.parametrize("proj", [p[0] for p in wl.LAYER70B_PROJECTIONS])
+def test_layer70b_projection_sampled(proj):
+    w = wl.layer70b_projection(proj)
+    say("layer70b", proj, w.n, w.d_in, w.d_out)
     r = run_hip(w, separate=False)
     ref = check_metadata(w, r)
     rows = sample_rows(w, ref, 512, extra=range(2048, 2304))
     e = check_values(w, r, rows=rows)
     assert torch.isfinite(r.Yf.float()).all()
-    say("cfg5 errors", proj, len(rows), e)
+    say("layer70b errors", proj, len(rows), e)
 
 
 # ---------------------------------------------------------------- structure and edge cases

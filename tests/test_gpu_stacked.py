@@ -187,7 +187,7 @@ def test_stacked_fp8_weight(n):
 def test_stacked_qkv_70b_shapes_sampled():
     """The 70B-shaped layer's q, k, v projections (8192 -> 8192 / 1024 / 1024,
     2304 rows, 64 slots with ranks 16 and 64) as one fused QKV call."""
-    ws = [wl.cfg5_projection(p) for p in ("q_proj", "k_proj", "v_proj")]
+    ws = [wl.layer70b_projection(p) for p in ("q_proj", "k_proj", "v_proj")]
     b = ws[0]
     for w in ws[1:]:
         w.X = b.X                       # one input for the three projections

@@ -46,9 +46,9 @@ def test_printed_metadata_example():
     assert m["status"] == 0
 
 
-def test_cfg1_offsets():
-    """Configuration 1's printed offsets [0, 8, 12, 28, 32] -> {A r8, base, B r16, C r8}."""
-    w = wl.make_config(1)
+def test_tiny_f32_offsets():
+    """The tiny fp32 case's offsets [0, 8, 12, 28, 32] -> {A r8, base, B r16, C r8}."""
+    w = wl.make_workload("tiny_f32")
     m = oracle.segment_metadata(w.row_slot, w.slot_rank, w.slot_alpha, w.r_max)
     assert m["segment_offsets"].tolist() == [0, 8, 12, 28, 32]
     assert m["segment_slots"].tolist() == [0, -1, 1, 2]
@@ -314,12 +314,12 @@ def test_parameter_arithmetic_printed():
 
 
 def test_workload_configs_shapes():
-    w1 = wl.make_config(1)
+    w1 = wl.make_workload("tiny_f32")
     assert (w1.n, w1.d_in, w1.d_out, w1.dtype) == (32, 512, 512, "f32")
-    w2 = wl.make_config(2)
+    w2 = wl.make_workload("decode")
     assert (w2.n, w2.d_in, w2.d_out, w2.n_slots, w2.r_max) == (256, 4096, 4096, 128, 16)
     frac_base = np.mean(w2.row_slot < 0)
     assert 0.03 < frac_base < 0.2
-    row_slot, ranks, _ = wl.cfg5_mapping()
+    row_slot, ranks, _ = wl.layer70b_mapping()
     assert len(row_slot) == 2304 and len(set(row_slot[:2048].tolist())) == 1
     assert ranks.tolist() == [16] * 32 + [64] * 32

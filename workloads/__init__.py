@@ -20,7 +20,8 @@ bf16 tensors are ``numpy.uint16`` bit patterns, rounded from float32 draws
 with round-to-nearest-even.  fp32 tensors are ``numpy.float32``.
 
 Shapes, distributions and mappings follow the five workloads the pages'
-prefill / decode discussion implies (see each ``_cfgN`` docstring).
+prefill / decode discussion implies (see the docstrings of ``tiny_f32``,
+``decode``, ``prefill``, ``skewed_decode`` and ``layer70b_projection``).
 """
 from __future__ import annotations
 
@@ -145,19 +146,19 @@ def build_workload(name, dtype, seed_seq, n, d_in, d_out, row_slot, slot_rank, r
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------
-def _cfg1(pad="nan") -> Workload:
+def tiny_f32(pad="nan") -> Workload:
     """Tiny fp32 check: d_in = d_out = 512, 32 rows in four runs
     [0,8) -> adapter A (r=8), [8,12) -> base only, [12,28) -> adapter B (r=16),
     [28,32) -> adapter C (r=8); alpha 16; W, A, B, X ~ N(0, 0.02)."""
     ss = np.random.SeedSequence(1)
     s_map, s_data = ss.spawn(2)
     row_slot = np.array([0] * 8 + [-1] * 4 + [1] * 16 + [2] * 4, dtype=np.int32)
-    return build_workload("cfg1_tiny_f32", "f32", s_data, 32, 512, 512, row_slot,
+    return build_workload("tiny_f32", "f32", s_data, 32, 512, 512, row_slot,
                           [8, 16, 8], 16, 0.02, 0.02, 0.02, pad,
                           meta={"offsets_printed": [0, 8, 12, 28, 32]})
 
 
-def _cfg2(pad="nan") -> Workload:
+def decode(pad="nan") -> Workload:
     """Decode GEMV, bf16: d_in = d_out = 4096 (an 8B-class q_proj), 256 rows of
     one token each, 128 slots all rank 16, each row base-only with p = 0.1 else
     a uniform slot; W, A, B ~ N(0, 0.02), X ~ N(0, 1)."""
@@ -168,11 +169,11 @@ def _cfg2(pad="nan") -> Workload:
     is_base = rng.random(n) < 0.1
     slots = rng.integers(0, 128, size=n)
     row_slot = np.where(is_base, -1, slots).astype(np.int32)
-    return build_workload("cfg2_decode_bf16", "bf16", s_data, n, 4096, 4096, row_slot,
+    return build_workload("decode_bf16", "bf16", s_data, n, 4096, 4096, row_slot,
                           [16] * 128, 16, 1.0, 0.02, 0.02, pad)
 
 
-def _cfg3(pad="nan", lengths_override: Optional[List[int]] = None) -> Workload:
+def prefill(pad="nan", lengths_override: Optional[List[int]] = None) -> Workload:
     """Prefill segmented GEMM, bf16: d_in 4096 -> d_out 14336 (MLP up-proj);
     8 requests with lengths uniform in [512, 4096]; slots 0..7 with ranks
     8,8,16,16,32,32,64,64; request k uses slot k for k < 7, request 7 is
@@ -186,12 +187,12 @@ def _cfg3(pad="nan", lengths_override: Optional[List[int]] = None) -> Workload:
         lengths = np.asarray(lengths_override)
     row_slot = np.concatenate([np.full(int(L), k if k < 7 else -1, dtype=np.int32)
                                for k, L in enumerate(lengths)])
-    return build_workload("cfg3_prefill_bf16", "bf16", s_data, int(lengths.sum()), 4096, 14336,
+    return build_workload("prefill_bf16", "bf16", s_data, int(lengths.sum()), 4096, 14336,
                           row_slot, [8, 8, 16, 16, 32, 32, 64, 64], 64, 1.0, 0.02, 0.02, pad,
                           meta={"lengths": [int(v) for v in lengths]})
 
 
-def _cfg4(pad="nan") -> Workload:
+def skewed_decode(pad="nan") -> Workload:
     """Skewed large-pool decode, bf16: d_in = d_out = 4096, 1024 rows, 1000
     resident slots (r_max 64), ranks uniform over {8,16,32,64}, adapter ids
     Zipf(1.0) truncated to 1000 ids (P(k) proportional to 1/(k+1)); adapter k
@@ -204,12 +205,12 @@ def _cfg4(pad="nan") -> Workload:
     p = 1.0 / np.arange(1, n_slots + 1, dtype=np.float64)
     p /= p.sum()
     row_slot = rng.choice(n_slots, size=n, p=p).astype(np.int32)
-    return build_workload("cfg4_skewed_decode_bf16", "bf16", s_data, n, 4096, 4096, row_slot,
+    return build_workload("skewed_decode_bf16", "bf16", s_data, n, 4096, 4096, row_slot,
                           ranks, 64, 1.0, 0.02, 0.02, pad)
 
 
 # 70B-class layer: GQA attention projections plus a gated MLP.
-CFG5_PROJECTIONS = (
+LAYER70B_PROJECTIONS = (
     ("q_proj", 8192, 8192),
     ("k_proj", 8192, 1024),
     ("v_proj", 8192, 1024),
@@ -220,7 +221,7 @@ CFG5_PROJECTIONS = (
 )
 
 
-def cfg5_mapping():
+def layer70b_mapping():
     """Rows [0, 2048) are one chunked-prefill request on one seeded slot; rows
     [2048, 2304) are decode rows, each on a uniform slot of 64.  Slots 0..31
     have rank 16, slots 32..63 rank 64.  No base-only rows."""
@@ -234,22 +235,29 @@ def cfg5_mapping():
     return row_slot, ranks, s_data
 
 
-def cfg5_projection(name: str, pad="nan", n_rows: Optional[int] = None) -> Workload:
+def layer70b_projection(name: str, pad="nan", n_rows: Optional[int] = None) -> Workload:
     """One projection of the 70B-shaped mixed layer (own seeded X, W, pool)."""
-    names = [p[0] for p in CFG5_PROJECTIONS]
+    names = [p[0] for p in LAYER70B_PROJECTIONS]
     i = names.index(name)
-    _, d_in, d_out = CFG5_PROJECTIONS[i]
-    row_slot, ranks, s_data = cfg5_mapping()
-    s_proj = s_data.spawn(len(CFG5_PROJECTIONS))[i]
+    _, d_in, d_out = LAYER70B_PROJECTIONS[i]
+    row_slot, ranks, s_data = layer70b_mapping()
+    s_proj = s_data.spawn(len(LAYER70B_PROJECTIONS))[i]
     if n_rows is not None:
         row_slot = row_slot[:n_rows]
-    return build_workload("cfg5_" + name, "bf16", s_proj, len(row_slot), d_in, d_out, row_slot,
+    return build_workload("layer70b_" + name, "bf16", s_proj, len(row_slot), d_in, d_out, row_slot,
                           ranks, 64, 1.0, 0.02, 0.02, pad, meta={"projection": name})
 
 
-def make_config(cfg_id: int, pad: str = "nan") -> Workload:
-    """Configurations 1..4 (5 has seven projections: ``cfg5_projection``)."""
-    return {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4}[cfg_id](pad=pad)
+# the single-projection workloads by name, and the seed each draws from (the
+# 70B-shaped layer, seven projections, is ``layer70b_projection``; seed 5)
+WORKLOADS = {"tiny_f32": tiny_f32, "decode": decode, "prefill": prefill,
+             "skewed_decode": skewed_decode}
+SEEDS = {"tiny_f32": 1, "decode": 2, "prefill": 3, "skewed_decode": 4, "layer70b": 5}
+
+
+def make_workload(name: str, pad: str = "nan") -> Workload:
+    """One of ``WORKLOADS`` by name."""
+    return WORKLOADS[name](pad=pad)
 
 
 # --------------------------------------------------------------------------
