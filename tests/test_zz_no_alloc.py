@@ -96,6 +96,43 @@ def test_static_call_repeated_and_empty():
     assert torch.equal(Yb, _with_buffers(big, db, pool))
 
 
+def test_static_call_stacked_pool():
+    """A stacked pool (two projections of one input, B stored once per
+    column): the same bits as the buffered calls, and the oracle per
+    projection."""
+    ws = []
+    for p, d_out in enumerate((200, 136)):
+        w = wl.make_random(910 + p, 600, 128, d_out, 10, 32, p_base=0.1, runs=True,
+                           ranks=None if p == 0 else list(ws[0].slot_rank))
+        if p:
+            w.X, w.row_slot = ws[0].X, ws[0].row_slot
+        ws.append(w)
+    b = ws[0]
+    pools = []
+    for w in ws:
+        dw = wl.device_tensors(w, DEV)
+        pools.append(srg.Pool(dw["A"], dw["Bt"], dw["slot_rank"], w.slot_alpha))
+    st = srg.Pool.stacked(pools)
+    d = wl.device_tensors(b, DEV)
+    d["W"] = torch.cat([wl.to_torch(w.W, "bf16", DEV) for w in ws], dim=0).contiguous()
+    Y = torch.full((b.n, st.d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+    srg.lora_linear_fused_static(d["row_slot"], d["X"], d["W"], st, Y)
+    # the buffered calls on the same stacked pool
+    seg = srg.Segments(b.n, b.n_slots, DEV)
+    H = torch.zeros((b.n, st.r_max), dtype=torch.float32, device=DEV)
+    srg.lora_build_shrink(d["row_slot"], d["X"], st, seg, H)
+    ref = torch.empty_like(Y)
+    srg.lora_linear_fused(d["X"], d["W"], H, seg, st, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, ref)
+    Yr, _, _ = oracle.stacked_forward(b.X, [w.W for w in ws], [w.A for w in ws],
+                                      [w.B for w in ws], b.row_slot, b.slot_rank, b.slot_alpha,
+                                      b.r_max, b.dtype)
+    e = normwise(to_f64(Y), Yr)
+    assert e <= TOL["bf16"], e
+    say("static stacked", b.n, e)
+
+
 def test_static_call_rejects_oversize_batch():
     w = wl.make_random(909, 16, 64, 64, 3, 64)
     d = wl.device_tensors(w, DEV)
